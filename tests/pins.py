@@ -1,0 +1,393 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes a loaded oracle library (``oracle.load()`` or a build of a
+deliberately altered copy) and raises AssertionError when the oracle violates
+the pin. They are collected by ``test_oracle_pins.py`` (real oracle: all must
+pass) and ``test_pin_sensitivity.py`` (planted mistakes: some must fail).
+
+Sources:
+  P4 = drill page "Implement INT4 group quantization, nibble packing and a
+       dequantizing matmul", statement and visible tests.
+  P5 = "Quantizing a Language Model From Scratch", Results table and
+       "Groupwise scales for INT4" / "Bit packing".
+  P1 = "Building a Pure-Python INT4 Transformer Weight Quantizer with
+       Block-wise Per-Channel Scaling", "Running and Testing It".
+  P3 = "Build a Blockwise INT4 Inference Engine", "Unit Tests".
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TINY = 2.0 ** -24          # smallest positive binary16
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _q(lib, w, g):
+    return oracle.quantize_int4(np.asarray(w, np.float32), g, lib=lib)
+
+
+def _unpack(lib, packed, K):
+    return oracle.unpack_int4(packed, K, lib=lib)
+
+
+def _sx_table():
+    """Sign extension of every 4-bit code by the XOR-8 identity: sx(v) = (v ^ 8) - 8."""
+    v = np.arange(16)
+    return (v ^ 8) - 8
+
+
+# --------------------------------------------------------------------- layout
+
+def pin_p4_nibble_layout(lib):
+    """P4 visible test: [1,-1,7,-7], group 4 -> scale 1.0, bytes [0xF1, 0x97]."""
+    gd = _golden("p4_nibble_layout.json")
+    packed, scales, K = _q(lib, gd["w"], gd["group"])
+    assert K == 4
+    assert float(scales[0, 0]) == gd["scale"]
+    assert int(scales.view(np.uint16)[0, 0]) == gd["scale_bits"]
+    assert [int(b) for b in packed[0]] == gd["packed"], [hex(b) for b in packed[0]]
+
+
+def pin_unpack_exhaustive(lib):
+    """Every byte value unpacks to (sx(low nibble), sx(high nibble)) (P4: element 2j low)."""
+    b = np.arange(256, dtype=np.uint8)[None, :]
+    out = _unpack(lib, b, 512)
+    sx = _sx_table()
+    assert np.array_equal(out[0, 0::2], sx[np.arange(256) & 0xF])
+    assert np.array_equal(out[0, 1::2], sx[np.arange(256) >> 4])
+    # odd K drops the final high nibble
+    out_odd = _unpack(lib, b, 511)
+    assert np.array_equal(out_odd[0], out[0, :511])
+
+
+def pin_pack_unpack_identity(lib):
+    """All 15x15 code pairs in [-7,7] survive quantize->unpack at scale exactly 1."""
+    a, b = np.meshgrid(np.arange(-7, 8), np.arange(-7, 8), indexing="ij")
+    pairs = np.stack([a.ravel(), b.ravel()], 1).astype(np.float32)   # 225 pairs
+    # groups of 8: three code pairs, then (7, -7) so that absmax is 7 and the scale 1
+    g = np.concatenate([pairs.reshape(75, 6), np.tile([[7.0, -7.0]], (75, 1))], 1)
+    w = g.reshape(1, -1).astype(np.float32)
+    packed, scales, K = _q(lib, w, 8)
+    assert np.all(scales.view(np.uint16) == 0x3C00)
+    assert np.array_equal(_unpack(lib, packed, K)[0], w[0].astype(np.int8))
+
+
+# ---------------------------------------------------------------- rounding
+
+def pin_round_half_even(lib):
+    """Ties go to the even integer (round() read as NumPy's rint)."""
+    packed, _, _ = _q(lib, [[0.5, 2.5, 7.0, -7.0]], 4)
+    assert [int(b) for b in packed[0]] == [0x20, 0x97]
+    packed, _, _ = _q(lib, [[-0.5, -2.5, 7.0, 1.5]], 4)   # q = [0, -2, 7, 2]
+    assert [int(b) for b in packed[0]] == [0xE0, 0x27]
+    packed, _, _ = _q(lib, [[3.5, -4.5, -7.0, 5.5]], 4)   # q = [4, -4, -7, 6]
+    assert [int(b) for b in packed[0]] == [0xC4, 0x69]
+
+
+def pin_p4_round_trip(lib, seeds=range(200)):
+    """P4 visible test: |q*s - w| <= 0.5 s + 1e-3 s + 1e-6, over many seeds."""
+    gd = _golden("p4_round_trip.json")
+    g = gd["group"]
+    for seed in seeds:
+        w = np.random.default_rng(seed).normal(size=gd["shape"]).astype(np.float32)
+        packed, scales, K = _q(lib, w, g)
+        q = _unpack(lib, packed, K).astype(np.float32)
+        s = np.repeat(scales.astype(np.float32), g, axis=1)[:, :K]
+        err = np.abs(q * s - w)
+        assert (err <= s * 0.5 + 1e-3 * s + 1e-6).all(), (seed, float(err.max()))
+
+
+def pin_round_trip_ragged(lib):
+    """Half-step bound on odd K, partial last groups and odd/small groups."""
+    rng = np.random.default_rng(11)
+    for (N, K, g) in [(5, 301, 128), (3, 17, 1), (4, 33, 3), (2, 99, 5), (6, 64, 32), (3, 129, 64)]:
+        w = rng.normal(size=(N, K)).astype(np.float32)
+        packed, scales, KK = _q(lib, w, g)
+        assert packed.shape == (N, (K + 1) // 2) and scales.shape == (N, -(-K // g))
+        q = _unpack(lib, packed, KK).astype(np.float32)
+        s = np.repeat(scales.astype(np.float32), g, axis=1)[:, :K]
+        assert (np.abs(q * s - w) <= s * 0.5 + 1e-3 * s + 1e-6).all(), (N, K, g)
+        if K % 2:
+            assert np.all(packed[:, -1] >> 4 == 0), "odd K pad nibble must be zero"
+
+
+# -------------------------------------------------------------- special rows
+
+def pin_zero_group(lib):
+    """P4: a group of zeros gets scale 0; its codes are 0 (also for a group whose
+    absmax/7 rounds to binary16 zero)."""
+    w = np.ones((2, 12), np.float32)
+    w[0, 4:8] = 0.0
+    w[1, 0:4] = 1e-8                       # 1e-8/7 < 2^-25 -> binary16 zero
+    w[1, 4:8] = -1e-8
+    packed, scales, K = _q(lib, w, 4)
+    s = scales.view(np.uint16)
+    assert s[0, 1] == 0 and s[1, 0] == 0 and s[1, 1] == 0
+    assert s[0, 0] != 0 and s[0, 2] != 0
+    q = _unpack(lib, packed, K)
+    assert np.all(q[0, 4:8] == 0) and np.all(q[1, 0:8] == 0)
+    assert packed[0, 2] == 0 and packed[0, 3] == 0
+
+
+def pin_minus_eight(lib):
+    """-8 codes: a row of -8 * 2^-24 has binary16 scale 2^-24 (bits 0x0001) and
+    quantizes to -8 (bytes 0x88; an odd K leaves 0x08 in the last byte);
+    the reconstruction q * scale is exact. Beyond the range, codes clamp."""
+    K = 301
+    w = np.full((1, K), -8.0 * TINY, np.float32)
+    packed, scales, KK = _q(lib, w, 128)
+    assert np.all(scales.view(np.uint16) == 0x0001)
+    assert np.all(packed[0, :-1] == 0x88) and packed[0, -1] == 0x08
+    q = _unpack(lib, packed, KK)
+    assert np.all(q == -8)
+    assert np.array_equal(q.astype(np.float32) * np.float32(TINY), w)
+    # clamp: -9.5 * 2^-24 -> t = -9.5 -> rint -10 -> -8 ; 7.6 * 2^-24 -> 8 -> 7
+    w2 = np.array([[-9.5 * TINY, 0.0, 0.0, 0.0], [7.6 * TINY, 0.0, 0.0, 0.0]], np.float32)
+    packed2, scales2, _ = _q(lib, w2, 4)
+    assert np.all(scales2.view(np.uint16) == 0x0001)
+    assert packed2[0, 0] == 0x08 and packed2[1, 0] == 0x07
+
+
+# ------------------------------------------------------------- fp16 scales
+
+def pin_half_conversion(lib):
+    """The hand-written binary16 rounding agrees with NumPy's astype(float16) on
+    edge values and on 2^21 random binary32 bit patterns spanning the full range."""
+    edge = np.array([0.0, -0.0, 1.0, 65504.0, 65519.996, 65520.0, 65536.0, 1e30, TINY,
+                     TINY / 2, TINY * 0.75, TINY * 1.5, TINY * 2.5, 2.0 ** -14,
+                     2.0 ** -14 * (1 - 2.0 ** -11), 2.0 ** -15 + 2.0 ** -25, 1.0 + 2.0 ** -11,
+                     1.0 + 3 * 2.0 ** -11, 1.0 / 7, 7.0 / 7, 0.5 / 7, 3e-8, 6e-8, 1e-10,
+                     np.inf, -np.inf], np.float32)
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2 ** 32, size=2 ** 21, dtype=np.uint64).astype(np.uint32)
+    rnd = bits.view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    # concentrate half the draws where binary16 is finite: |f| < 2^17
+    near = (rng.random(2 ** 20) * 2.0 ** 17).astype(np.float32) * np.where(
+        rng.random(2 ** 20) < 0.5, -1, 1).astype(np.float32)
+    small = (rng.random(2 ** 18) * 2.0 ** -13).astype(np.float32)   # subnormal region
+    f = np.concatenate([edge, -edge, rnd, near, small])
+    with np.errstate(over="ignore"):
+        want = f.astype(np.float16).view(np.uint16)
+    got = oracle.half_bits_from_float_array(f, lib=lib)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(f[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def pin_half_widening(lib):
+    """Widening every finite binary16 pattern equals NumPy's float16 -> float32."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = np.array([oracle.float_from_half(int(v), lib=lib) for v in h[::7]], np.float32)
+    ref = ref[::7]
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.all(np.isinf(got[np.isinf(ref)]))
+
+
+def pin_scale_is_absmax_over_7(lib):
+    """For absmax 7 * 2^e (normal binary16 range) the scale is exactly 2^e, and
+    only the group's own elements decide it (partial last group included)."""
+    for e in range(-10, 12):
+        w = np.zeros((1, 10), np.float32)
+        w[0, 3] = -7.0 * 2.0 ** e
+        w[0, 9] = 7.0 * 2.0 ** (e - 3)        # lone element of the partial last group
+        packed, scales, _ = _q(lib, w, 8)
+        assert float(scales[0, 0]) == 2.0 ** e and float(scales[0, 1]) == 2.0 ** (e - 3), e
+
+
+def _round_rational(v, frac_bits, emin):
+    """Round a positive Fraction to the nearest binary floating-point number with
+    ``frac_bits`` fraction bits and minimum normal exponent ``emin`` (ties to even),
+    in exact rational arithmetic."""
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    if Fraction(2) ** e > v:
+        e -= 1
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - frac_bits)
+    n = v / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl * quantum
+
+
+def pin_scale_rounding_exact(lib):
+    """scale = binary16(binary32(absmax / 7)), both roundings to nearest even, checked
+    against exact rational arithmetic on absmax values whose binary32 quotient lies
+    on or next to a binary16 rounding midpoint (where a reciprocal multiply, or a
+    single rounding of the exact quotient to binary16, would give another scale)."""
+    rng = np.random.default_rng(21)
+    a = (rng.random(2 ** 22) * 2.0 ** rng.integers(-20, 12, 2 ** 22)).astype(np.float32)
+    q = (a / np.float32(7)).view(np.uint32)
+    low = q & 0x1FFF                                   # bits dropped by binary16 (normal)
+    cand = a[(low == 0x1000) | (low == 0x0FFF) | (low == 0x1001)]
+    assert cand.size > 100
+    checked = 0
+    for amax in cand[:3000]:
+        exact = Fraction(float(amax)) / 7
+        s32 = _round_rational(exact, 23, -126)
+        want = np.float16(float(_round_rational(s32, 10, -14)))
+        _, scales, _ = _q(lib, [[float(amax)]], 1)
+        assert scales[0, 0] == want, (float(amax), float(scales[0, 0]), float(want))
+        checked += 1
+    assert checked == min(3000, cand.size)
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_idempotence(lib):
+    """Q(D(Q(W))) == Q(W) bit for bit when scales are binary16-normal."""
+    for sigma in (0.02, 1.0):
+        w = np.random.default_rng(3).normal(0, sigma, size=(64, 1024)).astype(np.float32)
+        p1, s1, K = _q(lib, w, 128)
+        wq = _unpack(lib, p1, K).astype(np.float32) * np.repeat(s1.astype(np.float32), 128, 1)
+        p2, s2, _ = _q(lib, wq, 128)
+        assert np.array_equal(p1, p2) and np.array_equal(s1.view(np.uint16), s2.view(np.uint16))
+
+
+def pin_sign_and_scale_symmetry(lib):
+    """Q(-W): same scales and negated codes; Q(2^e W): scales times 2^e, same bytes."""
+    w = np.random.default_rng(4).normal(0, 0.5, size=(16, 200)).astype(np.float32)
+    p, s, K = _q(lib, w, 32)
+    pn, sn, _ = _q(lib, -w, 32)
+    assert np.array_equal(s.view(np.uint16), sn.view(np.uint16))
+    assert np.array_equal(_unpack(lib, pn, K), -_unpack(lib, p, K))
+    for e in (-3, 2, 5):
+        pe, se, _ = _q(lib, w * np.float32(2.0 ** e), 32)
+        assert np.array_equal(pe, p)
+        assert np.array_equal(se.astype(np.float64), s.astype(np.float64) * 2.0 ** e)
+
+
+def pin_two_oracles_agree(lib):
+    """The scalar C oracle and the NumPy brute force agree bit for bit on quantize and
+    unpack over ragged shapes, several groups and tiny magnitudes (subnormal scales)."""
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        N = int(rng.integers(1, 24))
+        K = int(rng.integers(1, 300))
+        g = int(rng.choice([1, 2, 3, 4, 5, 7, 16, 32, 64, 128, 256]))
+        sigma = float(rng.choice([1.0, 0.02, 1e-5, 3e-7, 1e-8]))
+        w = rng.normal(0, sigma, size=(N, K)).astype(np.float32)
+        if trial % 5 == 0:
+            w[:, : min(g, K)] = 0.0
+        p_c, s_c, _ = _q(lib, w, g)
+        p_b, s_b, _ = brute.quantize_int4(w, g)
+        assert np.array_equal(s_c.view(np.uint16), s_b.view(np.uint16)), (N, K, g, sigma)
+        assert np.array_equal(p_c, p_b), (N, K, g, sigma)
+        assert np.array_equal(_unpack(lib, p_c, K), brute.unpack_int4(p_b, K))
+
+
+def pin_storage_sizes(lib):
+    """P5's quantized-layer sizes follow from N*ceil(K/2) packed bytes plus one scale
+    per (row, group): with the page's 4-byte scales the table is reproduced."""
+    gd = _golden("p5_storage.json")
+    tot = {"fp32": 0, "packed": 0, 64: 0, 32: 0}
+    for (N, K) in gd["linears_out_in"]:
+        tot["fp32"] += gd["layers"] * N * K * 4
+        tot["packed"] += gd["layers"] * N * lib.int4_oracle_packed_row_bytes(K)
+        for g in (64, 32):
+            tot[g] += gd["layers"] * N * lib.int4_oracle_num_groups(K, g) * gd["page_scale_bytes"]
+    mb = lambda b: round(b / 1e6, 2)
+    assert mb(tot["fp32"]) == gd["fp32_mb"]
+    assert mb(tot[64]) == gd["scale_overhead_g64_mb"] and mb(tot[32]) == gd["scale_overhead_g32_mb"]
+    assert mb(tot["packed"] + tot[64]) == gd["int4_g64_mb"]
+    assert mb(tot["packed"] + tot[32]) == gd["int4_g32_mb"]
+    assert round(tot["fp32"] / (tot["packed"] + tot[64]), 2) == gd["ratio_g64"]
+    assert round(tot["fp32"] / (tot["packed"] + tot[32]), 2) == gd["ratio_g32"]
+    # this build's own format: binary16 scales; ragged closed forms
+    assert lib.int4_oracle_num_groups(301, 128) == 3 and lib.int4_oracle_packed_row_bytes(301) == 151
+    assert lib.int4_oracle_num_groups(128, 128) == 1 and lib.int4_oracle_num_groups(129, 128) == 2
+
+
+def pin_p1_max_error(lib):
+    """P1's unit test bound max|w - w_hat| < 0.5 for randn(512,512), block 64 holds
+    (its MSE < 0.01 bound does not: MSE is about 0.0115 for this distribution)."""
+    w = np.random.default_rng(0).standard_normal((512, 512)).astype(np.float32)
+    p, s, K = _q(lib, w, 64)
+    wh = _unpack(lib, p, K).astype(np.float32) * np.repeat(s.astype(np.float32), 64, 1)
+    assert float(np.abs(w - wh).max()) < 0.5
+
+
+# -------------------------------------------------------------------- matmul
+
+def _mm(lib, x, p, s, K, g, bound=False):
+    return oracle.int4_matmul(x, p, s, K, g, with_bound=bound, lib=lib)
+
+
+def pin_matmul_vs_full_dequant(lib):
+    """int4_matmul equals x @ (unpack(packed) * repeated scales).T by brute force
+    (P4 hidden-suite topic 'the matmul against a full dequantization')."""
+    rng = np.random.default_rng(9)
+    for (M, N, K, g) in [(4, 64, 256, 128), (3, 48, 301, 128), (1, 5, 1, 1), (2, 7, 9, 2),
+                         (5, 9, 31, 3), (6, 13, 64, 4), (3, 11, 45, 5), (8, 16, 63, 32),
+                         (2, 3, 300, 128), (7, 17, 129, 64)]:
+        w = rng.normal(size=(N, K)).astype(np.float32)
+        x = rng.normal(size=(M, K)).astype(np.float32)
+        p, s, _ = _q(lib, w, g)
+        y, bnd = _mm(lib, x, p, s, K, g, bound=True)
+        ref = brute.int4_matmul(x, p, s, K, g)
+        assert np.all(np.abs(y.astype(np.float64) - ref) <= 1e-6 * bnd + 1e-30), (M, N, K, g)
+        dq = brute.dequantize(p, s, K, g)
+        assert np.allclose(bnd, np.abs(x.astype(np.float64)) @ np.abs(dq).T, rtol=1e-12, atol=0)
+
+
+def pin_matmul_one_hot(lib):
+    """x = identity (M = K) gives y = w_hat transposed exactly: each output is one
+    product q * scale; this fixes which nibble feeds which k and which scale."""
+    rng = np.random.default_rng(10)
+    for (N, K, g) in [(12, 33, 8), (8, 64, 32), (5, 17, 3)]:
+        w = rng.normal(size=(N, K)).astype(np.float32)
+        p, s, _ = _q(lib, w, g)
+        y = _mm(lib, np.eye(K, dtype=np.float32), p, s, K, g)
+        q = (np.asarray(w) * 0).astype(np.float64)
+        v = p.astype(np.int64)
+        q[:, 0::2] = ((v & 0xF) ^ 8) - 8
+        q[:, 1::2] = ((v[:, : K // 2] >> 4) ^ 8) - 8
+        sg = np.repeat(s.astype(np.float64), g, 1)[:, :K]
+        assert np.array_equal(y.astype(np.float64), (q * sg).T), (N, K, g)
+
+
+def pin_matmul_invariants(lib):
+    """x = 0 gives exactly 0; rows are independent; the result is linear in x."""
+    rng = np.random.default_rng(12)
+    N, K, g = 24, 200, 64
+    w = rng.normal(size=(N, K)).astype(np.float32)
+    p, s, _ = _q(lib, w, g)
+    assert np.all(_mm(lib, np.zeros((3, K), np.float32), p, s, K, g) == 0)
+    x = rng.normal(size=(6, K)).astype(np.float32)
+    y = _mm(lib, x, p, s, K, g)
+    for r in range(6):
+        assert np.array_equal(_mm(lib, x[r:r + 1], p, s, K, g)[0], y[r])
+    x2 = rng.normal(size=(6, K)).astype(np.float32)
+    xs = (x.astype(np.float64) + x2).astype(np.float32)
+    _, bnd = _mm(lib, xs, p, s, K, g, bound=True)
+    lin = _mm(lib, x, p, s, K, g).astype(np.float64) + _mm(lib, x2, p, s, K, g)
+    assert np.all(np.abs(_mm(lib, xs, p, s, K, g) - lin) <= 1e-5 * (bnd + 1))
+
+
+def pin_p3_correctness_pattern(lib):
+    """P3's unit test shape (M,N,K = 4,8,256, block 128, W*0.5): fused result vs a
+    dequantized reference within its max_err < 1e-3."""
+    rng = np.random.default_rng(123)
+    w = (rng.standard_normal((8, 256)) * 0.5).astype(np.float32)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    p, s, K = _q(lib, w, 128)
+    y = _mm(lib, x, p, s, K, 128)
+    assert float(np.abs(y - brute.int4_matmul(x, p, s, K, 128)).max()) < 1e-3
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
