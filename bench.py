@@ -1,0 +1,221 @@
+"""Benchmark of the INT4 quantize -> unpack -> dequantizing-matmul path on one MI355X.
+
+Workload: the 7B-class linear layers [4096,4096], [11008,4096] and [4096,11008]
+(weights ~N(0, 0.02) float32 with 0.1% entries x20, group 128; activations
+fp16 ~N(0,1); all seeded and synthetic, see workloads.py). One step runs the
+whole hot path on the three matrices:
+  1. int4_quantize of each fp32 weight matrix (fresh output buffers),
+  2. int4_unpack of each packed matrix,
+  3. a decode pass at M = 1: int4_matmul over a pool of R copies of the three
+     packed matrices (R * 55 MB >= 1 GiB, four times the 256 MB last-level
+     cache, so every launch streams its weights from HBM),
+  4. a prefill pass at M = 2048: int4_matmul on each matrix.
+Inputs are resident in HBM before the timed region. Per-phase durations are
+measured with HIP events recorded on the stream the kernels run on.
+
+The headline value is the packed-weight bandwidth of phase 3 (algorithmic
+bytes N*ceil(K/2) + 2*N*G per launch over the launch's average duration); the
+M = 2048 rate (2*M*N*K flops over the phase's time) is reported beside it,
+each as a fraction of the MI355X peak (HBM 8 TB/s; dense fp16 MFMA
+2.5 PFLOP/s).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+SHAPES = [("q_proj", 4096, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 11008)]
+GROUP = 128
+M_DECODE, M_PREFILL = 1, 2048
+POOL_BYTES = 1 << 30
+
+
+def packed_weight_bytes(N, K, g=GROUP):
+    return N * ((K + 1) // 2) + 2 * N * ((K + g - 1) // g)
+
+
+def cpu_baseline(min_seconds: float = 10.0):
+    """The oracle (scalar C, single thread) on a bounded sample of the same
+    workload: repeated M = 1 passes over the three matrices until at least
+    `min_seconds` of CPU time, in the headline unit (packed-weight GB/s)."""
+    import numpy as np
+    import oracle
+    import workloads
+    data = []
+    for name, N, K in SHAPES:
+        case = workloads.Case(name, N, K, GROUP, 0.02, True)
+        p, s, _ = oracle.quantize_int4(workloads.weights(case), GROUP)
+        data.append((p, s, K, workloads.activations(M_DECODE, K)))
+    passes, t_total = 0, 0.0
+    while t_total < min_seconds:
+        t0 = time.perf_counter()
+        for (p, s, K, x) in data:
+            oracle.int4_matmul(x, p, s, K, GROUP)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    nbytes = passes * sum(packed_weight_bytes(N, K) for _, N, K in SHAPES)
+    # the same oracle at M = 2048 on a 4-row sample of x, as flops/s
+    p, s, K, _ = data[0]
+    x4 = workloads.activations(4, K)
+    t0 = time.perf_counter()
+    oracle.int4_matmul(x4, p, s, K, GROUP)
+    t_mm = time.perf_counter() - t0
+    return {
+        "value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{passes} M=1 passes of the scalar C oracle over the three matrices "
+                  f"({t_total:.1f} s, 1 thread of os.cpu_count()={os.cpu_count()}, "
+                  f"affinity={len(os.sched_getaffinity(0))})",
+        "m2048_tflops_from_4_rows": round(2 * 4 * 4096 * 4096 / t_mm / 1e12, 6),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no "
+              "multi-GPU leg; a sharded layout is described in the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import dequantizing_gemm_amd as dq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+
+    mats = []
+    for name, N, K in SHAPES:
+        case = workloads.Case(name, N, K, GROUP, 0.02, True)
+        w = torch.from_numpy(workloads.weights(case)).to(dev)
+        x1 = torch.from_numpy(workloads.activations(M_DECODE, K)).to(dev)
+        xp = torch.from_numpy(workloads.activations(M_PREFILL, K)).to(dev)
+        packed, scales, _ = dq.quantize_int4(w, GROUP)
+        mats.append(dict(name=name, N=N, K=K, w=w, x1=x1, xp=xp, packed=packed, scales=scales,
+                         q_out=torch.empty_like(packed), s_out=torch.empty_like(scales),
+                         u_out=torch.empty((N, K), dtype=torch.int8, device=dev),
+                         y1=torch.empty((M_DECODE, N), dtype=torch.float32, device=dev),
+                         yp=torch.empty((M_PREFILL, N), dtype=torch.float32, device=dev)))
+    set_bytes = sum(packed_weight_bytes(m["N"], m["K"]) for m in mats)
+    R = max(2, -(-POOL_BYTES // set_bytes))
+    pool = [[(m["packed"].clone(), m["scales"].clone()) for m in mats] for _ in range(R)]
+    torch.cuda.synchronize()
+
+    L = dq.lib
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch_quantize():
+        for m in mats:
+            rc = L.int4_quantize(m["w"].data_ptr(), m["N"], m["K"], GROUP, m["q_out"].data_ptr(),
+                                 m["s_out"].data_ptr(), stream)
+            assert rc == 0
+
+    def launch_unpack():
+        for m in mats:
+            assert L.int4_unpack(m["q_out"].data_ptr(), m["N"], m["K"], m["u_out"].data_ptr(), stream) == 0
+
+    def launch_decode():
+        for r in range(R):
+            for m, (p, s) in zip(mats, pool[r]):
+                assert L.int4_matmul(m["x1"].data_ptr(), 1, M_DECODE, p.data_ptr(), s.data_ptr(),
+                                     m["N"], m["K"], GROUP, m["y1"].data_ptr(), stream) == 0
+
+    def launch_prefill():
+        for m in mats:
+            assert L.int4_matmul(m["xp"].data_ptr(), 1, M_PREFILL, m["packed"].data_ptr(),
+                                 m["scales"].data_ptr(), m["N"], m["K"], GROUP, m["yp"].data_ptr(),
+                                 stream) == 0
+
+    phases = [("quantize", launch_quantize), ("unpack", launch_unpack), ("decode_m1", launch_decode),
+              ("prefill_m2048", launch_prefill)]
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(phases):
+            if events is not None:
+                events[i].record()
+            fn()
+        if events is not None:
+            events[len(phases)].record()
+
+    print(f"bench: warmup {args.warmup} steps (pool of {R} weight copies, "
+          f"{R * set_bytes / 1e9:.2f} GB)", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phase_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, (name, _) in enumerate(phases)}
+    print(f"bench: timed {args.steps} steps in {wall:.3f} s; per-phase ms {phase_ms}",
+          file=sys.stderr, flush=True)
+
+    # algorithmic work per phase and per launch
+    q_bytes = sum(m["N"] * m["K"] * 4 + packed_weight_bytes(m["N"], m["K"]) for m in mats)
+    u_bytes = sum(m["N"] * ((m["K"] + 1) // 2) + m["N"] * m["K"] for m in mats)
+    d_bytes = R * set_bytes
+    p_flops = sum(2 * M_PREFILL * m["N"] * m["K"] for m in mats)
+    per_launch = {"quantize": 3, "unpack": 3, "decode_m1": 3 * R, "prefill_m2048": 3}
+
+    def roof(name, bound, work, unit, peak):
+        t = phase_ms[name] * 1e-3
+        achieved = work / t / (1e9 if unit == "GB/s" else 1e12)
+        return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "avg_launch_us": round(phase_ms[name] * 1e3 / per_launch[name], 3),
+                "launches_per_step": per_launch[name]}
+
+    roofs = [roof("quantize", "hbm", q_bytes, "GB/s", HBM_PEAK_GBS),
+             roof("unpack", "hbm", u_bytes, "GB/s", HBM_PEAK_GBS),
+             roof("decode_m1", "hbm", d_bytes, "GB/s", HBM_PEAK_GBS),
+             roof("prefill_m2048", "mfma", p_flops, "TFLOP/s", FP16_MFMA_PEAK_TFLOPS)]
+    dominant = max(roofs, key=lambda r: phase_ms[r["kernel"]])
+    decode = roofs[2]
+    ms_per_step = wall * 1e3 / args.steps
+    line = {
+        "metric": "int4_matmul packed-weight HBM GB/s @M=1 + TFLOP/s @M=2048, % of roofline",
+        "value": decode["achieved"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4 weights x fp16 activations -> fp32",
+        "data": "synthetic",
+        "config": {"workload": "7B-class linears [4096,4096],[11008,4096],[4096,11008], "
+                               "N(0,0.02) + 0.1% x20 outliers, group 128; x fp16 N(0,1); "
+                               f"step = quantize+unpack of all three, M=1 over {R} pooled copies, "
+                               "M=2048 on each", "group": GROUP, "m_decode": M_DECODE,
+                   "m_prefill": M_PREFILL, "pool_copies": R},
+        "m1_frac_of_hbm_peak": decode["frac"],
+        "m2048_tflops": roofs[3]["achieved"], "m2048_frac_of_fp16_peak": roofs[3]["frac"],
+        "roofline": dominant,
+        "rooflines": roofs,
+        "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

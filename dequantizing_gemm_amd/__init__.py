@@ -1,0 +1,177 @@
+"""INT4 group quantization and fused dequantizing matmul for MI355X (gfx950).
+
+Thin binding over the C ABI in ``include/int4dq.h`` (``libint4dq.so``, built
+in-tree by ``dequantizing_gemm_amd.build``). The functions keep the names and
+signatures of the drill page "Implement INT4 group quantization, nibble
+packing and a dequantizing matmul" (statement):
+
+    quantize_int4(w, group=128) -> (packed, scales, K)
+    unpack_int4(packed, K) -> int8 [N, K]
+    int4_matmul(x, packed, scales, K, group=128) -> float32 [M, N]
+
+All tensors are torch tensors on the GPU; torch provides the device memory and
+the stream (work is enqueued on ``torch.cuda.current_stream()``). Every step of
+the computation runs in the library's HIP kernels: this module only checks
+shapes and dtypes, allocates outputs and passes pointers. It raises ImportError
+when the library has not been built -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["quantize_int4", "unpack_int4", "int4_matmul", "int4_matmul_path", "matmul_select",
+           "num_groups", "packed_bytes", "lib", "LIB_PATH", "Int4Error", "PATHS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4dq.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+X_F32, X_F16 = 0, 1
+PATHS = {"auto": 0, "generic": 1, "skinny": 2, "tiled": 3}
+PATH_NAMES = {v: k for k, v in PATHS.items()}
+
+# Every function declared in include/int4dq.h, with its ctypes signature.
+_i64, _vp, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+SIGNATURES = {
+    "int4_num_groups": (_i64, [_i64, _i64]),
+    "int4_packed_bytes": (_i64, [_i64, _i64]),
+    "int4_quantize": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "int4_unpack": (_int, [_vp, _i64, _i64, _vp, _vp]),
+    "int4_matmul": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "int4_matmul_path": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "int4_matmul_select": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "int4_last_error": (ctypes.c_char_p, []),
+}
+
+
+class Int4Error(RuntimeError):
+    """A HIP launch failure reported by the library."""
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m dequantizing_gemm_amd.build` (hipcc, gfx950)")
+    cdll = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(cdll, name)
+        fn.restype, fn.argtypes = res, args
+    return cdll
+
+
+lib = _load()
+
+
+def _raise(rc: int, what: str):
+    if rc == OK:
+        return
+    msg = f"{what}: {lib.int4_last_error().decode()}"
+    if rc in (EINVAL, EUNSUPPORTED):
+        raise ValueError(msg)
+    raise Int4Error(msg)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _gpu(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int = 2):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def num_groups(K: int, group: int) -> int:
+    return int(lib.int4_num_groups(K, group))
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib.int4_packed_bytes(N, K))
+
+
+def quantize_int4(w: torch.Tensor, group: int = 128):
+    """w [N, K] float32 -> (packed uint8 [N, ceil(K/2)], scales float16 [N, G], K)."""
+    _gpu(w, "w", torch.float32)
+    N, K = w.shape
+    G = num_groups(K, group)
+    if G < 1:
+        raise ValueError(f"invalid K={K} / group={group}")
+    packed = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    with torch.cuda.device(w.device):
+        rc = lib.int4_quantize(w.data_ptr(), N, K, group, packed.data_ptr(), scales.data_ptr(),
+                               _stream(w))
+    _raise(rc, "int4_quantize")
+    return packed, scales, K
+
+
+def unpack_int4(packed: torch.Tensor, K: int) -> torch.Tensor:
+    """packed uint8 [N, ceil(K/2)] -> int8 [N, K], sign-extended."""
+    _gpu(packed, "packed", torch.uint8)
+    N = packed.shape[0]
+    if packed.shape[1] != (K + 1) // 2:
+        raise ValueError(f"packed has {packed.shape[1]} bytes per row, K={K} needs {(K + 1) // 2}")
+    out = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    with torch.cuda.device(packed.device):
+        rc = lib.int4_unpack(packed.data_ptr(), N, K, out.data_ptr(), _stream(packed))
+    _raise(rc, "int4_unpack")
+    return out
+
+
+def _matmul_args(x, packed, scales, K, group):
+    if not isinstance(x, torch.Tensor) or x.dtype not in (torch.float32, torch.float16):
+        raise ValueError("x must be a float32 or float16 torch tensor")
+    _gpu(x, "x", x.dtype)
+    _gpu(packed, "packed", torch.uint8)
+    _gpu(scales, "scales", torch.float16)
+    M, Kx = x.shape
+    N = packed.shape[0]
+    if Kx != K:
+        raise ValueError(f"x has {Kx} columns, K={K}")
+    if packed.shape[1] != (K + 1) // 2:
+        raise ValueError(f"packed has {packed.shape[1]} bytes per row, K={K} needs {(K + 1) // 2}")
+    if tuple(scales.shape) != (N, num_groups(K, group)):
+        raise ValueError(f"scales shape {tuple(scales.shape)} != {(N, num_groups(K, group))}")
+    if not (x.device == packed.device == scales.device):
+        raise ValueError("x, packed and scales must be on the same device")
+    return M, N, (X_F32 if x.dtype == torch.float32 else X_F16)
+
+
+def int4_matmul_path(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
+                     group: int = 128, path: str = "auto", out: torch.Tensor | None = None):
+    """y [M, N] float32 = x @ dequantize(W).T through a chosen kernel (see PATHS)."""
+    M, N, xd = _matmul_args(x, packed, scales, K, group)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    else:
+        _gpu(out, "out", torch.float32)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out shape {tuple(out.shape)} != {(M, N)}")
+    with torch.cuda.device(x.device):
+        rc = lib.int4_matmul_path(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), N, K,
+                                  group, out.data_ptr(), PATHS[path], _stream(x))
+    _raise(rc, "int4_matmul")
+    return out
+
+
+def int4_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
+                group: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] float32 = x @ dequantize(W).T, one group at a time (integer-first)."""
+    return int4_matmul_path(x, packed, scales, K, group, "auto", out)
+
+
+def matmul_select(x, packed, scales, K, group=128) -> str:
+    """Name of the kernel int4_matmul would run for these tensors."""
+    M, N, xd = _matmul_args(x, packed, scales, K, group)
+    p = lib.int4_matmul_select(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), N, K,
+                               group, 1)
+    return PATH_NAMES.get(p, "invalid")

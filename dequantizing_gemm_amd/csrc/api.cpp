@@ -1,0 +1,149 @@
+// api.cpp -- the C ABI declared in include/int4dq.h: argument validation,
+// kernel selection, launch on the caller's stream, and the thread-local error
+// text. No HIP call is made before the arguments have been validated, so
+// every invalid-argument path can be exercised on a host without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <stdarg.h>
+
+#include "../../include/int4dq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return INT4DQ_OK;
+}
+
+// a * b with overflow check into *out (both non-negative).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(INT4DQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shared validation of int4_matmul arguments; on success fills the sizes.
+int check_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                 const uint16_t* scales, int64_t N, int64_t K, int64_t group, const float* y) {
+  if (M < 0) return fail(INT4DQ_EINVAL, "int4_matmul: M must be >= 0 (got %lld)", (long long)M);
+  if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "int4_matmul: N and K must be >= 1 (got N=%lld K=%lld)", (long long)N, (long long)K);
+  if (group < 1) return fail(INT4DQ_EINVAL, "int4_matmul: group must be >= 1 (got %lld)", (long long)group);
+  if (x_dtype != INT4DQ_X_F32 && x_dtype != INT4DQ_X_F16)
+    return fail(INT4DQ_EINVAL, "int4_matmul: unknown x_dtype %d", x_dtype);
+  int64_t t;
+  const int64_t G = (K + group - 1) / group;
+  if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t) ||
+      !mul_ok(N, (K + 1) / 2, &t) || !mul_ok(N, G, &t) || !mul_ok(t, 2, &t))
+    return fail(INT4DQ_EINVAL, "int4_matmul: sizes overflow int64");
+  if (!packed || !scales) return fail(INT4DQ_EINVAL, "int4_matmul: packed and scales must be non-NULL");
+  if (M > 0 && (!x || !y)) return fail(INT4DQ_EINVAL, "int4_matmul: x and y must be non-NULL when M > 0");
+  return INT4DQ_OK;
+}
+
+int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t K,
+                int64_t group) {
+  if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, K, group)) return INT4DQ_PATH_SKINNY;
+  if (!int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group)) return INT4DQ_PATH_TILED;
+  return INT4DQ_PATH_GENERIC;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t int4_num_groups(int64_t K, int64_t group) {
+  if (K < 1 || group < 1) return -1;
+  return K / group + (K % group != 0);
+}
+
+int64_t int4_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return -1;
+  int64_t t;
+  if (!mul_ok(N, K / 2 + (K % 2), &t)) return -1;
+  return t;
+}
+
+int int4_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
+                  uint16_t* scales, void* stream) {
+  if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "int4_quantize: N and K must be >= 1 (got N=%lld K=%lld)", (long long)N, (long long)K);
+  if (group < 1) return fail(INT4DQ_EINVAL, "int4_quantize: group must be >= 1 (got %lld)", (long long)group);
+  int64_t t;
+  if (!mul_ok(N, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(N, (K + group - 1) / group, &t) || !mul_ok(t, 2, &t))
+    return fail(INT4DQ_EINVAL, "int4_quantize: sizes overflow int64");
+  if (!w || !packed || !scales) return fail(INT4DQ_EINVAL, "int4_quantize: w, packed and scales must be non-NULL");
+  return hip_status(int4dq::launch_quantize(w, N, K, group, packed, scales, (hipStream_t)stream),
+                    "int4_quantize launch");
+}
+
+int int4_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* out, void* stream) {
+  if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "int4_unpack: N and K must be >= 1 (got N=%lld K=%lld)", (long long)N, (long long)K);
+  int64_t t;
+  if (!mul_ok(N, K, &t)) return fail(INT4DQ_EINVAL, "int4_unpack: sizes overflow int64");
+  if (!packed || !out) return fail(INT4DQ_EINVAL, "int4_unpack: packed and out must be non-NULL");
+  return hip_status(int4dq::launch_unpack(packed, N, K, out, (hipStream_t)stream), "int4_unpack launch");
+}
+
+int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                     const uint16_t* scales, int64_t N, int64_t K, int64_t group, float* y,
+                     int path, void* stream) {
+  int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
+  if (rc != INT4DQ_OK) return rc;
+  if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_TILED)
+    return fail(INT4DQ_EINVAL, "int4_matmul_path: unknown path %d", path);
+  if (M == 0) return ok();
+  if (path == INT4DQ_PATH_AUTO) path = choose_path(x, x_dtype, M, packed, K, group);
+  const hipStream_t s = (hipStream_t)stream;
+  switch (path) {
+    case INT4DQ_PATH_SKINNY: {
+      const char* why = int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, K, group);
+      if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
+      return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, N, K, group, y, s),
+                        "int4_matmul skinny launch");
+    }
+    case INT4DQ_PATH_TILED: {
+      const char* why = int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group);
+      if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
+      return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, N, K, group, y, s),
+                        "int4_matmul tiled launch");
+    }
+    default:
+      return hip_status(int4dq::launch_matmul_generic(x, x_dtype, M, packed, scales, N, K, group, y, s),
+                        "int4_matmul generic launch");
+  }
+}
+
+int int4_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                const uint16_t* scales, int64_t N, int64_t K, int64_t group, float* y,
+                void* stream) {
+  return int4_matmul_path(x, x_dtype, M, packed, scales, N, K, group, y, INT4DQ_PATH_AUTO, stream);
+}
+
+int int4_matmul_select(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                       const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                       const float* y) {
+  if (check_matmul(x, x_dtype, M, packed, scales, N, K, group, y) != INT4DQ_OK) return -1;
+  return choose_path(x, x_dtype, M, packed, K, group);
+}
+
+const char* int4_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// kernels.h -- internal launch functions behind the C ABI (include/int4dq.h).
+// Arguments here are already validated by api.cpp; these functions only pick a
+// kernel variant and enqueue it on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace int4dq {
+
+hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
+                           uint16_t* scales, hipStream_t stream);
+
+hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* out,
+                         hipStream_t stream);
+
+hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                                 float* y, hipStream_t stream);
+
+// nullptr if the kernel takes these arguments, else the reason it does not.
+const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
+                                      const uint8_t* packed, int64_t K, int64_t group);
+hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
+                                const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                                float* y, hipStream_t stream);
+
+const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
+                                     int64_t K, int64_t group);
+hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
+                               const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                               float* y, hipStream_t stream);
+
+}  // namespace int4dq

@@ -1,0 +1,68 @@
+// matmul_generic.hip -- general dequantizing matmul (any M, N, K, group,
+// alignment; binary32 or binary16 activations) on the vector ALUs.
+//
+// Definition (drill page "Implement INT4 group quantization, nibble packing
+// and a dequantizing matmul", statement, int4_matmul):
+//   y[m, n] = sum over groups gi of scale[n, gi] * (sum over k in gi of x[m, k] * q[n, k])
+// i.e. x times the group's integer codes first, then the group's scale.
+//
+// One wavefront per output y[m, n]. The wavefront walks the groups of row n;
+// inside a group the 64 lanes stride over k (coalesced reads of x and of the
+// packed bytes), each lane forms its share of the group's integer-weighted sum
+// in fp32 and multiplies it by the group's scale; the lane sums are reduced at
+// the end. This path exists for shapes and dtypes the MFMA kernels do not
+// take (binary32 x, odd K, unaligned rows, group sizes other than 32, 64 or a
+// multiple of 128); it is not the fast path.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace int4dq {
+
+template <typename XT>
+__device__ __forceinline__ float load_x(const XT* p) { return (float)*p; }
+
+template <typename XT>
+__global__ __launch_bounds__(256) void matmul_generic_kernel(
+    const XT* __restrict__ x, int64_t M, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scales, int64_t N, int64_t K, int64_t group, int64_t G,
+    float* __restrict__ y) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t out = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (out >= M * N) return;                        // whole wavefronts only
+  const int64_t m = out / N, n = out - m * N;
+  const XT* xr = x + m * K;
+  const uint8_t* pr = packed + n * ((K + 1) >> 1);
+  const uint16_t* sr = scales + n * G;
+  float acc = 0.0f;
+  for (int64_t gi = 0; gi < G; ++gi) {
+    const int64_t k0 = gi * group;
+    const int64_t k1 = k0 + group < K ? k0 + group : K;
+    float part = 0.0f;
+    for (int64_t k = k0 + lane; k < k1; k += kWave) {
+      const uint32_t byte = pr[k >> 1];
+      const int q = sx4((byte >> (4 * (int)(k & 1))) & 0xFu);
+      part = __builtin_fmaf(load_x(xr + k), (float)q, part);
+    }
+    acc = __builtin_fmaf(half_bits_to_float(sr[gi]), part, acc);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) y[m * N + n] = acc;
+}
+
+hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                                 float* y, hipStream_t stream) {
+  const int64_t G = (K + group - 1) / group;
+  const int64_t outs = M * N;
+  const dim3 grid((unsigned)((outs + 3) / 4)), block(256);
+  if (x_dtype == 0)
+    hipLaunchKernelGGL(matmul_generic_kernel<float>, grid, block, 0, stream,
+                       static_cast<const float*>(x), M, packed, scales, N, K, group, G, y);
+  else
+    hipLaunchKernelGGL(matmul_generic_kernel<_Float16>, grid, block, 0, stream,
+                       static_cast<const _Float16*>(x), M, packed, scales, N, K, group, G, y);
+  return hipGetLastError();
+}
+
+}  // namespace int4dq

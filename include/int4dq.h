@@ -1,0 +1,147 @@
+/*
+ * int4dq.h -- C ABI of the MI355X (gfx950) INT4 group-quantization library:
+ * block-wise symmetric INT4 weight quantization with two's-complement nibble
+ * packing, unpacking, and the fused dequantizing matmul.
+ *
+ * The three operations are the ones stated on the drill page "Implement INT4
+ * group quantization, nibble packing and a dequantizing matmul"
+ * (inferenceinterviews.com), section "statement": quantize_int4,
+ * unpack_int4 and int4_matmul, with the same argument order (x, packed,
+ * scales, K, group) and the same layouts.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers (hipMalloc'd or equivalent) to
+ *    dense row-major arrays. The caller owns every buffer; the library never
+ *    allocates, frees, or synchronises, and never keeps a pointer after the
+ *    call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    default stream) and the call returns without waiting for it. A kernel
+ *    fault therefore surfaces at the caller's next synchronisation.
+ *  - Arguments are validated before anything is enqueued. On a non-OK return
+ *    nothing has been written to any output. int4_last_error() then returns a
+ *    description (thread-local; valid until the next call on this thread).
+ *  - Inputs are never modified; outputs are overwritten in full, including
+ *    the zero pad nibble of an odd K.
+ *  - There is no alignment requirement. Internally, 16-byte aligned bases with
+ *    suitable strides select the vectorised kernels; anything else runs a
+ *    general kernel with the same results.
+ *  - Calls hold no global state besides the thread-local error text, so they
+ *    may be issued concurrently from several threads and streams.
+ *  - Preconditions not checked: weights and activations are finite, and
+ *    |w| <= 7 * 65504 (so every scale is finite in binary16).
+ */
+#ifndef INT4DQ_H
+#define INT4DQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by the entry points. */
+#define INT4DQ_OK           0  /* enqueued */
+#define INT4DQ_EINVAL       1  /* bad argument: size, null pointer, dtype, overflow */
+#define INT4DQ_EUNSUPPORTED 2  /* a forced kernel path that cannot take this shape/layout */
+#define INT4DQ_EHIP         3  /* the HIP runtime refused the launch */
+
+/* Element type of the activations x in int4_matmul. */
+#define INT4DQ_X_F32 0         /* IEEE binary32 */
+#define INT4DQ_X_F16 1         /* IEEE binary16 */
+
+/* Kernel selection for int4_matmul_path (int4_matmul always uses AUTO). */
+#define INT4DQ_PATH_AUTO    0  /* choose by M, dtype and alignment */
+#define INT4DQ_PATH_GENERIC 1  /* VALU kernel, any shape, any group, fp32 or fp16 x */
+#define INT4DQ_PATH_SKINNY  2  /* M <= 16, fp16 x: weight-streaming MFMA kernel */
+#define INT4DQ_PATH_TILED   3  /* any M, fp16 x: LDS-tiled MFMA kernel */
+
+/*
+ * Number of scale groups per row, G = ceil(K / group) (drill page,
+ * statement: scales [N, G]). Returns -1 if K < 1 or group < 1.
+ */
+int64_t int4_num_groups(int64_t K, int64_t group);
+
+/*
+ * Bytes of the packed weight array, N * ceil(K / 2) (drill page, statement:
+ * packed [N, ceil(K / 2)] uint8). Returns -1 on N < 1, K < 1 or overflow.
+ * The scale array takes a further 2 * N * G bytes.
+ */
+int64_t int4_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * quantize_int4 (drill page, statement).
+ *   w       in : [N, K] binary32 weights.
+ *   packed  out: [N, ceil(K/2)] bytes. Byte j of row n holds element 2j in its
+ *                low nibble and element 2j+1 in its high nibble, each the 4-bit
+ *                two's complement code q = clip(round(w / scale), -8, 7); an odd
+ *                K leaves a zero high nibble in the row's last byte.
+ *   scales  out: [N, G] binary16 bit patterns, G = ceil(K / group). Group gi of
+ *                row n covers k in [gi*group, min((gi+1)*group, K)); its scale is
+ *                binary16(absmax / 7), the division done in binary32 and both
+ *                roundings to nearest even; a group of zeros gets scale 0 and
+ *                codes 0.
+ *   Rounding of w / scale: the divisor is the stored binary16 scale widened to
+ *   binary32, the division is correctly rounded binary32, and ties round to
+ *   even (NumPy's round). Bit-exact with a CPU reference computing the same.
+ *   Errors: EINVAL if N, K or group < 1, a pointer is NULL, or sizes overflow.
+ */
+int int4_quantize(const float *w, int64_t N, int64_t K, int64_t group,
+                  uint8_t *packed, uint16_t *scales, void *stream);
+
+/*
+ * unpack_int4 (drill page, statement): int8 [N, K], sign-extended.
+ *   packed in : [N, ceil(K/2)] bytes in the layout written by int4_quantize.
+ *   out    out: [N, K] int8, out[n, k] = the sign-extended nibble of element k
+ *               (the pad nibble of an odd K is not emitted).
+ *   Errors: EINVAL if N or K < 1, a pointer is NULL, or sizes overflow.
+ */
+int int4_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *out, void *stream);
+
+/*
+ * int4_matmul (drill page, statement):
+ *   y = x @ dequantize(W).T, computed one group at a time: x times the group's
+ *   integer weights first, then that group's scale on each output column.
+ *   x       in : [M, K], element type x_dtype (INT4DQ_X_F32 or INT4DQ_X_F16).
+ *   packed  in : [N, ceil(K/2)] bytes, scales in: [N, G] binary16, as written
+ *                by int4_quantize with the same K and group.
+ *   y       out: [M, N] binary32.
+ *   Arithmetic: products and sums in binary32 (MFMA fp16 x fp16 -> fp32 for
+ *   fp16 x; the integer codes are exact in fp16). Each output is within
+ *   2e-3 * sum_k |x[m,k] * q[n,k] * scale| of the exactly rounded result.
+ *   M = 0 is a valid no-op. The pad nibble of an odd K is never used and
+ *   x[:, K] is never read.
+ *   Errors: EINVAL if M < 0, N, K or group < 1, a pointer is NULL (when M > 0),
+ *   x_dtype is unknown, or sizes overflow.
+ */
+int int4_matmul(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                const uint16_t *scales, int64_t N, int64_t K, int64_t group,
+                float *y, void *stream);
+
+/*
+ * int4_matmul with an explicit kernel choice (INT4DQ_PATH_*), for testing
+ * one kernel against another on the same shapes. Same arguments, results
+ * and errors as int4_matmul, plus EUNSUPPORTED when the forced kernel cannot
+ * take this dtype, shape, group or alignment (the reason is in
+ * int4_last_error()).
+ */
+int int4_matmul_path(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                     const uint16_t *scales, int64_t N, int64_t K, int64_t group,
+                     float *y, int path, void *stream);
+
+/*
+ * Kernel that int4_matmul would run for these arguments (an INT4DQ_PATH_*
+ * other than AUTO), or -1 if the arguments are invalid. Enqueues nothing.
+ */
+int int4_matmul_select(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                       const uint16_t *scales, int64_t N, int64_t K, int64_t group,
+                       const float *y);
+
+/* Text describing the last non-OK status on the calling thread ("" if none). */
+const char *int4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT4DQ_H */

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, computes sizes, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "int4dq.h")
+
+
+def _lib():
+    from dequantizing_gemm_amd import build as hipbuild
+    if not os.path.exists(hipbuild.LIB):
+        hipbuild.build()
+    import dequantizing_gemm_amd as dq
+    return dq
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(int4_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    assert _declared() == sorted(["int4_num_groups", "int4_packed_bytes", "int4_quantize",
+                                  "int4_unpack", "int4_matmul", "int4_matmul_path",
+                                  "int4_matmul_select", "int4_last_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    dq = _lib()
+    raw = ctypes.CDLL(dq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(_declared()) == set(dq.SIGNATURES)
+
+
+def test_size_helpers():
+    dq = _lib()
+    L = dq.lib
+    assert L.int4_num_groups(301, 128) == 3 and L.int4_num_groups(256, 128) == 2
+    assert L.int4_num_groups(5, 1) == 5 and L.int4_num_groups(3, 1000) == 1
+    assert L.int4_num_groups(0, 128) == -1 and L.int4_num_groups(10, 0) == -1
+    assert L.int4_packed_bytes(48, 301) == 48 * 151 and L.int4_packed_bytes(1, 1) == 1
+    assert L.int4_packed_bytes(28672, 8192) == 117440512
+    assert L.int4_packed_bytes(0, 5) == -1 and L.int4_packed_bytes(5, -1) == -1
+    assert L.int4_packed_bytes(2 ** 62, 8) == -1                 # overflow
+    # storage for the 5 configurations' largest matrix: N*ceil(K/2) + 2*N*G
+    N, K, g = 28672, 8192, 128
+    assert L.int4_packed_bytes(N, K) + 2 * N * L.int4_num_groups(K, g) == 117440512 + 3670016
+
+
+FAKE = ctypes.c_void_p(0x1000)    # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((FAKE, 0, 8, 4, FAKE, FAKE, None), "N and K"),
+    ((FAKE, 4, 0, 4, FAKE, FAKE, None), "N and K"),
+    ((FAKE, 4, 8, 0, FAKE, FAKE, None), "group"),
+    ((None, 4, 8, 4, FAKE, FAKE, None), "non-NULL"),
+    ((FAKE, 4, 8, 4, None, FAKE, None), "non-NULL"),
+    ((FAKE, 2 ** 62, 8, 4, FAKE, FAKE, None), "overflow"),
+])
+def test_quantize_rejects(args, needle):
+    dq = _lib()
+    assert dq.lib.int4_quantize(*args) == dq.EINVAL
+    assert needle in dq.lib.int4_last_error().decode()
+
+
+def test_unpack_rejects():
+    dq = _lib()
+    assert dq.lib.int4_unpack(FAKE, -1, 8, FAKE, None) == dq.EINVAL
+    assert dq.lib.int4_unpack(None, 2, 8, FAKE, None) == dq.EINVAL
+    assert dq.lib.int4_unpack(FAKE, 2, 8, None, None) == dq.EINVAL
+    assert dq.lib.int4_unpack(FAKE, 2 ** 40, 2 ** 40, FAKE, None) == dq.EINVAL
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(M=-1), "M must be"),
+    (dict(N=0), "N and K"),
+    (dict(K=0), "N and K"),
+    (dict(group=0), "group"),
+    (dict(x_dtype=7), "x_dtype"),
+    (dict(x=None), "non-NULL"),
+    (dict(y=None), "non-NULL"),
+    (dict(packed=None), "non-NULL"),
+    (dict(scales=None, M=0), "non-NULL"),
+    (dict(M=2 ** 40, K=2 ** 30), "overflow"),
+])
+def test_matmul_rejects(kw, needle):
+    dq = _lib()
+    a = dict(x=FAKE, x_dtype=1, M=4, packed=FAKE, scales=FAKE, N=16, K=256, group=128, y=FAKE)
+    a.update(kw)
+    rc = dq.lib.int4_matmul(a["x"], a["x_dtype"], a["M"], a["packed"], a["scales"], a["N"],
+                            a["K"], a["group"], a["y"], None)
+    assert rc == dq.EINVAL
+    assert needle in dq.lib.int4_last_error().decode()
+    assert dq.lib.int4_matmul_select(a["x"], a["x_dtype"], a["M"], a["packed"], a["scales"],
+                                     a["N"], a["K"], a["group"], a["y"]) == -1
+
+
+def test_matmul_m0_is_noop_and_bad_path():
+    dq = _lib()
+    # M = 0 returns OK without touching the GPU (no pointer is dereferenced)
+    assert dq.lib.int4_matmul(None, 1, 0, FAKE, FAKE, 16, 256, 128, None, None) == dq.OK
+    assert dq.lib.int4_matmul_path(FAKE, 1, 4, FAKE, FAKE, 16, 256, 128, FAKE, 9, None) == dq.EINVAL
+
+
+def test_kernel_selection_rules():
+    """Which kernel the library picks (host logic only, no launch)."""
+    dq = _lib()
+    sel = lambda xd, M, K, g, x=0x1000, p=0x2000: dq.lib.int4_matmul_select(
+        ctypes.c_void_p(x), xd, M, ctypes.c_void_p(p), FAKE, 64, K, g, FAKE)
+    P = dq.PATHS
+    assert sel(1, 1, 4096, 128) == P["skinny"] and sel(1, 16, 4096, 128) == P["skinny"]
+    assert sel(1, 17, 4096, 128) == P["tiled"] and sel(1, 2048, 11008, 128) == P["tiled"]
+    assert sel(1, 4, 768, 64) == P["skinny"] and sel(1, 4, 768, 32) == P["skinny"]
+    assert sel(0, 4, 256, 128) == P["generic"]                 # binary32 x
+    assert sel(1, 3, 301, 128) == P["generic"]                 # odd K
+    assert sel(1, 4, 768, 96) == P["generic"]                  # group not 32/64/128k
+    assert sel(1, 4, 4096, 128, x=0x1002) == P["generic"]      # unaligned x
+    assert sel(1, 512, 4096, 256) == P["tiled"]
+
+
+def test_binding_rejects_host_tensors():
+    dq = _lib()
+    with pytest.raises(ValueError, match="GPU"):
+        dq.quantize_int4(torch.zeros(4, 8))
+    with pytest.raises(ValueError):
+        dq.int4_matmul(torch.zeros(2, 8, dtype=torch.float16), torch.zeros(4, 4, dtype=torch.uint8),
+                       torch.zeros(4, 1, dtype=torch.float16), 8, 8)

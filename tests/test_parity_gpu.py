@@ -1,0 +1,302 @@
+"""Parity of the HIP path with the CPU oracle on MI355X.
+
+Quantize, pack and unpack must match the oracle byte for byte; the matmul must
+satisfy |y_gpu - y_oracle| <= 2e-3 * sum_k |x[m,k] * q[n,k] * scale| for every
+checked output (exact zero where that sum is zero). Inputs are the seeded
+synthetic configurations of ``workloads.py`` at their full sizes; where the
+oracle cannot compute every output of a large case in seconds, it computes a
+fixed sample of rows and columns of y and the GPU result is compared there.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-3
+ORACLE_MACS = 3e8          # per matmul check; beyond this the outputs are sampled
+
+
+@pytest.fixture(scope="module")
+def dq():
+    import dequantizing_gemm_amd as dq
+    return dq
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+ALL_CASES = [(cfg.key, c) for cfg in workloads.CONFIGS.values() for c in cfg.cases]
+
+
+@functools.lru_cache(maxsize=2)
+def _case_data(key, name):
+    case = next(c for (k, c) in ALL_CASES if k == key and c.name == name)
+    w = workloads.weights(case)
+    p, s, K = oracle.quantize_int4(w, case.group)
+    return case, w, p, s
+
+
+def sample_rows_cols(M, N, K):
+    rows = np.arange(M)
+    if M > 64:
+        rng = np.random.default_rng(3)
+        mid = rng.choice(np.arange(16, M - 16), 32, replace=False)
+        rows = np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M), mid]))
+    cols = np.arange(N)
+    budget = int(ORACLE_MACS // (len(rows) * K))
+    if budget < N:
+        rng = np.random.default_rng(4)
+        mid = rng.choice(np.arange(16, N - 16), max(budget - 32, 16), replace=False)
+        cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N), mid]))
+    return rows, cols
+
+
+def check_matmul(y_gpu, x, p, s, K, g, rows=None, cols=None, what=""):
+    M, N = y_gpu.shape
+    if rows is None or cols is None:
+        rows, cols = sample_rows_cols(M, N, K)
+    xs = np.ascontiguousarray(x[rows])
+    y_ref, bound = oracle.int4_matmul(xs, p[cols], s[cols], K, g, with_bound=True)
+    yg = y_gpu[np.ix_(rows, cols)].astype(np.float64)
+    err = np.abs(yg - y_ref)
+    bad = err > TOL * bound
+    assert not bad.any(), (
+        f"{what}: {int(bad.sum())} outputs outside 2e-3*bound; worst ratio "
+        f"{float(np.max(err / np.maximum(bound, 1e-300))):.3e}")
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+# ---------------------------------------------------------------- page pins
+
+def test_p4_nibble_layout_gpu(dq):
+    say("case: drill-page layout [1,-1,7,-7] g=4 and an 8-wide copy at g=8")
+    p, s, K = dq.quantize_int4(dev(np.array([[1.0, -1.0, 7.0, -7.0]], np.float32)), 4)
+    assert host(p).tolist() == [[0xF1, 0x97]] and float(host(s)[0, 0]) == 1.0
+    p, s, K = dq.quantize_int4(dev(np.array([[1.0, -1.0, 7.0, -7.0] * 2], np.float32)), 8)
+    assert host(p).tolist() == [[0xF1, 0x97, 0xF1, 0x97]] and float(host(s)[0, 0]) == 1.0
+
+
+def test_p4_round_trip_gpu(dq):
+    for seed in range(20):
+        w = np.random.default_rng(seed).normal(size=(8, 256)).astype(np.float32)
+        p, s, K = dq.quantize_int4(dev(w), 128)
+        q = host(dq.unpack_int4(p, K)).astype(np.float32)
+        sc = np.repeat(host(s).astype(np.float32), 128, axis=1)[:, :K]
+        assert (np.abs(q * sc - w) <= sc * 0.5 + 1e-3 * sc + 1e-6).all(), seed
+
+
+def test_ties_and_clamps_gpu(dq):
+    say("case: ties to even, -8 clamp, zero groups, 8-wide and 4-wide groups")
+    T = 2.0 ** -24
+    w = np.array([[0.5, 2.5, 7.0, -7.0, -0.5, -2.5, 7.0, 1.5],
+                  [-9.5 * T, 0, 0, 0, 7.6 * T, 0, 0, 0],
+                  [0, 0, 0, 0, 1e-8, -1e-8, 0, 0]], np.float32)
+    for g in (4, 8):
+        p, s, K = dq.quantize_int4(dev(w), g)
+        pr, sr, _ = oracle.quantize_int4(w, g)
+        assert np.array_equal(host(p), pr) and np.array_equal(host(s).view(np.uint16), sr.view(np.uint16))
+    p, _, _ = dq.quantize_int4(dev(w), 4)
+    assert host(p)[0].tolist() == [0x20, 0x97, 0xE0, 0x27]
+
+
+# ---------------------------------------------------- quantize / unpack parity
+
+@pytest.mark.parametrize("key,case", ALL_CASES, ids=[f"{k}-{c.name}" for k, c in ALL_CASES])
+def test_quantize_unpack_bit_exact(dq, key, case):
+    say(f"case: quantize+unpack {key} {case.name} [{case.N},{case.K}] g={case.group}")
+    _, w, p_ref, s_ref = _case_data(key, case.name)
+    wd = dev(w)
+    p, s, K = dq.quantize_int4(wd, case.group)
+    ph, sh = host(p), host(s)
+    assert np.array_equal(sh.view(np.uint16), s_ref.view(np.uint16)), "scales differ"
+    assert np.array_equal(ph, p_ref), f"packed differs at {np.argwhere(ph != p_ref)[:3].tolist()}"
+    q = host(dq.unpack_int4(p, K))
+    assert np.array_equal(q, oracle.unpack_int4(p_ref, K))
+    if case.edge_rows:
+        assert np.all(sh.view(np.uint16)[7] == 0x0001)
+        assert np.all(ph[7, :-1] == 0x88) and ph[7, -1] == 0x08
+        assert sh.view(np.uint16)[5, 0] == 0 and np.all(ph[5, :64] == 0)
+        assert np.all(q[7] == -8)
+    del wd
+
+
+@pytest.mark.parametrize("N,K,g", [(7, 301, 1), (9, 33, 3), (5, 250, 5), (6, 200, 96),
+                                   (4, 777, 100), (3, 2048, 1024), (17, 64, 8), (33, 4104, 512),
+                                   (2, 9, 16), (1, 1, 1)])
+def test_quantize_ragged_groups(dq, N, K, g):
+    say(f"case: quantize ragged N={N} K={K} g={g}")
+    w = np.random.default_rng(N * K + g).normal(0, 0.3, size=(N, K)).astype(np.float32)
+    w[0, : min(g, K)] = 0.0
+    p, s, KK = dq.quantize_int4(dev(w), g)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    assert np.array_equal(host(p), pr) and np.array_equal(host(s).view(np.uint16), sr.view(np.uint16))
+    assert np.array_equal(host(dq.unpack_int4(p, KK)), oracle.unpack_int4(pr, KK))
+
+
+def test_quantize_unaligned_input(dq):
+    """An input that starts 4 bytes past an allocation runs the general kernels."""
+    say("case: quantize unaligned base pointer [64,512] g=128")
+    w = np.random.default_rng(8).normal(size=(64, 512)).astype(np.float32)
+    buf = torch.zeros(64 * 512 + 1, dtype=torch.float32, device=DEV)
+    buf[1:] = dev(w.reshape(-1))
+    view = buf[1:].view(64, 512)
+    p, s, K = dq.quantize_int4(view, 128)
+    pr, sr, _ = oracle.quantize_int4(w, 128)
+    assert np.array_equal(host(p), pr) and np.array_equal(host(s).view(np.uint16), sr.view(np.uint16))
+
+
+def test_unpack_exhaustive_gpu(dq):
+    b = np.arange(256, dtype=np.uint8)[None, :]
+    for K in (512, 511):
+        bb = b if K == 512 else b.copy()
+        out = host(dq.unpack_int4(dev(bb), K))
+        assert np.array_equal(out, oracle.unpack_int4(bb, K))
+    big = np.random.default_rng(6).integers(0, 256, size=(37, 1001), dtype=np.uint8)
+    for K in (2002, 2001):
+        assert np.array_equal(host(dq.unpack_int4(dev(big), K)), oracle.unpack_int4(big, K))
+
+
+def test_guard_bytes(dq):
+    """Outputs written through the C ABI into the middle of larger buffers leave
+    the surrounding canary bytes untouched (odd K pad byte included)."""
+    say("case: guard bytes around quantize/unpack/matmul outputs")
+    N, K, g, M = 21, 301, 128, 5
+    w = np.random.default_rng(2).normal(size=(N, K)).astype(np.float32)
+    x = np.random.default_rng(3).normal(size=(M, K)).astype(np.float16)
+    G, B, pad = 3, 151, 64
+    pbuf = torch.full((N * B + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((N * G + 2 * pad,), 0x5A5A, dtype=torch.int16, device=DEV)
+    obuf = torch.full((N * K + 2 * pad,), -91, dtype=torch.int8, device=DEV)
+    ybuf = torch.full((M * N + 2 * pad,), 123.0, dtype=torch.float32, device=DEV)
+    wd, xd = dev(w), dev(x)
+    L = dq.lib
+    stream = torch.cuda.current_stream().cuda_stream
+    assert L.int4_quantize(wd.data_ptr(), N, K, g, pbuf.data_ptr() + pad, sbuf.data_ptr() + 2 * pad, stream) == 0
+    assert L.int4_unpack(pbuf.data_ptr() + pad, N, K, obuf.data_ptr() + pad, stream) == 0
+    assert L.int4_matmul(xd.data_ptr(), 1, M, pbuf.data_ptr() + pad, sbuf.data_ptr() + 2 * pad, N, K, g,
+                         ybuf.data_ptr() + 4 * pad, stream) == 0
+    ph, sh, oh, yh = host(pbuf), host(sbuf), host(obuf), host(ybuf)
+    assert np.all(ph[:pad] == 0xA5) and np.all(ph[-pad:] == 0xA5)
+    assert np.all(sh[:pad] == 0x5A5A) and np.all(sh[-pad:] == 0x5A5A)
+    assert np.all(oh[:pad] == -91) and np.all(oh[-pad:] == -91)
+    assert np.all(yh[:pad] == 123.0) and np.all(yh[-pad:] == 123.0)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    assert np.array_equal(ph[pad:-pad].reshape(N, B), pr)
+    check_matmul(yh[pad:-pad].reshape(M, N), x, pr, sr, K, g, what="guarded")
+
+
+# ------------------------------------------------------------- matmul parity
+
+MM_CASES = [(k, c, M) for (k, c) in ALL_CASES for M in c.Ms]
+
+
+@pytest.mark.parametrize("key,case,M", MM_CASES, ids=[f"{k}-{c.name}-M{M}" for k, c, M in MM_CASES])
+def test_matmul_configs(dq, key, case, M):
+    _, w, p_ref, s_ref = _case_data(key, case.name)
+    x = workloads.activations(M, case.K, case.x_dtype)
+    pd, sd, xd = dev(p_ref), dev(s_ref), dev(x)
+    path = dq.matmul_select(xd, pd, sd, case.K, case.group)
+    say(f"case: matmul {key} {case.name} [{case.N},{case.K}] g={case.group} M={M} "
+        f"x={case.x_dtype} kernel={path}")
+    y = host(dq.int4_matmul(xd, pd, sd, case.K, case.group))
+    r = check_matmul(y, x, p_ref, s_ref, case.K, case.group, what=f"{key}/{case.name}/M{M}")
+    say(f"  max |err|/bound = {r:.2e}")
+
+
+@pytest.mark.parametrize("N,K,g,M", [(200, 768, 64, 1), (200, 768, 32, 5), (48, 4096, 128, 16),
+                                     (136, 1024, 256, 3), (50, 512, 128, 200), (300, 1024, 128, 130),
+                                     (129, 256, 32, 257), (64, 2048, 64, 100)])
+def test_matmul_kernels_agree(dq, N, K, g, M):
+    """Every kernel that takes a shape matches the oracle on it (ragged M and N tails)."""
+    w = np.random.default_rng(N + K).normal(0, 0.02, size=(N, K)).astype(np.float32)
+    x = np.random.default_rng(M).normal(size=(M, K)).astype(np.float16)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    pd, sd, xd = dev(pr), dev(sr), dev(x)
+    for path in ("generic", "skinny", "tiled"):
+        if path == "skinny" and M > 16:
+            continue
+        say(f"case: kernel {path} N={N} K={K} g={g} M={M}")
+        y = host(dq.int4_matmul_path(xd, pd, sd, K, g, path))
+        check_matmul(y, x, pr, sr, K, g, what=path)
+
+
+def test_matmul_fp32_x(dq):
+    say("case: binary32 activations, c1/c2 shapes and a [40,1000] g=7 matrix")
+    for (N, K, g, M) in [(64, 256, 128, 4), (48, 301, 128, 3), (40, 1000, 7, 6)]:
+        w = np.random.default_rng(K).normal(size=(N, K)).astype(np.float32)
+        x = np.random.default_rng(M).normal(size=(M, K)).astype(np.float32)
+        pr, sr, _ = oracle.quantize_int4(w, g)
+        y = host(dq.int4_matmul(dev(x), dev(pr), dev(sr), K, g))
+        check_matmul(y, x, pr, sr, K, g, what=f"fp32 {N}x{K}")
+
+
+def test_matmul_one_hot_exact(dq):
+    """x = identity gives y = (q * scale)^T exactly: one exact product per output.
+    Tiled kernel at M = K = 256 and 4096; skinny kernel on 16-row slices."""
+    for (N, K, g) in [(48, 256, 128), (64, 4096, 128), (32, 768, 64), (32, 768, 32)]:
+        say(f"case: one-hot N={N} K={K} g={g}")
+        w = np.random.default_rng(K).normal(size=(N, K)).astype(np.float32)
+        pr, sr, _ = oracle.quantize_int4(w, g)
+        what = (oracle.unpack_int4(pr, K).astype(np.float64) *
+                np.repeat(sr.astype(np.float64), g, 1)[:, :K]).T
+        eye = dev(np.eye(K, dtype=np.float16))
+        pd, sd = dev(pr), dev(sr)
+        y = host(dq.int4_matmul_path(eye, pd, sd, K, g, "tiled"))
+        assert np.array_equal(y.astype(np.float64), what)
+        for r0 in (0, K // 2, K - 16):
+            ys = host(dq.int4_matmul_path(eye[r0:r0 + 16].contiguous(), pd, sd, K, g, "skinny"))
+            assert np.array_equal(ys.astype(np.float64), what[r0:r0 + 16])
+
+
+def test_matmul_zero_and_empty(dq):
+    w = np.random.default_rng(1).normal(size=(64, 512)).astype(np.float32)
+    pr, sr, _ = oracle.quantize_int4(w, 128)
+    pd, sd = dev(pr), dev(sr)
+    for M in (1, 16, 300):
+        for path in ("skinny", "tiled", "generic"):
+            if path == "skinny" and M > 16:
+                continue
+            y = host(dq.int4_matmul_path(torch.zeros(M, 512, dtype=torch.float16, device=DEV), pd, sd, 512, 128, path))
+            assert np.all(y == 0)
+    y = dq.int4_matmul(torch.zeros(0, 512, dtype=torch.float16, device=DEV), pd, sd, 512, 128)
+    assert tuple(y.shape) == (0, 64)
+
+
+def test_matmul_deterministic(dq):
+    """No atomics: two calls give the same bits."""
+    w = np.random.default_rng(1).normal(0, 0.02, size=(1024, 4096)).astype(np.float32)
+    pr, sr, _ = oracle.quantize_int4(w, 128)
+    pd, sd = dev(pr), dev(sr)
+    for M in (1, 16, 512):
+        x = dev(np.random.default_rng(M).normal(size=(M, 4096)).astype(np.float16))
+        a = host(dq.int4_matmul(x, pd, sd, 4096, 128))
+        b = host(dq.int4_matmul(x, pd, sd, 4096, 128))
+        assert np.array_equal(a, b)
+
+
+def test_rows_independent(dq):
+    """Row m of an M-row call equals the 1-row call on x[m] within tolerance."""
+    case, w, pr, sr = _case_data("c4", "q_proj_4096x4096")
+    x = workloads.activations(512, 4096)
+    pd, sd = dev(pr), dev(sr)
+    big = host(dq.int4_matmul(dev(x), pd, sd, 4096, 128))
+    for m in (0, 255, 511):
+        one = host(dq.int4_matmul(dev(x[m:m + 1]), pd, sd, 4096, 128))
+        _, bound = oracle.int4_matmul(x[m:m + 1], pr, sr, 4096, 128, with_bound=True)
+        assert np.all(np.abs(one[0] - big[m]) <= 2 * TOL * bound[0])
