@@ -59,9 +59,9 @@ int check_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
   return INT4DQ_OK;
 }
 
-int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t K,
-                int64_t group) {
-  if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, K, group)) return INT4DQ_PATH_SKINNY;
+int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t N,
+                int64_t K, int64_t group) {
+  if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_SKINNY;
   if (!int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group)) return INT4DQ_PATH_TILED;
   return INT4DQ_PATH_GENERIC;
 }
@@ -110,11 +110,11 @@ int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packe
   if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_TILED)
     return fail(INT4DQ_EINVAL, "int4_matmul_path: unknown path %d", path);
   if (M == 0) return ok();
-  if (path == INT4DQ_PATH_AUTO) path = choose_path(x, x_dtype, M, packed, K, group);
+  if (path == INT4DQ_PATH_AUTO) path = choose_path(x, x_dtype, M, packed, N, K, group);
   const hipStream_t s = (hipStream_t)stream;
   switch (path) {
     case INT4DQ_PATH_SKINNY: {
-      const char* why = int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, K, group);
+      const char* why = int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
       return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, N, K, group, y, s),
                         "int4_matmul skinny launch");
@@ -141,7 +141,7 @@ int int4_matmul_select(const void* x, int x_dtype, int64_t M, const uint8_t* pac
                        const uint16_t* scales, int64_t N, int64_t K, int64_t group,
                        const float* y) {
   if (check_matmul(x, x_dtype, M, packed, scales, N, K, group, y) != INT4DQ_OK) return -1;
-  return choose_path(x, x_dtype, M, packed, K, group);
+  return choose_path(x, x_dtype, M, packed, N, K, group);
 }
 
 const char* int4_last_error(void) { return g_err; }

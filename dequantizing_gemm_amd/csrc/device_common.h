@@ -35,37 +35,39 @@ __device__ __forceinline__ int sx4(uint32_t v) { return (int)(v ^ 8u) - 8; }
 
 // "Spread" order: from one word d of 8 codes c0..c7 produce four fp16 pairs
 //   (c0, c4), (c1, c5), (c2, c6), (c3, c7).
-// 10 VALU ops per 8 codes. The matching activations must be arranged in the
-// same order (see spread_perm_x).
+// Since the masked code bits and the exponent bits 0x6400 do not overlap,
+// ((d & mask) ^ 8-per-code) | 0x6400 == (d & mask) ^ (0x6400 | 8-per-code):
+// one AND-XOR (a single v_bitop3_b32 on gfx950) per pair, plus one packed fp16
+// op per pair and one shift per word -- 9 VALU ops per 8 codes. The matching
+// activations must be arranged in the same order (see spread_perm_x).
 __device__ __forceinline__ void codes_to_half_spread(uint32_t d, half2_t out[4]) {
-  const uint32_t u = d ^ 0x88888888u;
-  const uint32_t v = u >> 8;
+  const uint32_t v = d >> 8;
   const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2_t bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  out[0] = __builtin_bit_cast(half2_t, (u & 0x000F000Fu) | 0x64006400u) + bias;
+  out[0] = __builtin_bit_cast(half2_t, (d & 0x000F000Fu) ^ 0x64086408u) + bias;
   out[1] = __builtin_elementwise_fma(
-      __builtin_bit_cast(half2_t, (u & 0x00F000F0u) | 0x64006400u), sixteenth, bias16);
-  out[2] = __builtin_bit_cast(half2_t, (v & 0x000F000Fu) | 0x64006400u) + bias;
+      __builtin_bit_cast(half2_t, (d & 0x00F000F0u) ^ 0x64806480u), sixteenth, bias16);
+  out[2] = __builtin_bit_cast(half2_t, (v & 0x000F000Fu) ^ 0x64086408u) + bias;
   out[3] = __builtin_elementwise_fma(
-      __builtin_bit_cast(half2_t, (v & 0x00F000F0u) | 0x64006400u), sixteenth, bias16);
+      __builtin_bit_cast(half2_t, (v & 0x00F000F0u) ^ 0x64806480u), sixteenth, bias16);
 }
 
 // Natural order: from one word d of 8 codes produce (c0,c1), (c2,c3), (c4,c5),
 // (c6,c7). Byte b (codes 2b, 2b+1) is copied into both 16-bit halves with a
-// byte permute, then the low half keeps bits 0..3 and the high half bits 4..7.
-// 13 VALU ops per 8 codes.
+// byte permute, then the low half keeps bits 0..3 and the high half bits 4..7
+// (AND-XOR with the exponent and the flipped sign bits, as above).
+// 12 VALU ops per 8 codes.
 __device__ __forceinline__ void codes_to_half_natural(uint32_t d, half2_t out[4]) {
-  const uint32_t u = d ^ 0x88888888u;
   const half2_t scale = {(_Float16)1.0f, (_Float16)0.0625f};
   const half2_t bias = {(_Float16)-1032.0f, (_Float16)-72.0f};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    // v_perm_b32 selector: result bytes = [u.b, 0, u.b, 0]
+    // v_perm_b32 selector: result bytes = [d.b, 0, d.b, 0]
     const uint32_t sel = (uint32_t)b | 0x0C000C00u | ((uint32_t)b << 16);
-    const uint32_t dup = __builtin_amdgcn_perm(0u, u, sel);
+    const uint32_t dup = __builtin_amdgcn_perm(0u, d, sel);
     out[b] = __builtin_elementwise_fma(
-        __builtin_bit_cast(half2_t, (dup & 0x00F0000Fu) | 0x64006400u), scale, bias);
+        __builtin_bit_cast(half2_t, (dup & 0x00F0000Fu) ^ 0x64806408u), scale, bias);
   }
 }
 
@@ -87,6 +89,14 @@ __device__ __forceinline__ half8_t as_half8(const half2_t h[4]) {
   w.z = __builtin_bit_cast(uint32_t, h[2]);
   w.w = __builtin_bit_cast(uint32_t, h[3]);
   return __builtin_bit_cast(half8_t, w);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// (lgkmcnt) and then for all waves. Unlike __syncthreads() it does not wait
+// for outstanding global loads, so weight prefetches stay in flight across it.
+// The "memory" clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {

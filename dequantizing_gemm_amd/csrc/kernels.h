@@ -20,7 +20,7 @@ hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const ui
 
 // nullptr if the kernel takes these arguments, else the reason it does not.
 const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
-                                      const uint8_t* packed, int64_t K, int64_t group);
+                                      const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
                                 float* y, hipStream_t stream);

@@ -9,38 +9,38 @@
 // memory; the takeaways put the bottleneck in memory bandwidth.)
 //
 // At M <= 16 every packed byte is used 2*M times, far below the machine's
-// flop/byte balance, so the kernel is built to stream the packed weights
-// once at full bandwidth and spend as few vector-ALU ops per byte as possible:
+// flop/byte balance. The kernel streams the packed weights once and keeps
+// each block's critical path short, because at these sizes (1-120 MB per
+// call) a launch is a single round of loads and its latency chain, not a
+// steady stream:
 //
 //  * The contraction runs on the matrix cores: v_mfma_f32_16x16x32_f16 with
-//    the 16 weight rows of a block as B (16 columns) and the M <= 16
-//    activation rows as A (rows >= M are zero). The integer codes are exact in
-//    fp16, products are exact, and sums are fp32.
-//  * A lane never converts codes one by one: a 32-bit word of 8 codes becomes
-//    four exact fp16 pairs with one AND-OR and one packed fp16 op per pair
-//    (codes_to_half_spread, 10 VALU ops per 8 codes). That routine pairs code c
-//    with code c+4, so the activations are staged into LDS once per block in
-//    the same order, and every A fragment is then one 16-byte LDS read.
-//  * Lane l of a wavefront owns weight row (l mod 16) and one contiguous
-//    quarter of each K-block (KB = 128 codes for group sizes that are
-//    multiples of 128, else KB = group = 64 or 32), i.e. one 16-byte (KB=128)
-//    load per K-block: 16 rows x 64 contiguous bytes per wavefront load.
-//    The block's waves take interleaved K-blocks, so at any moment a block
-//    reads neighbouring stretches of its 16 rows.
-//  * Per K-block each MFMA chain starts from zero, and the group's scale is
+//    16 weight rows as B (one per lane column) and the activation rows as A.
+//    Lanes of A rows >= M load row M-1 again: those output rows are computed
+//    and discarded, so nothing has to be zeroed or masked. The integer codes
+//    are exact in fp16, products are exact, sums are fp32.
+//  * A 32-bit word of 8 codes becomes four exact fp16 pairs in natural order
+//    (codes_to_half_natural, 12 VALU ops per 8 codes), so each lane's A
+//    fragment is 8 consecutive activations: one 16-byte load straight from
+//    global memory (x is tiny and stays in L2). No LDS staging and no barrier
+//    stand between a wave's loads and its first MFMA.
+//  * Lane l owns weight row (l mod 16) and one quarter of each K-block
+//    (KB = 128 codes for group sizes 128 * 2^p, else KB = group = 64 or 32):
+//    one 16-byte weight load per K-block for KB = 128, and a wavefront load
+//    covers 16 rows x 64 contiguous bytes. The block's waves take interleaved
+//    K-blocks. Every wave issues all loads of its share (U K-blocks: weights,
+//    scales, activations) before it waits for any of them.
+//  * Per K-block the MFMA chain starts from zero and the group's scale is
 //    applied to that fp32 partial on the output column (lane l holds column
-//    l mod 16) -- the integer-first order of the statement.
-//  * The waves' partial tiles are summed through LDS at the end; no atomics,
-//    results are deterministic.
+//    l mod 16): the integer-first order of the statement.
+//  * The waves' partial 16x16 tiles are summed through LDS at the end (the
+//    only barrier); no atomics, results are deterministic.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace int4dq {
 
 namespace {
-
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyLdsX = 48 * 1024;   // bytes of LDS for the staged activations
 
 template <int KB> struct WLoad;
 template <> struct WLoad<128> { typedef u32x4_t T; };
@@ -58,67 +58,139 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 
 }  // namespace
 
-// U = K-blocks whose weight loads a wave issues before consuming any of them.
-template <int KB, int U>
-__global__ __launch_bounds__(kSkinnyWaves * 64) void matmul_skinny_kernel(
+// WAVES waves per block, each handling up to U K-blocks (K-blocks j = wave,
+// wave + WAVES, ...; the launch guarantees WAVES * U >= K / KB).
+// MR > 0 (M <= MR <= 4): the wave stages its own slice of x (MR rows x U
+// K-blocks; rows >= M repeat row M-1) into a wave-private LDS region in the
+// spread order and expands the codes with codes_to_half_spread (9 VALU ops per
+// 8 codes). MR == 0: each lane loads its A fragments from global memory in
+// natural order (codes_to_half_natural, 12 ops per 8 codes). Staging moves one
+// copy of x per wave instead of one 16-byte load per lane and MFMA, and is used
+// for small M where the slices fit LDS.
+template <int KB, int WAVES, int U, int MR>
+__global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int64_t N, int64_t K, int64_t group, int64_t G,
-    int64_t KC, float* __restrict__ y) {
+    const uint16_t* __restrict__ scales, int N, int K, int G, int kb_shift,
+    float* __restrict__ y) {
   typedef typename WLoad<KB>::T wvec_t;
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
-  // Dynamic LDS: wave partials [waves][64][4] fp32, then the staged x chunk.
+  constexpr int XB = U < 4 ? U : 4;           // K-blocks per batch of direct x loads
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float* red = reinterpret_cast<float*>(lds);
-  _Float16* xs = reinterpret_cast<_Float16*>(lds + kSkinnyWaves * 64 * 4 * sizeof(float));
+  float* red = reinterpret_cast<float*>(lds);                  // [WAVES][64][4]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 15, h = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t nrow = (n0 + col < N) ? n0 + col : N - 1;     // tail rows: read, discard
-  const uint8_t* prow = packed + nrow * (K >> 1) + h * (KB / 8);
-  const uint16_t* srow = scales + nrow * G;
-  const int xstride = (int)KC + 8;                             // halves; +16 B vs bank conflicts
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int n0 = blockIdx.x * 16;
+  const int nrow = (n0 + col < N) ? n0 + col : N - 1;       // tail rows: read, discard
+  const int xrow = col < M ? col : M - 1;                    // rows >= M: discarded
+  const uint8_t* prow = packed + (int64_t)nrow * (K >> 1) + h * (KB / 8);
+  const uint16_t* srow = scales + (int64_t)nrow * G;
+  const int nkb = K / KB;
 
-  for (int64_t kc0 = 0; kc0 < K; kc0 += KC) {
-    const int kcn = (int)((K - kc0) < KC ? (K - kc0) : KC);
-    __syncthreads();
-    const int pieces = kcn / 8;
-    for (int p = tid; p < M * pieces; p += kSkinnyWaves * 64) {
-      const int m = p / pieces, c = p - m * pieces;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)m * K + kc0 + 8 * c);
-      *reinterpret_cast<u32x4_t*>(xs + m * xstride + 8 * c) = spread_perm_x(v);
+  // Weight and scale loads of the wave's share, K-block by K-block. They are
+  // issued after the (smaller) x staging loads, so that each K-block's
+  // compute waits only for its own weights (loads return in order).
+  wvec_t wv[U];
+  uint32_t sraw[U];
+  // Straight-line, unconditional loads: a K-block index past the end is
+  // clamped to the wave's last valid one (the value is loaded and ignored), so
+  // no branch splits the sequence and no use is scheduled between the loads.
+  // Scales first: the compiler converts them to fp32 as soon as they arrive,
+  // and with the weights issued after them that wait does not cover the weights.
+  auto load_w = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
+      sraw[u] = srow[j >> kb_shift];
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
+      wv[u] = __builtin_nontemporal_load(reinterpret_cast<const wvec_t*>(prow + j * (KB / 2)));
+    }
+  };
 
-    const int nkb = kcn / KB;
-    const _Float16* xa = xs + col * xstride + h * (KB / 4);
-    for (int j0 = wave; j0 < nkb; j0 += kSkinnyWaves * U) {
-      wvec_t wv[U];
-      float sf[U];
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (MR > 0) {
+    // Wave-private region: [MR][U][KB] halves, spread order within each 8.
+    _Float16* xw = reinterpret_cast<_Float16*>(lds + WAVES * 64 * 4 * sizeof(float)) +
+                   (size_t)wave * MR * U * KB;
+    constexpr int PPB = KB / 8;                // 16-byte pieces per K-block row
+    constexpr int BPI = 64 / PPB;              // K-blocks covered by one wave load
+    constexpr int XR = (U + BPI - 1) / BPI;    // wave loads per x row
+    // Straight-line: all x loads, then the weights, then the LDS writes (which
+    // wait for x only). Indices past the end are clamped, values unused.
+    u32x4_t xv[MR][XR];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kSkinnyWaves;
-        if (j < nkb) {
-          const int64_t kb = kc0 + (int64_t)j * KB;
-          wv[u] = __builtin_nontemporal_load(reinterpret_cast<const wvec_t*>(prow + (kb >> 1)));
-          sf[u] = half_bits_to_float(srow[kb / group]);
-        }
+    for (int mm = 0; mm < MR; ++mm)
+#pragma unroll
+      for (int r = 0; r < XR; ++r) {
+        const int u = r * BPI + lane / PPB, c = lane % PPB;
+        const int uu = u < U ? u : U - 1;
+        const int j = wave + uu * WAVES < nkb ? wave + uu * WAVES : nkb - 1;
+        const int m = mm < M ? mm : M - 1;
+        xv[mm][r] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)m * K + j * KB + 8 * c);
       }
+    load_w();
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kSkinnyWaves;
-        if (j < nkb) {
-          float4_t dg = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mm = 0; mm < MR; ++mm)
+#pragma unroll
+      for (int r = 0; r < XR; ++r) {
+        const int u = r * BPI + lane / PPB, c = lane % PPB;
+        if (u < U)
+          *reinterpret_cast<u32x4_t*>(xw + (mm * U + u) * KB + 8 * c) = spread_perm_x(xv[mm][r]);
+      }
+    // A wave's LDS operations complete in order, so no barrier is needed
+    // between these writes and the reads below; keep the compiler from
+    // moving the reads above the writes.
+    __builtin_amdgcn_wave_barrier();
+    const _Float16* xa = xw + (col < MR ? col : MR - 1) * U * KB + h * (KB / 4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (wave + u * WAVES < nkb) {
+        half8_t a[DW];
+#pragma unroll
+        for (int i = 0; i < DW; ++i) a[i] = *reinterpret_cast<const half8_t*>(xa + u * KB + 8 * i);
+        float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < DW; ++i) {
+          half2_t hw[4];
+          codes_to_half_spread(word_at<KB>(wv[u], i), hw);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], as_half8(hw), d, 0, 0, 0);
+        }
+        acc += half_bits_to_float((uint16_t)sraw[u]) * d;
+      }
+    }
+  } else {
+    // Activation fragments straight from global memory (L2 hits), natural
+    // order, in batches of XB K-blocks to bound register use.
+    const _Float16* xp = x + (int64_t)xrow * K + h * (KB / 4) + wave * KB;
+    load_w();
+    half8_t xa[XB][DW];
+    auto load_x = [&](int b) {
+#pragma unroll
+      for (int v = 0; v < XB; ++v)
+        if (b + v < U && wave + (b + v) * WAVES < nkb)
+#pragma unroll
+          for (int i = 0; i < DW; ++i)
+            xa[v][i] = *reinterpret_cast<const half8_t*>(xp + (b + v) * (WAVES * KB) + 8 * i);
+    };
+#pragma unroll
+    for (int b = 0; b < U; b += XB) {
+      load_x(b);
+#pragma unroll
+      for (int v = 0; v < XB; ++v) {
+        const int u = b + v;
+        if (u < U && wave + u * WAVES < nkb) {
+          float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int i = 0; i < DW; ++i) {
             half2_t hw[4];
-            codes_to_half_spread(word_at<KB>(wv[u], i), hw);
-            half8_t a = {};
-            if (col < M) a = *reinterpret_cast<const half8_t*>(xa + j * KB + 8 * i);
-            dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_half8(hw), dg, 0, 0, 0);
+            codes_to_half_natural(word_at<KB>(wv[u], i), hw);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[v][i], as_half8(hw), d, 0, 0, 0);
           }
-          acc += sf[u] * dg;
+          acc += half_bits_to_float((uint16_t)sraw[u]) * d;
         }
       }
     }
@@ -132,55 +204,91 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void matmul_skinny_kernel(
     const int src = ((m >> 2) * 16 + nn) * 4 + (m & 3);
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kSkinnyWaves; ++w) s += red[w * 256 + src];
+    for (int w = 0; w < WAVES; ++w) s += red[w * 256 + src];
     if (n0 + nn < N) y[(int64_t)m * N + n0 + nn] = s;
   }
 }
 
-// KB for a group size, or 0 if the skinny kernel does not take it.
+// KB for a group size, or 0 if the skinny kernel does not take it
+// (group / KB must be a power of two: the scale index is a shift).
 static int skinny_kb(int64_t group) {
-  if (group % 128 == 0) return 128;
-  if (group == 64) return 64;
-  if (group == 32) return 32;
+  if (group == 32 || group == 64) return (int)group;
+  if (group % 128 == 0 && ((group / 128) & (group / 128 - 1)) == 0) return 128;
   return 0;
 }
 
+// Largest K-block count one launch handles (16 waves x 8 K-blocks).
+constexpr int kSkinnyMaxKB = 16 * 8;
+
 const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
-                                      const uint8_t* packed, int64_t K, int64_t group) {
+                                      const uint8_t* packed, int64_t N, int64_t K,
+                                      int64_t group) {
   if (x_dtype != 1) return "skinny kernel takes binary16 activations only";
   if (M > 16) return "skinny kernel takes M <= 16";
   const int KB = skinny_kb(group);
-  if (KB == 0) return "skinny kernel takes group 32, 64 or a multiple of 128";
+  if (KB == 0) return "skinny kernel takes group 32, 64 or 128 times a power of two";
   if (K % KB != 0) return "skinny kernel needs K to be a multiple of min(group, 128)";
+  if (K / KB > kSkinnyMaxKB) return "skinny kernel takes K <= 128 * min(group, 128)";
+  if (N >= (1ll << 30)) return "skinny kernel needs N below 2^30";
   if ((uintptr_t)x % 16 || (uintptr_t)packed % 16) return "skinny kernel needs 16-byte aligned x and packed";
   return nullptr;
+}
+
+// Bytes of LDS a launch uses: the reduction buffer, plus the wave-private x
+// slices of MR rows when they are staged.
+static size_t skinny_lds(int waves, int U, int KB, int MR) {
+  return (size_t)waves * 64 * 4 * sizeof(float) + (size_t)waves * MR * U * KB * 2;
+}
+constexpr size_t kSkinnyLdsMax = 64 * 1024;
+
+template <int KB, int WAVES, int U, int MR>
+static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
+                      int N, int K, int G, int kbs, float* y, hipStream_t stream) {
+  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR>), dim3((unsigned)((N + 15) / 16)),
+                     dim3(WAVES * 64), skinny_lds(WAVES, U, KB, MR), stream, x, M, packed, scales,
+                     N, K, G, kbs, y);
+}
+
+template <int KB, int WAVES, int U>
+static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
+                       int N, int K, int G, int kbs, float* y, hipStream_t stream) {
+  const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
+  if (M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax)
+    launch_mr<KB, WAVES, U, 0>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else if (MR == 1)
+    launch_mr<KB, WAVES, U, 1>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else if (MR == 2)
+    launch_mr<KB, WAVES, U, 2>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else
+    launch_mr<KB, WAVES, U, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
+}
+
+// Waves per block and K-blocks per wave for nkb K-blocks: the fewest waves
+// (<= 16) that cover K with at most 4 K-blocks each, else 16 waves with up to 8.
+template <int KB>
+static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
+                      int N, int K, int G, int kbs, float* y, hipStream_t stream) {
+  const int nkb = K / KB;
+  if (nkb <= 4 * 2) launch_one<KB, 4, 2>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else if (nkb <= 4 * 4) launch_one<KB, 4, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else if (nkb <= 8 * 4) launch_one<KB, 8, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else if (nkb <= 16 * 4) launch_one<KB, 16, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else if (nkb <= 16 * 6) launch_one<KB, 16, 6>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  else launch_one<KB, 16, 8>(x, M, packed, scales, N, K, G, kbs, y, stream);
 }
 
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
                                 float* y, hipStream_t stream) {
   const int KB = skinny_kb(group);
-  const int64_t G = (K + group - 1) / group;
-  // Largest multiple of KB whose M padded rows fit the staging buffer.
-  int64_t KC = ((int64_t)(kSkinnyLdsX / 2) / M - 8) / KB * KB;
-  if (KC > K) KC = K;
-  const size_t lds = kSkinnyWaves * 64 * 4 * sizeof(float) + (size_t)M * (KC + 8) * 2;
-  const dim3 grid((unsigned)((N + 15) / 16)), block(kSkinnyWaves * 64);
+  const int G = (int)((K + group - 1) / group);
+  int kbs = 0;
+  while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);
-  const int Mi = (int)M;
   switch (KB) {
-    case 128:
-      hipLaunchKernelGGL((matmul_skinny_kernel<128, 4>), grid, block, lds, stream, xh, Mi, packed,
-                         scales, N, K, group, G, KC, y);
-      break;
-    case 64:
-      hipLaunchKernelGGL((matmul_skinny_kernel<64, 4>), grid, block, lds, stream, xh, Mi, packed,
-                         scales, N, K, group, G, KC, y);
-      break;
-    default:
-      hipLaunchKernelGGL((matmul_skinny_kernel<32, 8>), grid, block, lds, stream, xh, Mi, packed,
-                         scales, N, K, group, G, KC, y);
-      break;
+    case 128: launch_kb<128>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, stream); break;
+    case 64: launch_kb<64>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, stream); break;
+    default: launch_kb<32>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, stream); break;
   }
   return hipGetLastError();
 }

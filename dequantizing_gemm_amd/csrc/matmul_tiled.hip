@@ -118,9 +118,9 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   const int64_t nkb = K / KB;
   fetch(0);
   for (int64_t t = 0; t < nkb; ++t) {
-    __syncthreads();                                  // previous K-block's readers done
+    lds_barrier();                                    // previous K-block's readers done
     stage();
-    __syncthreads();
+    lds_barrier();                                    // (next K-block's loads stay in flight)
     if (t + 1 < nkb) fetch((t + 1) * KB);             // next loads overlap the MFMAs
 
     float4_t dg[4][4];
