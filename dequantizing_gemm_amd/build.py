@@ -36,11 +36,16 @@ HIPFLAGS = [
 SOURCES = ["api.cpp", "quantize.hip", "unpack.hip", "matmul_generic.hip", "matmul_skinny.hip",
            "matmul_tiled.hip"]
 
+# The tiled kernel rescales its MFMA accumulators with VALU ops at every group
+# boundary; selecting the VGPR form of the MFMA instructions keeps the
+# accumulators in VGPRs instead of AGPRs (no accvgpr read/write around them).
+EXTRA = {"matmul_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *HIPFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *HIPFLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -247,7 +247,11 @@ def test_matmul_fp32_x(dq):
 
 
 def test_matmul_one_hot_exact(dq):
-    """x = identity gives y = (q * scale)^T exactly: one exact product per output.
+    """x = identity gives y = (q * scale)^T: one product per output. The skinny
+    kernel forms each group's integer sum and scales it, so it is exact; the
+    tiled kernel keeps a running scale and multiplies its accumulator by
+    s_prev / s_new at group boundaries, which adds an fp32 rounding per group,
+    so it is checked to 1e-6 relative (an index error would be O(1)).
     Tiled kernel at M = K = 256 and 4096; skinny kernel on 16-row slices."""
     for (N, K, g) in [(48, 256, 128), (64, 4096, 128), (32, 768, 64), (32, 768, 32)]:
         say(f"case: one-hot N={N} K={K} g={g}")
@@ -258,7 +262,7 @@ def test_matmul_one_hot_exact(dq):
         eye = dev(np.eye(K, dtype=np.float16))
         pd, sd = dev(pr), dev(sr)
         y = host(dq.int4_matmul_path(eye, pd, sd, K, g, "tiled"))
-        assert np.array_equal(y.astype(np.float64), what)
+        assert np.all(np.abs(y.astype(np.float64) - what) <= 1e-6 * np.abs(what))
         for r0 in (0, K // 2, K - 16):
             ys = host(dq.int4_matmul_path(eye[r0:r0 + 16].contiguous(), pd, sd, K, g, "skinny"))
             assert np.array_equal(ys.astype(np.float64), what[r0:r0 + 16])
