@@ -7,22 +7,24 @@
 // group's scale on each output column. Full-precision weights never reach
 // memory ("Build a Blockwise INT4 Inference Engine", architecture overview:
 // the fusion boundary); here they exist only as exact fp16 integer codes in
-// the registers that feed the matrix cores.
+// LDS, one sub-step at a time.
 //
 // Block tile 256 (rows of x) x 128 (weight rows), 256 threads = 2 x 2
 // wavefronts, each owning 128 x 64 outputs as 4 x 2 tiles of
 // v_mfma_f32_32x32x16_f16 (fp32 accumulation, 128 accumulator VGPRs).
 // K advances in sub-steps of BK = min(group, 64) codes:
 //  * x tiles [256 x BK] fp16 go global -> LDS by DMA (global_load_lds, 16 B
-//    per lane, no VGPRs) into a 3-stage ring, two sub-steps ahead. Each 128-B
-//    row holds 8 16-byte pieces stored at piece ^ (row & 7), so the 32 rows an
-//    MFMA operand read touches fall in distinct banks.
-//  * The weights never touch LDS: each lane loads the 16 packed bytes of its
-//    weight row that its B fragments need (two sub-steps ahead, in registers)
-//    and expands each 32-bit word to 8 exact fp16 codes right before the MFMA
-//    (codes_to_half_natural). The k order inside a sub-step is a fixed
-//    permutation shared by A and B (lane half h, k-step s: codes 32h + 8s ..),
-//    which leaves the dot product unchanged.
+//    per lane, no VGPRs) into a 3-stage ring, two sub-steps ahead.
+//  * The block's packed weights [128 x BK/2 bytes] are loaded to registers
+//    three sub-steps ahead; one sub-step ahead each thread expands its 16 (or
+//    8) bytes to exact fp16 codes (codes_to_half_natural) into a 2-stage LDS
+//    ring, so each code is expanded once per block, not once per wave.
+//  * Both LDS tiles use rows of BK halves made of 16-byte pieces; logical
+//    piece c of row r is stored at c ^ ((r / (16 / pieces)) % pieces). The 16
+//    rows one pass of an MFMA operand read touches then cover all 64 banks.
+//  * The k order inside a sub-step is a fixed permutation shared by A and B
+//    (lane half h, k-step s: piece (BK / 16) h + s), which leaves the dot
+//    product unchanged.
 //  * Integer-first scaling with one accumulator set: the accumulator holds
 //    (sum of finished groups' scaled partials) / (scale of the current group);
 //    at each group boundary it is multiplied by s_prev / s_new for its column,
@@ -30,6 +32,8 @@
 //    value is multiplied by the last scale. A zero scale (a group of zero
 //    codes) leaves the running scale unchanged. Mathematically this is
 //    sum_g s_g * (x . q_g); the ratio multiply adds one fp32 rounding per group.
+//    Which sub-steps open a group is a template parameter, so every sub-step is
+//    one branch-free block that the scheduler can interleave with the MFMAs.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -49,69 +53,113 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 }  // namespace
 
-// BK: codes per sub-step (32 or 64). Requires K % BK == 0 and group = BK << gshift.
-template <int BK>
+// BK: codes per sub-step (32 or 64); K % BK == 0. SPG: sub-steps per group
+// (1, 2 or 4), or 0 for any power of two 2^gshift, decided at run time.
+template <int BK, int SPG>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int gshift,
     float* __restrict__ y) {
+  static_assert(SPG == 0 || SPG == 1 || SPG == 2 || SPG == 4, "sub-steps per group");
   constexpr int KS = BK / 16;                 // MFMA k-steps per sub-step
-  constexpr int PIECES = BK / 8;              // 16-byte pieces per x row per sub-step
-  constexpr int STAGE_HALVES = kBM * BK;      // one x stage
-  constexpr int XDMA = kBM * PIECES / 64 / 4; // DMA instructions per wave per stage
+  constexpr int PIECES = BK / 8;              // 16-byte pieces per row per sub-step
+  constexpr int RPB = 16 / PIECES;            // rows per 256-byte LDS bank period
+  constexpr int A_HALVES = kBM * BK;          // one x stage
+  constexpr int B_HALVES = kBN * BK;          // one expanded-weight stage
+  constexpr int XDMA = kBM * PIECES / 64 / 4; // x DMA instructions per wave per stage
+  constexpr int RPI = 64 / PIECES;            // rows per DMA instruction
+  constexpr int WPT = BK / 16;                // packed 32-bit words per thread per sub-step
+  // Sub-step t issues one group of loads: x(t+3) (XDMA), w(t+4) (1) and, when
+  // sub-step t+3 opens a group, s(t+3) (2). Sizes by t % 4, compile-time.
+  constexpr auto s_used = [](int j) { return SPG == 0 || ((j + 3) & 3) % SPG == 0; };
+  constexpr auto group_loads = [s_used](int j) { return XDMA + 1 + (s_used(j & 3) ? 2 : 0); };
   typedef typename std::conditional<BK == 64, u32x4_t, u32x2_t>::type wvec_t;
-  __shared__ __attribute__((aligned(1024))) _Float16 xs[3 * STAGE_HALVES];
+  // One array for both rings: with x stages and B stages at offsets the
+  // compiler can tell apart, it does not wait for the x DMA before every read.
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[4 * A_HALVES + 2 * B_HALVES];
+  _Float16* const as = lds;
+  _Float16* const bs = lds + 4 * A_HALVES;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int c32 = lane & 31, h = lane >> 5;
 
-  // Tile assignment: consecutive block ids walk down the M tiles first so the
-  // blocks resident together share weight tiles.
+  // Tile assignment: consecutive block ids walk down the M tiles first. The
+  // hardware deals block ids round-robin to the 8 XCDs, so with 8 M tiles each
+  // XCD keeps one x row-tile in its L2.
   const int mtiles = (M + kBM - 1) / kBM;
   const int bm = blockIdx.x % mtiles, bn = blockIdx.x / mtiles;
   const int m0 = bm * kBM, n0 = bn * kBN;
 
-  // --- x DMA addressing: wave instruction i writes LDS bytes [1 KB * (wave*XDMA+i), +1 KB):
-  //     rows R + i * (64 / PIECES) with R = wave * XDMA * (64 / PIECES) + lane / PIECES, and
-  //     physical piece lane % PIECES, which holds logical piece c = (lane % PIECES) ^ (row % PIECES)
-  //     -- the same c for every i, since each instruction advances by whole swizzle periods.
-  constexpr int RPI = 64 / PIECES;                            // rows per DMA instruction
-  const int xr0 = wave * XDMA * RPI + lane / PIECES;
-  const int xc = (lane % PIECES) ^ (xr0 & (PIECES - 1));
-  const bool xfull = m0 + kBM <= M;                           // common case: no row clamping
-  auto xrow_off = [&](int i) -> int64_t {                     // element offset of row i's piece
-    int r = m0 + xr0 + i * RPI;
-    if (!xfull) r = r < M ? r : M - 1;                        // rows past M: discarded
-    return (int64_t)r * K + 8 * xc;
-  };
-  auto dma_x = [&](int t, int stage) {
-#pragma unroll
-    for (int i = 0; i < XDMA; ++i)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(x + xrow_off(i) + t * BK),
-          reinterpret_cast<void*>(xs + stage * STAGE_HALVES + (wave * XDMA + i) * 512), 16, 0, 0);
-  };
+  auto swz = [](int r, int c) { return c ^ ((r / RPB) & (PIECES - 1)); };
 
-  // --- weights: lane (c32, h) of n-tile b reads row n, bytes [t*BK/2 + h*BK/4, +BK/4)
-  const uint8_t* wsrc[2];
+  // --- x: DMA, wave instruction i writes 1 KB: rows xr0 + i*RPI, physical piece lane%PIECES.
+  // Byte offsets from the tile's first row fit 32 bits (256 rows, K < 2^23).
+  const int xr0 = wave * XDMA * RPI + lane / PIECES;
+  const char* xtile = reinterpret_cast<const char*>(x + (int64_t)m0 * K);
+  uint32_t xoff[XDMA];
+#pragma unroll
+  for (int i = 0; i < XDMA; ++i) {
+    const int r = xr0 + i * RPI;
+    const int rr = m0 + r < M ? r : M - 1 - m0;                // rows past M: read row M-1, discarded
+    xoff[i] = 2u * ((uint32_t)rr * (uint32_t)K + 8u * (uint32_t)swz(r, lane % PIECES));
+  }
+
+  // --- weights: thread t expands codes [wc*BK/2, +BK/2) of weight row wrow.
+  const int wrow = tid >> 1, wc = tid & 1;
+  const uint8_t* wsrc;
+  {
+    int n = n0 + wrow;
+    n = n < N ? n : N - 1;                                     // tail rows: read, discarded
+    wsrc = packed + (int64_t)n * (K >> 1) + wc * (BK / 4);
+  }
+  // scales of the lane's two output columns
   const uint16_t* ssrc[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     int n = n0 + wn * 64 + b * 32 + c32;
-    n = n < N ? n : N - 1;                                     // tail rows: read, discard
-    wsrc[b] = packed + (int64_t)n * (K >> 1) + h * (BK / 4);
+    n = n < N ? n : N - 1;
     ssrc[b] = scales + (int64_t)n * G;
   }
-  wvec_t wr[3][2];
-  uint32_t sr[3][2];
+  const int T = K / BK;
+  const int spg_log = SPG == 0 ? gshift : SPG == 4 ? 2 : SPG == 2 ? 1 : 0;
+  wvec_t wr[4];                                                // w(t) in slot t % 4
+  uint32_t sr[4][2];                                           // s(t) in slot t % 4
+
+  // Loads of sub-step t's operands: weights, scales, x (always issued: an
+  // index past the end is clamped to the last sub-step and its data is never
+  // used, so the wait counts stay exact).
   auto load_w = [&](int t, int slot) {
+    const int tc = t < T ? t : T - 1;
+    wr[slot] = __builtin_nontemporal_load(reinterpret_cast<const wvec_t*>(wsrc + tc * (BK / 2)));
+  };
+  auto load_sx = [&](int t, int slot, bool with_s) {
+    const int tc = t < T ? t : T - 1;
+    if (with_s) {
+      // Sub-steps of one group load the same scales; the opaque index keeps
+      // the compiler from merging such loads, which would change the load
+      // counts the waits rely on.
+      int gi = tc >> spg_log;
+      asm volatile("" : "+s"(gi));
 #pragma unroll
-    for (int b = 0; b < 2; ++b) sr[slot][b] = ssrc[b][(t * BK) >> (gshift + (BK == 64 ? 6 : 5))];
+      for (int b = 0; b < 2; ++b) sr[slot][b] = ssrc[b][gi];
+    }
+    const char* base = xtile + (int64_t)tc * (2 * BK);
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-      wr[slot][b] = __builtin_nontemporal_load(reinterpret_cast<const wvec_t*>(wsrc[b] + t * (BK / 2)));
+    for (int i = 0; i < XDMA; ++i)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(base + xoff[i]),
+          reinterpret_cast<void*>(as + slot * A_HALVES + (wave * XDMA + i) * 512), 16, 0, 0);
+  };
+  auto expand = [&](int slot, int bstage) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      half2_t hw[4];
+      codes_to_half_natural(wr[slot][i], hw);
+      const int c = wc * WPT + i;
+      *reinterpret_cast<half8_t*>(bs + bstage * B_HALVES + wrow * BK + 8 * swz(wrow, c)) = as_half8(hw);
+    }
   };
 
   float16_t acc[4][2];
@@ -123,78 +171,103 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
   float srun[2] = {0.0f, 0.0f};
 
-  const int T = K / BK;
-  const int steps_per_group = 1 << gshift;
-  // A-fragment LDS offsets (halves) for k-step s within a stage, for m-tile 0;
-  // m-tile a adds a * 32 rows (a constant, and a whole number of swizzle periods).
-  int aoff[KS];
-  {
-    const int r = wm * 128 + c32;
+  // Operand LDS offsets (halves) for k-step s; m-tile a adds a*32 rows, n-tile b
+  // adds b*32 rows (whole swizzle periods, so the piece is unchanged).
+  int aoff[KS], boff[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int c = (PIECES == 8 ? 4 * h : 2 * h) + s;         // logical piece of k = 32h/16h + 8s
-      aoff[s] = r * BK + 8 * (c ^ (r & (PIECES - 1)));
-    }
+  for (int s = 0; s < KS; ++s) {
+    const int c = (BK / 16) * h + s;
+    const int ra = wm * 128 + c32, rb = wn * 64 + c32;
+    aoff[s] = ra * BK + 8 * swz(ra, c);
+    boff[s] = rb * BK + 8 * swz(rb, c);
   }
 
-  // Loads of sub-step t (x DMA + scales + weights), always issued: an index
-  // past the end is clamped to the last sub-step (its data lands in a stage or
-  // register slot that is never read again). With no branch around loads the
-  // wait counts below stay exact.
-  auto issue = [&](int t, int stage, int slot) {
-    const int tc = t < T ? t : T - 1;
-    dma_x(tc, stage);
-    load_w(tc, slot);
-  };
-  issue(0, 0, 0);
-  issue(1, 1, 1);
+  // The loads of one group may be issued in any order. Sub-step t needs s(t),
+  // x(t) and w(t+1) -- exactly the group that sub-step t-3 issued -- so it
+  // waits until only the two newer groups are pending. x(t+3) goes to the
+  // stage sub-step t-1 read, w(t+4) to the slot of w(t), which sub-step t-1
+  // expanded. Every load issued is used, so none is dropped by the compiler.
+  // Prologue: w0, then the groups of sub-steps -3, -2, -1, then expand w0.
+  // (Scheduling barriers keep the groups apart, as the waits assume.)
+  load_w(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < 3; ++g) {
+    load_sx(g, g, s_used(g + 1));
+    load_w(g + 1, g + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmcnt<group_loads(1) + group_loads(2) + group_loads(3)>(); // w(0)
+  __builtin_amdgcn_sched_barrier(0);
+  expand(0, 0);
 
-  auto substep = [&](int t, int stage, int slot, int slot2) {
-    // Outstanding: loads of t and t+1 (XDMA + 4 each, in order); wait for t's.
-    wait_vmcnt<XDMA + 4>();
-    lds_barrier();                                             // x stage t visible; stage t+2 free
-    issue(t + 2, (stage + 2) % 3, slot2);
-    if ((t & (steps_per_group - 1)) == 0) {                    // first sub-step of a group
+  // Sub-step t = t0 + j with t0 a multiple of 4: x stage, scale slot and
+  // weight slot j, B stage j % 2, all compile-time.
+  // In the tail (after the last whole block of 4) no loads are issued and
+  // only the groups of sub-steps t0-2 and t0-1 can still be newer.
+  auto substep = [&](auto J, auto Tail, int t) {
+    constexpr int j = decltype(J)::value;
+    constexpr bool tail = decltype(Tail)::value;
+    constexpr int p = j & 1;
+    if constexpr (!tail) wait_vmcnt<group_loads(j + 2) + group_loads(j + 3)>();  // group of t-3 landed
+    else if constexpr (j == 0) wait_vmcnt<group_loads(2) + group_loads(3)>();
+    else if constexpr (j == 1) wait_vmcnt<group_loads(3)>();
+    else wait_vmcnt<0>();
+    lds_barrier();                                             // x(t), B(t) visible; stages of t-1 free
+    // Keep every use of the awaited registers below the wait: a use hoisted
+    // above it makes the compiler add a wait of its own, and with LDS DMA in
+    // flight that wait is for every load.
+    __builtin_amdgcn_sched_barrier(0);
+    bool gstart;
+    if constexpr (SPG == 0) gstart = (t & ((1 << gshift) - 1)) == 0;
+    else gstart = j % SPG == 0;
+    float ratio[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const float sn = half_bits_to_float((uint16_t)sr[slot][b]);
-        const bool live = sn != 0.0f;                          // zero scale: keep the running one
-        const float ratio = live ? (srun[b] == 0.0f ? 0.0f : srun[b] / sn) : 1.0f;
-        srun[b] = live ? sn : srun[b];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) acc[a][b] *= ratio;
-      }
+    for (int b = 0; b < 2; ++b) {
+      const float sn = half_bits_to_float((uint16_t)sr[j][b]);
+      const bool live = gstart && sn != 0.0f;                  // zero scale: keep the running one
+      // srun / sn to within an ulp (a uniform relative error of the finished
+      // groups' part, far inside the tolerance); srun = 0 gives 0.
+      ratio[b] = live ? srun[b] * __builtin_amdgcn_rcpf(sn) : 1.0f;
+      srun[b] = live ? sn : srun[b];
     }
-    const _Float16* st = xs + stage * STAGE_HALVES;
+    expand((j + 1) & 3, p ^ 1);                                // w(t+1) -> B stage of t+1
+    if constexpr (!tail) {
+      load_sx(t + 3, (j + 3) & 3, s_used(j));
+      load_w(t + 4, j);
+    }
+    const _Float16* sa = as + j * A_HALVES;
+    const _Float16* sb = bs + p * B_HALVES;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       half8_t af[4], bf[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = *reinterpret_cast<const half8_t*>(st + aoff[s] + a * 32 * BK);
+      for (int a = 0; a < 4; ++a) af[a] = *reinterpret_cast<const half8_t*>(sa + aoff[s] + a * 32 * BK);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        half2_t hw[4];
-        codes_to_half_natural(wr[slot][b][s], hw);
-        bf[b] = as_half8(hw);
-      }
+      for (int b = 0; b < 2; ++b) bf[b] = *reinterpret_cast<const half8_t*>(sb + boff[s] + b * 32 * BK);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b) {
+          if (s == 0 && (SPG == 0 || gstart)) acc[a][b] *= ratio[b];
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+        }
     }
   };
 
-  // Main loop over whole triples (ring slots and stages are compile-time),
-  // then the one or two remaining sub-steps.
-  const int Tm = T - T % 3;
-  for (int t = 0; t < Tm; t += 3) {
-    substep(t, 0, 0, 2);
-    substep(t + 1, 1, 1, 0);
-    substep(t + 2, 2, 2, 1);
+  // Whole blocks of 4 sub-steps without branches, then up to 3 more.
+  using body = std::false_type;
+  using tail = std::true_type;
+  int t0 = 0;
+  for (; t0 + 4 <= T; t0 += 4) {
+    substep(std::integral_constant<int, 0>(), body(), t0);
+    substep(std::integral_constant<int, 1>(), body(), t0 + 1);
+    substep(std::integral_constant<int, 2>(), body(), t0 + 2);
+    substep(std::integral_constant<int, 3>(), body(), t0 + 3);
   }
-  if (Tm < T) substep(Tm, 0, 0, 2);
-  if (Tm + 1 < T) substep(Tm + 1, 1, 1, 0);
+  if (t0 < T) substep(std::integral_constant<int, 0>(), tail(), t0);
+  if (t0 + 1 < T) substep(std::integral_constant<int, 1>(), tail(), t0 + 1);
+  if (t0 + 2 < T) substep(std::integral_constant<int, 2>(), tail(), t0 + 2);
   wait_vmcnt<0>();                                             // no LDS DMA in flight at exit
 
   // Epilogue: apply the last running scale; lane l holds column l%32 and rows
@@ -226,7 +299,7 @@ const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* 
   const int BK = tiled_bk(group);
   if (BK == 0) return "tiled kernel takes group 32 or 64 times a power of two";
   if (K % BK != 0) return "tiled kernel needs K to be a multiple of min(group, 64)";
-  if (K >= (1ll << 30)) return "tiled kernel needs K below 2^30";
+  if (K >= (1ll << 23)) return "tiled kernel needs K below 2^23";
   if ((uintptr_t)x % 16 || (uintptr_t)packed % 16) return "tiled kernel needs 16-byte aligned x and packed";
   return nullptr;
 }
@@ -241,12 +314,13 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   const int64_t blocks = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   if (M >= (1ll << 31) || N >= (1ll << 31) || blocks >= (1ll << 31)) return hipErrorInvalidValue;
   const _Float16* xh = static_cast<const _Float16*>(x);
-  if (BK == 64)
-    hipLaunchKernelGGL(matmul_tiled_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, xh,
-                       (int)M, packed, scales, (int)N, (int)K, G, gshift, y);
-  else
-    hipLaunchKernelGGL(matmul_tiled_kernel<32>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, xh,
-                       (int)M, packed, scales, (int)N, (int)K, G, gshift, y);
+  auto kernel = matmul_tiled_kernel<64, 0>;
+  if (BK == 32) kernel = matmul_tiled_kernel<32, 1>;
+  else if (gshift == 0) kernel = matmul_tiled_kernel<64, 1>;
+  else if (gshift == 1) kernel = matmul_tiled_kernel<64, 2>;
+  else if (gshift == 2) kernel = matmul_tiled_kernel<64, 4>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, xh, (int)M, packed,
+                     scales, (int)N, (int)K, G, gshift, y);
   return hipGetLastError();
 }
 
