@@ -19,7 +19,19 @@ M = 2048 rate (2*M*N*K flops over the phase's time) is reported beside it,
 each as a fraction of the MI355X peak (HBM 8 TB/s; dense fp16 MFMA
 2.5 PFLOP/s).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
+
+--copy-probe adds, after the timed region, three plain device-to-device
+copies of 512 MiB: under rocprofv3 --pmc they give the FETCH_SIZE and
+WRITE_SIZE readings of a kernel whose HBM traffic is known, which calibrates
+the same counters on the path's kernels.
+
+python bench.py --summarize-pmc FETCH_CSV WRITE_CSV OUT_JSON turns the
+counter_collection.csv files of two such runs (one counter each) into
+per-launch HBM traffic per phase, scaled by the copy calibration, and records
+the sha256 of the kernel sources it was measured on. A later bench run fills
+each roofline's "traffic" from that file only while those sources are
+unchanged (else it reports null).
 """
 from __future__ import annotations
 
@@ -38,6 +50,65 @@ SHAPES = [("q_proj", 4096, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 
 GROUP = 128
 M_DECODE, M_PREFILL = 1, 2048
 POOL_BYTES = 1 << 30
+COPY_PROBE_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c4.json")
+CSRC = os.path.join(ROOT, "dequantizing_gemm_amd", "csrc")
+# kernel-name fragment -> bench phase
+PHASE_KERNELS = {"quantize": "quantize_vec_kernel", "unpack": "unpack_flat_kernel",
+                 "decode_m1": "matmul_skinny_kernel", "prefill_m2048": "matmul_tiled_kernel"}
+
+
+def csrc_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv, write_csv, out_json, command=""):
+    """Per-phase HBM bytes per launch from two rocprofv3 --pmc runs of
+    `bench.py --copy-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+    Each counter is scaled by (512 MiB / its largest reading on the runtime's
+    copy kernel), i.e. by what it reads for the probe copy of known size.
+    Every phase launches the three shapes in the order of SHAPES, so within a
+    kernel family the shape of a dispatch is its position mod 3."""
+    import csv
+    import statistics
+
+    out = {"source_sha256": csrc_digest(), "command": command, "phases": {}, "shapes": {}}
+    for label, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        copy_max = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        factor = COPY_PROBE_BYTES / 1024 / copy_max
+        out[label + "_factor"] = round(factor, 4)
+        for phase, frag in PHASE_KERNELS.items():
+            vals = [float(r["Counter_Value"]) for r in rows if frag in r["Kernel_Name"]]
+            if not vals or len(vals) % len(SHAPES):
+                continue
+            per_shape = [statistics.median(vals[i::len(SHAPES)]) * 1024 * factor for i in range(len(SHAPES))]
+            out["shapes"].setdefault(phase, {})[label + "_bytes"] = {
+                name: round(b) for (name, _, _), b in zip(SHAPES, per_shape)}
+            out["phases"].setdefault(phase, {})[label + "_bytes_per_launch"] = round(sum(per_shape) / len(SHAPES))
+    for ph in out["phases"].values():
+        ph["traffic_bytes_per_launch"] = ph.get("fetch_bytes_per_launch", 0) + ph.get("write_bytes_per_launch", 0)
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def measured_traffic():
+    """Per-phase traffic from the committed counter summary, or {} if the
+    kernel sources have changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if t.get("source_sha256") != csrc_digest():
+        return {}
+    return {k: v["traffic_bytes_per_launch"] for k, v in t.get("phases", {}).items()}
 
 
 def packed_weight_bytes(N, K, g=GROUP):
@@ -85,7 +156,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, command=os.environ.get("PMC_COMMAND", ""))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no "
               "multi-GPU leg; a sharded layout is described in the design notes.", file=sys.stderr)
@@ -199,11 +275,14 @@ def main():
     p_flops = sum(2 * M_PREFILL * m["N"] * m["K"] for m in mats)
     per_launch = {"quantize": 3, "unpack": 3, "decode_m1": 3 * R, "prefill_m2048": 3}
 
+    traffic = measured_traffic()
+
     def roof(name, bound, work, unit, peak):
         t = phase_ms[name] * 1e-3
         achieved = work / t / (1e9 if unit == "GB/s" else 1e12)
         return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic.get(name),
+                "algorithmic_per_launch": round(work / per_launch[name]),
                 "avg_launch_us": round(phase_ms[name] * 1e3 / per_launch[name], 3),
                 "launches_per_step": per_launch[name]}
 
@@ -231,6 +310,14 @@ def main():
         "rooflines": roofs,
         "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
     }
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = COPY_PROBE_BYTES
+        del src, dst
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline()
