@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4dq.s
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 X_F32, X_F16 = 0, 1
-PATHS = {"auto": 0, "generic": 1, "skinny": 2, "tiled": 3}
+PATHS = {"auto": 0, "generic": 1, "skinny": 2, "tiled": 3, "gemv": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 # Every function declared in include/int4dq.h, with its ctypes signature.

@@ -34,7 +34,7 @@ HIPFLAGS = [
 ]
 
 SOURCES = ["api.cpp", "quantize.hip", "unpack.hip", "matmul_generic.hip", "matmul_skinny.hip",
-           "matmul_tiled.hip"]
+           "matmul_tiled.hip", "matmul_gemv.hip"]
 
 # The tiled kernel rescales its MFMA accumulators with VALU ops at every group
 # boundary; selecting the VGPR form of the MFMA instructions keeps the

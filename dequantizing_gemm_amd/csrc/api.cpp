@@ -61,6 +61,7 @@ int check_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
 
 int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t N,
                 int64_t K, int64_t group) {
+  if (!int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_GEMV;
   if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_SKINNY;
   if (!int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group)) return INT4DQ_PATH_TILED;
   return INT4DQ_PATH_GENERIC;
@@ -107,7 +108,7 @@ int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packe
                      int path, void* stream) {
   int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
   if (rc != INT4DQ_OK) return rc;
-  if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_TILED)
+  if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_GEMV)
     return fail(INT4DQ_EINVAL, "int4_matmul_path: unknown path %d", path);
   if (M == 0) return ok();
   if (path == INT4DQ_PATH_AUTO) path = choose_path(x, x_dtype, M, packed, N, K, group);
@@ -118,6 +119,12 @@ int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packe
       if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
       return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, N, K, group, y, s),
                         "int4_matmul skinny launch");
+    }
+    case INT4DQ_PATH_GEMV: {
+      const char* why = int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group);
+      if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
+      return hip_status(int4dq::launch_matmul_gemv(x, packed, scales, N, K, group, y, s),
+                        "int4_matmul gemv launch");
     }
     case INT4DQ_PATH_TILED: {
       const char* why = int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group);

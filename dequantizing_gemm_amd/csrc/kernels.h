@@ -25,6 +25,11 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
                                 float* y, hipStream_t stream);
 
+const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
+                                    const uint8_t* packed, int64_t N, int64_t K, int64_t group);
+hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
+                              int64_t N, int64_t K, int64_t group, float* y, hipStream_t stream);
+
 const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
                                      int64_t K, int64_t group);
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,

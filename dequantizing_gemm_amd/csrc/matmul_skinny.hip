@@ -1,5 +1,6 @@
 // matmul_skinny.hip -- dequantizing matmul for few activation rows (M <= 16,
-// binary16 x) on gfx950: a weight-streaming kernel bound by HBM bandwidth.
+// binary16 x; M = 1 normally takes matmul_gemv.hip) on gfx950: a
+// weight-streaming kernel bound by HBM bandwidth.
 //
 // Definition (drill page "Implement INT4 group quantization, nibble packing
 // and a dequantizing matmul", statement, int4_matmul): y = x @ dequantize(W).T,
@@ -19,11 +20,13 @@
 //    Lanes of A rows >= M load row M-1 again: those output rows are computed
 //    and discarded, so nothing has to be zeroed or masked. The integer codes
 //    are exact in fp16, products are exact, sums are fp32.
-//  * A 32-bit word of 8 codes becomes four exact fp16 pairs in natural order
-//    (codes_to_half_natural, 12 VALU ops per 8 codes), so each lane's A
-//    fragment is 8 consecutive activations: one 16-byte load straight from
-//    global memory (x is tiny and stays in L2). No LDS staging and no barrier
-//    stand between a wave's loads and its first MFMA.
+//  * A 32-bit word of 8 codes becomes four exact fp16 pairs. For M <= 4 each
+//    wave stages its own slice of x in LDS, permuted to the "spread" order
+//    that codes_to_half_spread produces (9 VALU ops per 8 codes); for larger
+//    M each lane's A fragment is 8 consecutive activations loaded straight
+//    from global memory (x is tiny and stays in L2) and the codes are expanded
+//    in natural order (codes_to_half_natural, 12 ops). No block barrier
+//    stands between a wave's loads and its first MFMA.
 //  * Lane l owns weight row (l mod 16) and one quarter of each K-block
 //    (KB = 128 codes for group sizes 128 * 2^p, else KB = group = 64 or 32):
 //    one 16-byte weight load per K-block for KB = 128, and a wavefront load

@@ -118,7 +118,11 @@ def test_kernel_selection_rules():
     sel = lambda xd, M, K, g, x=0x1000, p=0x2000: dq.lib.int4_matmul_select(
         ctypes.c_void_p(x), xd, M, ctypes.c_void_p(p), FAKE, 64, K, g, FAKE)
     P = dq.PATHS
-    assert sel(1, 1, 4096, 128) == P["skinny"] and sel(1, 16, 4096, 128) == P["skinny"]
+    assert sel(1, 1, 4096, 128) == P["gemv"] and sel(1, 16, 4096, 128) == P["skinny"]
+    assert sel(1, 2, 4096, 128) == P["skinny"] and sel(1, 1, 11008, 128) == P["gemv"]
+    assert sel(1, 1, 768, 32) == P["gemv"] and sel(1, 1, 768, 64) == P["gemv"]
+    assert sel(1, 1, 4096, 16) == P["generic"]                 # group not a multiple of 32
+    assert sel(1, 1, 65536, 128) == P["tiled"]                 # K beyond the gemv and skinny kernels
     assert sel(1, 17, 4096, 128) == P["tiled"] and sel(1, 2048, 11008, 128) == P["tiled"]
     assert sel(1, 4, 768, 64) == P["skinny"] and sel(1, 4, 768, 32) == P["skinny"]
     assert sel(0, 4, 256, 128) == P["generic"]                 # binary32 x

@@ -228,12 +228,46 @@ def test_matmul_kernels_agree(dq, N, K, g, M):
     x = np.random.default_rng(M).normal(size=(M, K)).astype(np.float16)
     pr, sr, _ = oracle.quantize_int4(w, g)
     pd, sd, xd = dev(pr), dev(sr), dev(x)
-    for path in ("generic", "skinny", "tiled"):
-        if path == "skinny" and M > 16:
+    for path in ("generic", "skinny", "tiled", "gemv"):
+        if (path == "skinny" and M > 16) or (path == "gemv" and M != 1):
             continue
         say(f"case: kernel {path} N={N} K={K} g={g} M={M}")
         y = host(dq.int4_matmul_path(xd, pd, sd, K, g, path))
         check_matmul(y, x, pr, sr, K, g, what=path)
+
+
+@pytest.mark.parametrize("N,K,g", [(300, 11008, 128), (77, 4096, 96), (513, 2080, 32), (40, 32768, 128),
+                                   (10, 32, 32), (4099, 4096, 128), (8195, 4096, 64), (2051, 2048, 128)])
+def test_matmul_gemv_shapes(dq, N, K, g):
+    """The M = 1 row-streaming kernel: a partial last 1 KB chunk (K = 11008,
+    2080), a group that is not a power of two (96), the largest K it takes
+    (16 chunks), the smallest (one lane), and N tails for 1, 2 and 4 rows per
+    block."""
+    say(f"case: gemv N={N} K={K} g={g}")
+    w = np.random.default_rng(N + K).normal(0, 0.02, size=(N, K)).astype(np.float32)
+    x = np.random.default_rng(K).normal(size=(1, K)).astype(np.float16)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    pd, sd, xd = dev(pr), dev(sr), dev(x)
+    assert dq.matmul_select(xd, pd, sd, K, g) == "gemv"
+    y = host(dq.int4_matmul_path(xd, pd, sd, K, g, "gemv"))
+    check_matmul(y, x, pr, sr, K, g, what=f"gemv {N}x{K}")
+
+
+def test_matmul_gemv_one_hot_exact(dq):
+    """One-hot x through the M = 1 kernel gives column k of (q * scale)^T
+    bit-exactly: one exact product per output, zeros elsewhere."""
+    for (N, K, g) in [(48, 4096, 128), (300, 11008, 128), (32, 768, 32)]:
+        say(f"case: gemv one-hot N={N} K={K} g={g}")
+        w = np.random.default_rng(K).normal(size=(N, K)).astype(np.float32)
+        pr, sr, _ = oracle.quantize_int4(w, g)
+        what = (oracle.unpack_int4(pr, K).astype(np.float64) *
+                np.repeat(sr.astype(np.float64), g, 1)[:, :K]).T
+        pd, sd = dev(pr), dev(sr)
+        for k in sorted({0, 1, 31, 32, K // 2 + 7, K - 33, K - 1}):
+            e = np.zeros((1, K), dtype=np.float16)
+            e[0, k] = 1.0
+            y = host(dq.int4_matmul_path(dev(e), pd, sd, K, g, "gemv"))
+            assert np.array_equal(y[0].astype(np.float64), what[k]), f"k={k}"
 
 
 def test_matmul_fp32_x(dq):
@@ -273,8 +307,8 @@ def test_matmul_zero_and_empty(dq):
     pr, sr, _ = oracle.quantize_int4(w, 128)
     pd, sd = dev(pr), dev(sr)
     for M in (1, 16, 300):
-        for path in ("skinny", "tiled", "generic"):
-            if path == "skinny" and M > 16:
+        for path in ("skinny", "tiled", "generic", "gemv"):
+            if (path == "skinny" and M > 16) or (path == "gemv" and M != 1):
                 continue
             y = host(dq.int4_matmul_path(torch.zeros(M, 512, dtype=torch.float16, device=DEV), pd, sd, 512, 128, path))
             assert np.all(y == 0)
