@@ -55,7 +55,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c4.json")
 CSRC = os.path.join(ROOT, "dequantizing_gemm_amd", "csrc")
 # kernel-name fragment -> bench phase
 PHASE_KERNELS = {"quantize": "quantize_vec_kernel", "unpack": "unpack_flat_kernel",
-                 "decode_m1": "matmul_skinny_kernel", "prefill_m2048": "matmul_tiled_kernel"}
+                 "decode_m1": "matmul_gemv", "prefill_m2048": "matmul_tiled_kernel"}
 
 
 def csrc_digest():

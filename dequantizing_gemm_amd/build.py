@@ -36,10 +36,11 @@ HIPFLAGS = [
 SOURCES = ["api.cpp", "quantize.hip", "unpack.hip", "matmul_generic.hip", "matmul_skinny.hip",
            "matmul_tiled.hip", "matmul_gemv.hip"]
 
-# The tiled kernel rescales its MFMA accumulators with VALU ops at every group
-# boundary; selecting the VGPR form of the MFMA instructions keeps the
-# accumulators in VGPRs instead of AGPRs (no accvgpr read/write around them).
-EXTRA = {"matmul_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# The tiled and gemv kernels read or rescale their MFMA accumulators with VALU
+# ops; selecting the VGPR form of the MFMA instructions keeps the accumulators
+# in VGPRs instead of AGPRs (no accvgpr read/write around them).
+EXTRA = {"matmul_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+         "matmul_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src: str) -> str:
