@@ -7,37 +7,45 @@
 // group's scale on each output column. Full-precision weights never reach
 // memory ("Build a Blockwise INT4 Inference Engine", architecture overview:
 // the fusion boundary); here they exist only as exact fp16 integer codes in
-// LDS, one sub-step at a time.
+// registers, one MFMA k-step at a time.
 //
-// Block tile 256 (rows of x) x 128 (weight rows), 512 threads = 4 x 2
-// wavefronts (two per SIMD), each owning 64 x 64 outputs as 2 x 2 tiles of
-// v_mfma_f32_32x32x16_f16 (fp32 accumulation in VGPRs). K advances in
-// sub-steps of BK = min(group, 64) codes:
+// Block tile 256 (rows of x) x 128 (weight rows), 256 threads = 2 x 2
+// wavefronts, one per SIMD, each owning 128 x 64 outputs as 4 x 2 tiles of
+// v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 VGPRs). Larger wave tiles
+// than 64 x 64 halve the LDS bytes read per MFMA, which bounds this kernel.
+// K advances in sub-steps of BK = min(group, 64) codes:
 //  * x tiles [256 x BK] fp16 go global -> LDS by DMA (global_load_lds, 16 B
 //    per lane, no VGPRs) into a 4-stage ring, three sub-steps ahead.
-//  * The block's packed weights [128 x BK/2 bytes] are loaded to registers
-//    four sub-steps ahead; one sub-step ahead each thread expands its words
-//    to exact fp16 codes (codes_to_half_natural) into a 2-stage LDS ring, so
-//    each code is expanded once per block, not once per wave.
-//  * Both LDS tiles use rows of BK halves made of 16-byte pieces; logical
-//    piece c of row r is stored at c ^ ((r / (16 / pieces)) % pieces). The 16
-//    rows one pass of an MFMA operand read touches then cover all 64 banks;
-//    each expansion store writes 1 KB contiguously (conflict-free for
-//    ds_write_b128, which the row pattern is not).
+//  * Packed weights go global -> LDS by DMA too, in "super-tiles" of 128 B
+//    (256 codes) of each of the block's 128 rows: eight lanes cover a full
+//    128-byte line, and a 2-slot ring loads super-tile j+1 while j is used.
+//  * Each wavefront reads its own packed words (one 16-byte read per 32-column
+//    tile per sub-step) and expands them to exact fp16 codes in registers
+//    (codes_to_half_natural) right before the MFMAs that use them.
 //  * The k order inside a sub-step is a fixed permutation shared by A and B
-//    (lane half h, k-step s: piece (BK / 16) h + s), which leaves the dot
-//    product unchanged.
+//    (lane half h, k-step s: codes (BK/2) h + 8 s .. +7), so each lane's
+//    packed bytes for a sub-step are contiguous and the dot product is
+//    unchanged.
+//  * LDS rows are made of 16-byte pieces; logical piece c of row r is stored
+//    at c ^ f(r), which makes every 16-lane pass of an operand read cover all
+//    64 banks. DMA writes stay contiguous (the swizzle is applied to the
+//    global source address).
+//  * Sub-step t's A fragments for k-step 0 and its packed words are read at
+//    the end of sub-step t-1, so the MFMA pipe does not wait for LDS after the
+//    barrier; the barrier of sub-step t therefore makes the data of t+1
+//    visible (it waits for the loads issued two sub-steps earlier).
 //  * Integer-first scaling with one accumulator set: the accumulator holds
 //    (sum of finished groups' scaled partials) / (scale of the current group);
-//    at each group boundary it is multiplied by s_prev / s_new for its column,
-//    the group's integer products are accumulated by the MFMAs, and the final
-//    value is multiplied by the last scale. A zero scale (a group of zero
-//    codes) leaves the running scale unchanged. Mathematically this is
+//    at each group boundary it is multiplied by s_prev / s_new for its column
+//    (done at the end of the group's last sub-step, overlapping the last
+//    MFMAs), the group's integer products are accumulated by the MFMAs, and
+//    the final value is multiplied by the last scale. A zero scale (a group of
+//    zero codes) leaves the running scale unchanged. Mathematically this is
 //    sum_g s_g * (x . q_g); the ratio multiply adds one fp32 rounding per group.
-//    Which sub-steps open a group is a template parameter, so every sub-step is
-//    one branch-free block.
-//  * Each sub-step waits for exactly the group of loads issued D sub-steps
-//    earlier (counts known at compile time), then one LDS-only barrier.
+//  * Each sub-step waits for exactly the loads issued two sub-steps earlier
+//    (counts known at compile time; the loop is unrolled over two super-tiles
+//    so every stage and slot index is a constant), then one LDS-only barrier.
+//    Scheduling groups interleave LDS reads, code expansion and MFMAs.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -55,59 +63,56 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    unroll<B + 1, E>(f);
+  }
+}
+
+constexpr int kTileM = 256, kTileN = 128, kThreads = 256;
 }  // namespace
 
-// Tile configuration: block tile BM x BN, WM x WN wavefronts (each owning a
-// (BM/WM) x (BN/WN) tile of 32x32 MFMA tiles), BK codes per sub-step, NXS
-// stages in the x ring (2 or 4; loads run NXS-1 sub-steps ahead), SPG
-// sub-steps per group (1, 2 or 4, dividing NXS or equal to it), or 0: any
-// power of two 2^gshift, decided at run time.
-template <int BM, int BN, int WM, int WN, int BK, int NXS, int SPG>
-__global__ __launch_bounds__(64 * WM * WN) void matmul_tiled_kernel(
+// BK: codes per sub-step (32 or 64). SPG: sub-steps per group (1, 2, 4 or 8),
+// or 0: any power of two 2^gshift, decided at run time.
+template <int BK, int SPG>
+__global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int gshift,
     float* __restrict__ y) {
-  constexpr int NW = WM * WN, NT = 64 * NW;
-  constexpr int WMT = BM / WM, WNT = BN / WN;  // wave tile
-  constexpr int TM = WMT / 32, TN = WNT / 32;  // 32x32 MFMA tiles per wave
+  constexpr int BM = kTileM, BN = kTileN, WN = 2, NW = 4;
+  constexpr int WMT = 128, WNT = 64, TM = 4, TN = 2;   // wave tile, in 32x32 MFMA tiles
   constexpr int KS = BK / 16;                  // MFMA k-steps per sub-step
-  constexpr int PIECES = BK / 8;               // 16-byte pieces per row per sub-step
-  constexpr int RPB = 16 / PIECES;             // rows per 256-byte LDS bank period
-  constexpr int A_HALVES = BM * BK;            // one x stage
-  constexpr int B_HALVES = BN * BK;            // one expanded-weight stage
-  constexpr int XDMA = BM * PIECES / (64 * NW);// x DMA instructions per wave per stage
-  constexpr int RPI = 64 / PIECES;             // rows per DMA instruction
-  constexpr int WPT = BN * BK / 8 / NT;        // packed 32-bit words per thread per sub-step
-  constexpr int D = NXS - 1;                   // x / scale prefetch distance (sub-steps)
-  constexpr int U = NXS;                       // sub-steps per unrolled loop body
-  static_assert(NXS == 2 || NXS == 4, "x ring depth");
-  static_assert(SPG == 0 || (U % SPG == 0), "sub-steps per group");
-  static_assert(XDMA >= 1 && BM * PIECES % (64 * NW) == 0, "x DMA split");
-  static_assert(WPT >= 1 && BN * BK / 8 == WPT * NT, "weight words per thread");
-  static_assert(WMT % 32 == 0 && WNT % 32 == 0, "wave tile");
-  // Sub-step t issues one group of loads: x(t+D) (XDMA), w(t+D+1) (WPT) and,
-  // when sub-step t+D opens a group, s(t+D) (TN). Sizes by t % U.
-  constexpr auto s_used = [](int j) { return SPG == 0 || ((j + D) % U) % SPG == 0; };
+  constexpr int PIECES = BK / 8;               // 16-byte pieces per x row per stage
+  constexpr int RPB = 16 / PIECES;             // x rows per 256-byte bank period
+  constexpr int NXS = 4, D = 3;                // x ring stages, x prefetch distance
+  constexpr int A_BYTES = BM * BK * 2;         // one x stage
+  constexpr int XDMA = BM * PIECES / (64 * NW);// x DMA instructions per wave per sub-step
+  constexpr int RPI = 64 / PIECES;             // x rows per DMA instruction
+  constexpr int SUB = 256 / BK;                // sub-steps per packed super-tile
+  constexpr int U = 2 * SUB;                   // sub-steps per unrolled body
+  constexpr int W_BYTES = BN * 128;            // one packed super-tile
+  constexpr int WDMA = W_BYTES / 1024 / NW;    // W DMA instructions per wave per super-tile
+  static_assert(BK == 32 || BK == 64, "sub-step");
+  static_assert(SPG == 0 || U % SPG == 0, "sub-steps per group");
+  static_assert(NXS * A_BYTES + 2 * W_BYTES <= 160 * 1024, "LDS");
+  // Sub-step t issues x(t+D), s(t+D) when t+D opens a group (every sub-step
+  // when SPG is decided at run time), and super-tile t/SUB + 1 when t is the
+  // first sub-step of a super-tile. Sizes by position in the unrolled body.
+  constexpr auto s_used = [](int j) { return SPG == 0 || (((j % U) + U) % U) % SPG == 0; };
   constexpr auto group_loads = [s_used](int j) {
-    return XDMA + WPT + (s_used(((j % U) + U) % U) ? TN : 0);
-  };
-  // Loads pending that are newer than the group sub-step t needs: the groups of
-  // sub-steps t-D+1 .. t-1 (main loop), or those issued before the tail.
-  constexpr auto newer_loads = [group_loads](int j, bool tail) {
-    int n = 0;
-    if (!tail) {
-      for (int i = 1; i < D; ++i) n += group_loads(j - i);
-    } else {
-      for (int i = 1; i <= D - 1 - j; ++i) n += group_loads(U - i);
-    }
-    return n;
+    const int jj = ((j % U) + U) % U;
+    return XDMA + (s_used(jj + D) ? TN : 0) + (jj % SUB == 0 ? WDMA : 0);
   };
 
-  // One array for both rings: with x stages and B stages at offsets the
-  // compiler can tell apart, it does not wait for the x DMA before every read.
-  __shared__ __attribute__((aligned(1024))) _Float16 lds[NXS * A_HALVES + 2 * B_HALVES];
-  _Float16* const as = lds;
-  _Float16* const bs = lds + NXS * A_HALVES;
+  // One array for both rings: with stages and slots at constant offsets the
+  // compiler can tell the DMA targets from the regions being read. Every LDS
+  // address is written as an offset from the array itself (not from a pointer
+  // variable into it), which keeps the DMA destinations scalar.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NXS * A_BYTES + 2 * W_BYTES];
+  constexpr int W_LDS = NXS * A_BYTES;         // offset of the packed-weight slots
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -120,80 +125,91 @@ __global__ __launch_bounds__(64 * WM * WN) void matmul_tiled_kernel(
   const int mtiles = (M + BM - 1) / BM;
   const int bm = blockIdx.x % mtiles, bn = blockIdx.x / mtiles;
   const int m0 = bm * BM, n0 = bn * BN;
+  const int RB = K >> 1;                       // bytes per packed row
+  const int T = K / BK;                        // sub-steps
 
   auto swz = [](int r, int c) { return c ^ ((r / RPB) & (PIECES - 1)); };
 
-  // --- x: DMA, wave instruction i writes 1 KB: rows xr0 + i*RPI, physical piece lane%PIECES.
-  // Byte offsets from the tile's first row fit 32 bits (BM <= 256 rows, K < 2^23).
+  // --- x DMA: wave instruction i writes 1 KB: rows xr0 + i*RPI, physical
+  // piece lane % PIECES. Byte offsets from the tile's first row fit 32 bits
+  // (BM rows, K < 2^23). Rows past M read row M-1 (discarded).
   const int xr0 = wave * XDMA * RPI + lane / PIECES;
   const char* xtile = reinterpret_cast<const char*>(x + (int64_t)m0 * K);
   uint32_t xoff[XDMA];
 #pragma unroll
   for (int i = 0; i < XDMA; ++i) {
     const int r = xr0 + i * RPI;
-    const int rr = m0 + r < M ? r : M - 1 - m0;                // rows past M: read row M-1, discarded
+    const int rr = m0 + r < M ? r : M - 1 - m0;
     xoff[i] = 2u * ((uint32_t)rr * (uint32_t)K + 8u * (uint32_t)swz(r, lane % PIECES));
   }
-
-  // --- weights: write i of a wave stores 1 KB of the B stage contiguously
-  // (piece P = (wave*WPT + i)*64 + lane, row P / PIECES, physical piece
-  // P % PIECES): ds_write_b128 has no bank conflicts on contiguous addresses.
-  // The thread loads the packed word of that row's logical piece.
-  const uint8_t* wsrc[WPT];
+  // --- W DMA: chunk c = wave*WDMA + i holds block rows 8c .. 8c+7 (128 B of
+  // each); lane l writes row 8c + l/8 at physical piece l % 8, which holds
+  // logical piece (l % 8) ^ ((row >> 1) & 7). Rows past N read row N-1.
+  const uint8_t* wsrc[WDMA];
+  int wpiece[WDMA];
 #pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int P = (wave * WPT + i) * 64 + lane;
-    const int row = P / PIECES, c = swz(row, P % PIECES);
-    int n = n0 + row;
-    n = n < N ? n : N - 1;                                     // tail rows: read, discarded
-    wsrc[i] = packed + (int64_t)n * (K >> 1) + 4 * c;
+  for (int i = 0; i < WDMA; ++i) {
+    const int R = 8 * (wave * WDMA + i) + lane / 8;
+    const int n = n0 + R < N ? n0 + R : N - 1;
+    wsrc[i] = packed + (int64_t)n * RB;
+    wpiece[i] = 16 * ((lane % 8) ^ ((R >> 1) & 7));
   }
-  // scales of the lane's output columns
+  // --- scales of the lane's two output columns
   const uint16_t* ssrc[TN];
 #pragma unroll
   for (int b = 0; b < TN; ++b) {
-    int n = n0 + wn * WNT + b * 32 + c32;
-    n = n < N ? n : N - 1;
-    ssrc[b] = scales + (int64_t)n * G;
+    const int n = n0 + wn * WNT + b * 32 + c32;
+    ssrc[b] = scales + (int64_t)(n < N ? n : N - 1) * G;
   }
-  const int T = K / BK;
-  const int spg_log = SPG == 0 ? gshift : SPG == 4 ? 2 : SPG == 2 ? 1 : 0;
-  uint32_t wr[NXS][WPT];                                       // w(t) in slot t % NXS
-  uint32_t sr[NXS][TN];                                        // s(t) in slot t % NXS
+  const int spg_log = SPG == 0 ? gshift : SPG == 8 ? 3 : SPG == 4 ? 2 : SPG == 2 ? 1 : 0;
 
-  // Loads of sub-step t's operands (an index past the end is clamped to the
-  // last sub-step; such data is never used).
-  auto load_w = [&](int t, int slot) {
+  // Loads (an index past the end is clamped to a valid address; such data is
+  // never used).
+  uint32_t sr[NXS][TN];                        // s(t) in slot t % NXS
+  auto issue_x = [&](int t, int stage) {
     const int tc = t < T ? t : T - 1;
-#pragma unroll
-    for (int i = 0; i < WPT; ++i)
-      wr[slot][i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wsrc[i] + tc * (BK / 2)));
-  };
-  auto load_sx = [&](int t, int slot, bool with_s) {
-    const int tc = t < T ? t : T - 1;
-    if (with_s) {
-      // Sub-steps of one group load the same scales; the opaque index keeps
-      // the compiler from merging such loads, which would change the load
-      // counts the waits rely on.
-      int gi = tc >> spg_log;
-      asm volatile("" : "+s"(gi));
-#pragma unroll
-      for (int b = 0; b < TN; ++b) sr[slot][b] = ssrc[b][gi];
-    }
     const char* base = xtile + (int64_t)tc * (2 * BK);
 #pragma unroll
     for (int i = 0; i < XDMA; ++i)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(base + xoff[i]),
-          reinterpret_cast<void*>(as + slot * A_HALVES + (wave * XDMA + i) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + xoff[i]),
+                                       reinterpret_cast<void*>(lds + stage * A_BYTES + (wave * XDMA + i) * 1024),
+                                       16, 0, 0);
   };
-  auto expand = [&](int slot, int bstage) {
+  auto issue_s = [&](int t, int slot) {
+    const int tc = t < T ? t : T - 1;
+    // Sub-steps of one group load the same scales; the opaque index keeps the
+    // compiler from merging such loads, which would change the load counts the
+    // waits rely on.
+    int gi = tc >> spg_log;
+    asm volatile("" : "+s"(gi));
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      half2_t hw[4];
-      codes_to_half_natural(wr[slot][i], hw);
-      *reinterpret_cast<half8_t*>(bs + bstage * B_HALVES + ((wave * WPT + i) * 64 + lane) * 8) = as_half8(hw);
+    for (int b = 0; b < TN; ++b) sr[slot][b] = ssrc[b][gi];
+  };
+  auto issue_w = [&](int st, int slot) {
+#pragma unroll
+    for (int i = 0; i < WDMA; ++i) {
+      int o = 128 * st + wpiece[i];
+      o = o < RB - 16 ? o : RB - 16;           // past the row end: valid, unused
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wsrc[i] + (uint32_t)o),
+                                       reinterpret_cast<void*>(lds + W_LDS + slot * W_BYTES + (wave * WDMA + i) * 1024),
+                                       16, 0, 0);
     }
+  };
+
+  // Operand LDS offsets. A, k-step s: row wm*128 + c32 (+ 32 a), logical
+  // piece KS*h + s. Packed W of lane (n = c32, h), tile b, sub-step u of a
+  // super-tile: bytes (BK/2) u + (BK/4) h of row wn*64 + 32 b + n, whose
+  // swizzle term (row >> 1) & 7 is (n >> 1) & 7.
+  int aoff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int ra = wm * WMT + c32;
+    aoff[s] = 2 * (ra * BK + 8 * swz(ra, KS * h + s));
+  }
+  const int wsw = (c32 >> 1) & 7;
+  auto woff = [&](int u, int b) {
+    const int byte = (BK / 2) * u + (BK / 4) * h;
+    return (wn * WNT + b * 32 + c32) * 128 + 16 * ((byte >> 4) ^ wsw) + (byte & 15);
   };
 
   float16_t acc[TM][TN];
@@ -207,108 +223,157 @@ __global__ __launch_bounds__(64 * WM * WN) void matmul_tiled_kernel(
 #pragma unroll
   for (int b = 0; b < TN; ++b) srun[b] = 0.0f;
 
-  // Operand LDS offsets (halves) for k-step s; m-tile a adds a*32 rows, n-tile b
-  // adds b*32 rows (whole swizzle periods, so the piece is unchanged).
-  int aoff[KS], boff[KS];
+  half8_t af[TM];                              // A fragments of the next k-step
+  uint32_t wp[TN][KS];                         // packed words of the current sub-step
+  auto read_a = [&](int stage, int s, half8_t* dst) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int c = (BK / 16) * h + s;
-    const int ra = wm * WMT + c32, rb = wn * WNT + c32;
-    aoff[s] = ra * BK + 8 * swz(ra, c);
-    boff[s] = rb * BK + 8 * swz(rb, c);
-  }
-
-  // The loads of one group may be issued in any order. Sub-step t needs s(t),
-  // x(t) and w(t+1) -- exactly the group that sub-step t-D issued -- so it
-  // waits until only the newer groups are pending. x(t+D) goes to the stage
-  // sub-step t-1 read, w(t+D+1) to the slot of w(t), which sub-step t-1
-  // expanded. Every load issued is used, so none is dropped by the compiler.
-  // Prologue: w0, then the groups of sub-steps -D .. -1, then expand w0
-  // (scheduling barriers keep the groups apart, as the waits assume).
-  load_w(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int g = 0; g < D; ++g) {
-    load_sx(g, g, s_used(g + U - D));
-    load_w(g + 1, g + 1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  constexpr auto prologue_loads = [group_loads]() {
-    int n = 0;
-    for (int g = 0; g < D; ++g) n += group_loads(g - D);
-    return n;
+    for (int a = 0; a < TM; ++a)
+      dst[a] = *reinterpret_cast<const half8_t*>(lds + stage * A_BYTES + aoff[s] + a * 32 * BK * 2);
   };
-  wait_vmcnt<prologue_loads()>();                              // w(0)
-  __builtin_amdgcn_sched_barrier(0);
-  expand(0, 0);
-
-  // Sub-step t = t0 + j with t0 a multiple of U: x stage, scale slot and
-  // weight slot j, B stage j % 2, all compile-time. In the tail (after the
-  // last whole block of U) no loads are issued.
-  auto substep = [&](auto J, auto Tail, int t) {
-    constexpr int j = decltype(J)::value;
-    constexpr bool tail = decltype(Tail)::value;
-    constexpr int p = j & 1;
-    wait_vmcnt<newer_loads(j, tail)>();                        // group of t-D landed
-    lds_barrier();                                             // x(t), B(t) visible; stages of t-1 free
-    // Keep every use of the awaited registers below the wait: a use hoisted
-    // above it makes the compiler add a wait of its own, and with LDS DMA in
-    // flight that wait is for every load.
-    __builtin_amdgcn_sched_barrier(0);
-    bool gstart;
-    if constexpr (SPG == 0) gstart = (t & ((1 << gshift) - 1)) == 0;
-    else gstart = j % SPG == 0;
-    float ratio[TN];
+  auto read_w = [&](int slot, int u, uint32_t (*dst)[KS]) {
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
-      const float sn = half_bits_to_float((uint16_t)sr[j][b]);
-      const bool live = gstart && sn != 0.0f;                  // zero scale: keep the running one
-      // srun / sn to within an ulp (a uniform relative error of the finished
-      // groups' part, far inside the tolerance); srun = 0 gives 0.
-      ratio[b] = live ? srun[b] * __builtin_amdgcn_rcpf(sn) : 1.0f;
-      srun[b] = live ? sn : srun[b];
+      const uint8_t* p = lds + W_LDS + slot * W_BYTES + woff(u, b);
+      if constexpr (BK == 64) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+        dst[b][0] = v.x; dst[b][1] = v.y; dst[b][2] = v.z; dst[b][3] = v.w;
+      } else {
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+        dst[b][0] = v.x; dst[b][1] = v.y;
+      }
     }
-    expand((j + 1) % U, p ^ 1);                                // w(t+1) -> B stage of t+1
-    if constexpr (!tail) {
-      load_sx(t + D, (j + D) % U, s_used(j));
-      load_w(t + D + 1, j);
+  };
+  auto expand_b = [&](const uint32_t (*w)[KS], int s, half8_t* bf) {
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      half2_t hw[4];
+      codes_to_half_natural(w[b][s], hw);
+      bf[b] = as_half8(hw);
     }
-    const _Float16* sa = as + j * A_HALVES;
-    const _Float16* sb = bs + p * B_HALVES;
+  };
+
+  // Prologue: load groups of the virtual sub-steps -3 (x0, s0, super-tile 0),
+  // -2 (x1, s1) and -1 (x2, s2); wait for the first, then read sub-step 0's
+  // k-step-0 fragments and packed words.
+  issue_x(0, 0);
+  issue_s(0, 0);
+  issue_w(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_x(1, 1);
+  if constexpr (s_used(1)) issue_s(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_x(2, 2);
+  if constexpr (s_used(2)) issue_s(2, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int prologue_newer = 2 * XDMA + (s_used(1) ? TN : 0) + (s_used(2) ? TN : 0);
+  wait_vmcnt<prologue_newer>();
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read_a(0, 0, af);
+  read_w(0, 0, wp);
+  // Sub-step 0 opens the first group: the running scale starts at s(0) (a
+  // zero scale leaves it 0, and the accumulator is still 0).
+#pragma unroll
+  for (int b = 0; b < TN; ++b) srun[b] = half_bits_to_float((uint16_t)sr[0][b]);
+
+  // Sub-step t = t0 + J, t0 a multiple of U: x stage J % NXS, W slot
+  // (J / SUB) % 2, scale slot J % NXS, all compile-time.
+  auto substep = [&](auto J_, int t) {
+    constexpr int J = decltype(J_)::value;
+    constexpr int ws = (J / SUB) % 2, xs = J % NXS;
+    constexpr int J1 = (J + 1) % U;
+    constexpr int xs1 = J1 % NXS, ws1 = (J1 / SUB) % 2, u1 = J1 % SUB;
+    // The group of sub-step t-2 (x(t+1), s(t+1), the super-tile of t+1) has
+    // landed once only the group of t-1 is newer.
+    wait_vmcnt<group_loads(J - 1)>();
+    lds_barrier();                             // data of t+1 visible; stages of t-1 free
+    // Keep every use of the awaited data below the wait: a use hoisted above
+    // it makes the compiler add a wait of its own, and with LDS DMA in flight
+    // that wait is for every load.
+    __builtin_amdgcn_sched_barrier(0);
+    issue_x(t + D, (J + D) % NXS);             // into the stage of t-1
+    if constexpr (s_used(J + D)) issue_s(t + D, (J + D) % NXS);
+    if constexpr (J % SUB == 0) issue_w(t / SUB + 1, ws ^ 1);
+    half8_t bcur[TN];
+    expand_b(wp, 0, bcur);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t wnext[TN][KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      half8_t af[TM], bf[TN];
+      half8_t cur[TM];
 #pragma unroll
-      for (int a = 0; a < TM; ++a) af[a] = *reinterpret_cast<const half8_t*>(sa + aoff[s] + a * 32 * BK);
-#pragma unroll
-      for (int b = 0; b < TN; ++b) bf[b] = *reinterpret_cast<const half8_t*>(sb + boff[s] + b * 32 * BK);
+      for (int a = 0; a < TM; ++a) cur[a] = af[a];
+      if (s + 1 < KS) {
+        read_a(xs, s + 1, af);
+      } else {                                 // sub-step t+1: k-step 0 and its packed words
+        read_a(xs1, 0, af);
+        read_w(ws1, u1, wnext);
+      }
+      half8_t bnext[TN];
+      if (s + 1 < KS) expand_b(wp, s + 1, bnext);
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          if (s == 0 && (SPG == 0 || gstart)) acc[a][b] *= ratio[b];
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[a], bcur[b], acc[a][b], 0, 0, 0);
+      if (s + 1 < KS) {
+        // one MFMA, three VALU (next k-step's codes), one LDS read
+#pragma unroll
+        for (int i = 0; i < TM * TN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          if (i < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+      } else {
+        // If t+1 opens a group, rescale now: the accumulators are not used
+        // again before sub-step t+1. Never past the last sub-step.
+        bool gnext;
+        if constexpr (SPG == 0) gnext = ((t + 1) & ((1 << gshift) - 1)) == 0;
+        else gnext = (J + 1) % SPG == 0;
+        gnext = gnext && t + 1 < T;
+        float ratio[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const float sn = half_bits_to_float((uint16_t)sr[xs1][b]);
+          const bool live = gnext && sn != 0.0f;   // zero scale: keep the running one
+          // srun / sn to within an ulp (a uniform relative error of the finished
+          // groups' part, far inside the tolerance); srun = 0 gives 0.
+          ratio[b] = live ? srun[b] * __builtin_amdgcn_rcpf(sn) : 1.0f;
+          srun[b] = live ? sn : srun[b];
+        }
+        if constexpr (SPG == 0 || (J + 1) % SPG == 0) {
+#pragma unroll
+          for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) acc[a][b] *= ratio[b];
+        }
+#pragma unroll
+        for (int i = 0; i < TM * TN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < TN; ++b) bcur[b] = bnext[b];
     }
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int i = 0; i < KS; ++i) wp[b][i] = wnext[b][i];
   };
 
-  using body = std::false_type;
-  using tail = std::true_type;
+  // Main loop over whole bodies, then the last partial body with each
+  // sub-step guarded (sub-steps skipped there are all at the end, so the
+  // load counts of the ones that run are unchanged).
   int t0 = 0;
-  for (; t0 + U <= T; t0 += U) {
-    substep(std::integral_constant<int, 0>(), body(), t0);
-    substep(std::integral_constant<int, 1>(), body(), t0 + 1);
-    if constexpr (U == 4) {
-      substep(std::integral_constant<int, 2>(), body(), t0 + 2);
-      substep(std::integral_constant<int, 3>(), body(), t0 + 3);
-    }
-  }
-  if (t0 < T) substep(std::integral_constant<int, 0>(), tail(), t0);
-  if constexpr (U == 4) {
-    if (t0 + 1 < T) substep(std::integral_constant<int, 1>(), tail(), t0 + 1);
-    if (t0 + 2 < T) substep(std::integral_constant<int, 2>(), tail(), t0 + 2);
-  }
-  wait_vmcnt<0>();                                             // no LDS DMA in flight at exit
+  for (; t0 + U <= T; t0 += U)
+    unroll<0, U>([&](auto J) { substep(J, t0 + decltype(J)::value); });
+  unroll<0, U>([&](auto J) {
+    if (t0 + decltype(J)::value < T) substep(J, t0 + decltype(J)::value);
+  });
+  wait_vmcnt<0>();                             // no LDS DMA in flight at exit
 
   // Epilogue: apply the last running scale; lane l holds column l%32 and rows
   // 8*(i/4) + 4*(l/32) + (i%4) of each 32x32 tile (register i).
@@ -324,23 +389,6 @@ __global__ __launch_bounds__(64 * WM * WN) void matmul_tiled_kernel(
       }
   }
 }
-
-// Launch one tiled configuration for group = BK << gs. Sub-steps per group
-// are a template parameter when they divide the unroll (NXS), else read at
-// run time.
-#define INT4DQ_TILED_LAUNCH(BM, BN, WM, WN, BK, NXS)                                          \
-  do {                                                                                        \
-    int gs = 0;                                                                               \
-    while ((int64_t(BK) << gs) < group) ++gs;                                                 \
-    auto kernel = matmul_tiled_kernel<BM, BN, WM, WN, BK, NXS, 0>;                            \
-    if (gs == 0) kernel = matmul_tiled_kernel<BM, BN, WM, WN, BK, NXS, 1>;                    \
-    else if (gs == 1) kernel = matmul_tiled_kernel<BM, BN, WM, WN, BK, NXS, 2>;               \
-    else if (gs == 2 && NXS == 4) kernel = matmul_tiled_kernel<BM, BN, WM, WN, BK, NXS, (NXS == 4 ? 4 : 0)>; \
-    const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);                         \
-    if (blocks >= (1ll << 31)) return hipErrorInvalidValue;                                   \
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * WM * WN), 0, stream, xh,      \
-                       (int)M, packed, scales, (int)N, (int)K, G, gs, y);                     \
-  } while (0)
 
 // BK for a group size, or 0 if the kernel does not take it (group / BK must be
 // a power of two: the group index of a sub-step is a shift).
@@ -367,9 +415,17 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   const int BK = tiled_bk(group);
   const int G = (int)((K + group - 1) / group);
   if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
-  const _Float16* xh = static_cast<const _Float16*>(x);
-  if (BK == 32) INT4DQ_TILED_LAUNCH(256, 128, 4, 2, 32, 4);
-  else INT4DQ_TILED_LAUNCH(256, 128, 4, 2, 64, 4);
+  const int64_t blocks = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
+  if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
+  int gs = 0;                                  // group = BK << gs
+  while ((int64_t(BK) << gs) < group) ++gs;
+  auto kernel = matmul_tiled_kernel<32, 1>;
+  if (BK == 64)
+    kernel = gs == 0 ? matmul_tiled_kernel<64, 1> : gs == 1 ? matmul_tiled_kernel<64, 2>
+           : gs == 2 ? matmul_tiled_kernel<64, 4> : gs == 3 ? matmul_tiled_kernel<64, 8>
+                     : matmul_tiled_kernel<64, 0>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     static_cast<const _Float16*>(x), (int)M, packed, scales, (int)N, (int)K, G, gs, y);
   return hipGetLastError();
 }
 
