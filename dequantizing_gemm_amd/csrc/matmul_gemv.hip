@@ -9,12 +9,17 @@
 // memory bandwidth.)
 //
 // With one activation row every packed byte is used for two flops, so the
-// kernel is a pure stream of the packed weights, and the way it reads them
-// decides its speed. A wavefront load instruction here covers 1 KB of one
-// weight row (lane l: bytes c*1024 + 16 l), i.e. eight full 128-byte lines:
-// this streams at the rate of a plain contiguous copy, where a layout that
-// feeds the matrix cores directly (16 rows x 64 bytes per instruction, half
-// lines) measured 12-25% slower. So the contraction runs on the VALU:
+// kernels here are pure streams of the packed weights, and the way they read
+// them decides their speed. Three variants, chosen by the launcher:
+//
+//  * large matrices (packed weights >= 48 MB, K <= 16384): whole rows per
+//    wavefront, 1 KB of one row per load, 4x4x4 MFMAs used on their diagonal
+//    (matmul_gemv_rows_kernel, below);
+//  * K <= 12288 with group = 32 << p: 4 rows x 256 bytes per load, which is
+//    directly the B operand of v_mfma_f32_4x4x4f16 (matmul_gemv_mfma_kernel);
+//  * everything else (K <= 32768, group a multiple of 32): the VALU kernel
+//    that follows, where a wavefront load covers 1 KB of one weight row
+//    (lane l: bytes c*1024 + 16 l):
 //
 //  * Block = C wavefronts x RW weight rows, C = ceil(row bytes / 1 KB).
 //    Wavefront c owns byte chunk c of each of the block's rows; its lane l
@@ -25,7 +30,7 @@
 //    codes_to_half_spread (9 VALU ops per 8 exact fp16 codes). Each word is
 //    then four v_dot2_f32_f16: exact products, fp32 sums.
 //  * The lane's integer dot product is multiplied by its group's scale
-//    (integer-first), summed over the wavefront (DPP and lane-swap
+//    (integer-first), summed over the wavefront (DPP and lane-read
 //    butterfly) and over the block's wavefronts in a fixed order through
 //    LDS: deterministic, no atomics.
 //  * Lanes past the end of a row (last chunk) read the row's last 16 bytes
@@ -298,6 +303,149 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   if (b == 0 && n0 + 4 * wave + j < N) y[n0 + 4 * wave + j] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// Row-streaming variant for large matrices (packed weights >= 48 MB, K <=
+// 16384): on those the launch is long enough for the read pattern to decide
+// the rate, and reading 1 KB of one row per load beats the 4-row layout above.
+//
+// Each wavefront owns whole rows r0, r0 + TW, r0 + 2 TW, ... (TW = all
+// wavefronts of the grid, at most 64 rows each). Lane l reads bytes
+// 1024 c + 16 l of every chunk c of a row, and holds the matching 32
+// activations of every chunk in registers (spread order, staged once per
+// block through LDS, zero past K). The dot products use v_mfma_f32_4x4x4f16
+// "on the diagonal": lane 4b+i supplies row i of block b's A (its own
+// activations) and column i of its B (its own codes), so D_b[i][i] -- register
+// i of lane 4b+i -- is the lane's own 4-code dot product, accumulated over its
+// 32 codes; the other D entries are unused. The lane scales its partial by its
+// group's scale (integer-first), the wavefront sums the 64 partials of a row
+// (DPP butterfly + four lane reads), and lane k keeps the row's result until
+// one store at the end. Two rows are in flight per wavefront: row k+2 is
+// issued as soon as row k has been consumed, with exact load counts.
+constexpr int kRowWaves = 8;                   // wavefronts per block
+
+template <int C>
+__global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
+    const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scales, int N, int K, int G, int group,
+    float* __restrict__ y) {
+  typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+  constexpr int P = 2;                         // rows in flight per wavefront
+  constexpr int NT = 64 * kRowWaves;
+  constexpr int XPT = (C * 256 + NT - 1) / NT; // 16-byte x units staged per thread
+  constexpr int LPR = 2 * C;                   // loads per row: C scales, C weight chunks
+  __shared__ __attribute__((aligned(16))) uint32_t xsp[XPT * NT * 4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int RB = K >> 1;
+  const int xunits = K >> 3;
+
+  // Per lane and chunk: byte offset in a row (past the row end: the row's
+  // last 16 bytes, multiplied by zero activations) and group index.
+  int off[C], sidx[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int o = 1024 * c + 16 * lane;
+    off[c] = o < RB - 16 ? o : RB - 16;
+    const int gi = (2 * o) / group;
+    sidx[c] = gi < G ? gi : G - 1;
+  }
+  const int TW = gridDim.x * kRowWaves;
+  const int r0 = blockIdx.x * kRowWaves + wave;
+  const int R = r0 < N ? (N - 1 - r0) / TW + 1 : 0;   // rows of this wavefront (<= 64)
+
+  u32x4_t w[P][C];
+  uint32_t sc[P][C];
+  // Loads of the wavefront's k-th row into slot `slot` (a constant at every
+  // call); rows past the end read row N-1 and are not stored.
+  auto issue = [&](int k, int slot) {
+    const int r = r0 + k * TW < N ? r0 + k * TW : N - 1;
+    const uint8_t* prow = packed + (int64_t)r * RB;
+    const uint16_t* srow = scales + (int64_t)r * G;
+#pragma unroll
+    for (int c = 0; c < C; ++c) sc[slot][c] = srow[sidx[c]];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      w[slot][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(prow + (uint32_t)off[c]));
+  };
+
+  // x loads, then the first P rows, then stage x (the row loads stay in flight).
+  u32x4_t xv[XPT];
+#pragma unroll
+  for (int t = 0; t < XPT; ++t) {
+    const int u = t * NT + tid < xunits ? t * NT + tid : xunits - 1;
+    xv[t] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(x) + 16u * (uint32_t)u);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<0, P>([&](auto S) {
+    issue(decltype(S)::value, decltype(S)::value);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  wait_vmcnt_gemv<P * LPR>();                  // x landed
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < XPT; ++t) {
+    const int u = t * NT + tid;
+    const uint32_t z = u < xunits ? 0xFFFFFFFFu : 0u;
+    u32x4_t sp;
+    sp.x = __builtin_amdgcn_perm(xv[t].z, xv[t].x, 0x05040100u) & z;
+    sp.y = __builtin_amdgcn_perm(xv[t].z, xv[t].x, 0x07060302u) & z;
+    sp.z = __builtin_amdgcn_perm(xv[t].w, xv[t].y, 0x05040100u) & z;
+    sp.w = __builtin_amdgcn_perm(xv[t].w, xv[t].y, 0x07060302u) & z;
+    *reinterpret_cast<u32x4_t*>(xsp + 4 * u) = sp;
+  }
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4_t xa[C][4];                            // lane's activations: units 256 c + 4 l .. +3
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xa[c][i] = *reinterpret_cast<const u32x4_t*>(xsp + 4 * (256 * c + 4 * lane + i));
+
+  const int jsel = lane & 3;
+  float yv = 0.0f;
+  // At least one pass (a wavefront without rows computes a clamped row and
+  // stores nothing): a guarded loop would let the compiler sink the first row
+  // loads below the barrier into the guard.
+  int k0 = 0;
+  do {
+    static_for<0, P>([&](auto S) {
+      constexpr int sl = decltype(S)::value;
+      const int k = k0 + sl;
+      wait_vmcnt_gemv<(P - 1) * LPR>();        // row k landed
+      __builtin_amdgcn_sched_barrier(0);
+      float part = 0.0f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          half2_t hw[4];
+          codes_to_half_spread(w[sl][c][i], hw);
+          const half4_t b0 = __builtin_bit_cast(half4_t, u32x2v_t{__builtin_bit_cast(uint32_t, hw[0]), __builtin_bit_cast(uint32_t, hw[1])});
+          const half4_t b1 = __builtin_bit_cast(half4_t, u32x2v_t{__builtin_bit_cast(uint32_t, hw[2]), __builtin_bit_cast(uint32_t, hw[3])});
+          const half4_t a0 = __builtin_bit_cast(half4_t, u32x2v_t{xa[c][i].x, xa[c][i].y});
+          const half4_t a1 = __builtin_bit_cast(half4_t, u32x2v_t{xa[c][i].z, xa[c][i].w});
+          d = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d, 0, 0, 0);
+        }
+        // the lane's own dot product is register (lane & 3); selects, not branches
+        const float d01 = (jsel & 1) ? d.y : d.x;
+        const float d23 = (jsel & 1) ? d.w : d.z;
+        part += half_bits_to_float((uint16_t)sc[sl][c]) * ((jsel & 2) ? d23 : d01);
+      }
+      const float tot = wave_sum(part);
+      yv = lane == k ? tot : yv;
+      __builtin_amdgcn_sched_barrier(0);
+      issue(k + P, sl);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    k0 += P;
+  } while (k0 < R);
+  wait_vmcnt_gemv<0>();
+  if (lane < R) y[r0 + lane * TW] = yv;
+}
+
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
                                     const uint8_t* packed, int64_t N, int64_t K,
                                     int64_t group) {
@@ -318,6 +466,29 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
   while ((32ll << gsh) < group) ++gsh;
   if ((32ll << gsh) != group) gsh = -1;
   const _Float16* xh0 = static_cast<const _Float16*>(x);
+  const int chunks = (int)((K / 2 + 1023) / 1024);            // 1 KB chunks per row
+  if (N * (K / 2) >= (48ll << 20) && chunks <= 8) {
+    // Large matrix: row streaming. 256 blocks of 8 wavefronts (more if a
+    // wavefront would own over 64 rows).
+    int64_t blocks = 256;
+    while ((N + blocks * kRowWaves - 1) / (blocks * kRowWaves) > 64) blocks *= 2;
+    const dim3 grid((unsigned)blocks), block(64 * kRowWaves);
+#define INT4DQ_GEMV_ROWS(CC)                                                                     \
+  hipLaunchKernelGGL(matmul_gemv_rows_kernel<CC>, grid, block, 0, stream, xh0, packed, scales,  \
+                     (int)N, (int)K, G, (int)group, y)
+    switch (chunks) {
+      case 1: INT4DQ_GEMV_ROWS(1); break;
+      case 2: INT4DQ_GEMV_ROWS(2); break;
+      case 3: INT4DQ_GEMV_ROWS(3); break;
+      case 4: INT4DQ_GEMV_ROWS(4); break;
+      case 5: INT4DQ_GEMV_ROWS(5); break;
+      case 6: INT4DQ_GEMV_ROWS(6); break;
+      case 7: INT4DQ_GEMV_ROWS(7); break;
+      default: INT4DQ_GEMV_ROWS(8); break;
+    }
+#undef INT4DQ_GEMV_ROWS
+    return hipGetLastError();
+  }
   const int cols = (int)((K / 2 + 255) / 256);                // 256-byte column blocks per row
   if (cols <= 24 && gsh >= 0 && g_gemv_mfma) {
     constexpr int W = g_gemv_waves;                              // wavefronts (4 rows each) per block
@@ -340,7 +511,6 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
 #undef INT4DQ_GEMV_MFMA
     return hipGetLastError();
   }
-  const int chunks = (int)((K / 2 + 1023) / 1024);
   // Rows per block: enough wavefronts in flight (about 4096) to keep every
   // memory channel busy, up to 4 rows per wavefront.
   const int64_t want = (int64_t)chunks * N / 4096;

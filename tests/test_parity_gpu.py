@@ -237,12 +237,14 @@ def test_matmul_kernels_agree(dq, N, K, g, M):
 
 
 @pytest.mark.parametrize("N,K,g", [(300, 11008, 128), (77, 4096, 96), (513, 2080, 32), (40, 32768, 128),
-                                   (10, 32, 32), (4099, 4096, 128), (8195, 4096, 64), (2051, 2048, 128)])
+                                   (10, 32, 32), (4099, 4096, 128), (8195, 4096, 64), (2051, 2048, 128),
+                                   (12300, 8224, 32), (24577, 4096, 96), (6700, 16384, 256)])
 def test_matmul_gemv_shapes(dq, N, K, g):
-    """The M = 1 row-streaming kernel: a partial last 1 KB chunk (K = 11008,
-    2080), a group that is not a power of two (96), the largest K it takes
-    (16 chunks), the smallest (one lane), and N tails for 1, 2 and 4 rows per
-    block."""
+    """The M = 1 kernels: a partial last 1 KB chunk (K = 11008, 2080), a group
+    that is not a power of two (96), the largest K (16 chunks), the smallest
+    (one lane), N tails for 1, 2 and 4 rows per block; and matrices of 48 MB
+    and more, which take the whole-row variant (partial last chunk, group 96,
+    its largest K, 16384, ragged rows per wavefront)."""
     say(f"case: gemv N={N} K={K} g={g}")
     w = np.random.default_rng(N + K).normal(0, 0.02, size=(N, K)).astype(np.float32)
     x = np.random.default_rng(K).normal(size=(1, K)).astype(np.float16)
@@ -268,6 +270,23 @@ def test_matmul_gemv_one_hot_exact(dq):
             e[0, k] = 1.0
             y = host(dq.int4_matmul_path(dev(e), pd, sd, K, g, "gemv"))
             assert np.array_equal(y[0].astype(np.float64), what[k]), f"k={k}"
+
+
+def test_matmul_gemv_rows_one_hot_exact(dq):
+    """One-hot x through the whole-row M = 1 variant (a 50 MB matrix, partial
+    last chunk): column k of (q * scale)^T bit-exactly."""
+    N, K, g = 12300, 8224, 32
+    say(f"case: gemv rows one-hot N={N} K={K} g={g}")
+    w = np.random.default_rng(5).normal(size=(N, K)).astype(np.float32)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    q = oracle.unpack_int4(pr, K)
+    pd, sd = dev(pr), dev(sr)
+    for k in (0, 1, 31, 32, 4111, 8191, 8192, K - 1):
+        e = np.zeros((1, K), dtype=np.float16)
+        e[0, k] = 1.0
+        y = host(dq.int4_matmul_path(dev(e), pd, sd, K, g, "gemv"))
+        col = q[:, k].astype(np.float64) * sr[:, k // g].astype(np.float64)
+        assert np.array_equal(y[0].astype(np.float64), col), f"k={k}"
 
 
 def test_matmul_fp32_x(dq):
