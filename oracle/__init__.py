@@ -65,6 +65,10 @@ def _declare(lib):
     lib.int4_oracle_unpack.restype = None
     lib.int4_oracle_matmul.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp, vp]
     lib.int4_oracle_matmul.restype = None
+    lib.int4_oracle_dequantize.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.int4_oracle_dequantize.restype = None
+    lib.int4_oracle_dequantize_half.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.int4_oracle_dequantize_half.restype = None
     return lib
 
 
@@ -115,6 +119,27 @@ def int4_matmul(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, K: int,
     lib.int4_oracle_matmul(_ptr(x), M, _ptr(packed), _ptr(s16), N, K, group, _ptr(y),
                            _ptr(bound) if with_bound else None)
     return (y, bound) if with_bound else y
+
+
+def dequantize_int4(packed: np.ndarray, scales: np.ndarray, K: int, group: int = 128,
+                    dtype=np.float32, lib=None) -> np.ndarray:
+    """w_hat [N, K] = q * scale, as float32 (exact) or float16 (the exact
+    product rounded to nearest even, by the oracle's own binary16 rounding)."""
+    lib = lib or load()
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    s16 = np.ascontiguousarray(np.asarray(scales).view(np.uint16))
+    N = packed.shape[0]
+    assert packed.shape[1] == (K + 1) // 2
+    assert s16.shape == (N, (K + group - 1) // group)
+    if np.dtype(dtype) == np.float32:
+        out = np.empty((N, K), dtype=np.float32)
+        lib.int4_oracle_dequantize(_ptr(packed), _ptr(s16), N, K, group, _ptr(out))
+        return out
+    if np.dtype(dtype) == np.float16:
+        out = np.empty((N, K), dtype=np.uint16)
+        lib.int4_oracle_dequantize_half(_ptr(packed), _ptr(s16), N, K, group, _ptr(out))
+        return out.view(np.float16)
+    raise ValueError(f"dtype {dtype}: float32 or float16")
 
 
 def half_from_float(f: float, lib=None) -> int:

@@ -234,3 +234,41 @@ void int4_oracle_matmul(const float *x, int64_t M, const uint8_t *packed,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* dequantize (drill page, statement: w_hat = q * scale; "Build a Blockwise */
+/* INT4 Inference Engine", the unfused dequantize-then-GEMM baseline):      */
+/* out[n, k] = q[n, k] * scale[n, k / group].                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * binary32 output. q has at most 4 significant bits and the widened scale at
+ * most 11, so the binary32 product is exact.
+ */
+void int4_oracle_dequantize(const uint8_t *packed, const uint16_t *scales,
+                            int64_t N, int64_t K, int64_t group, float *out)
+{
+    int64_t G = int4_oracle_num_groups(K, group);
+    int64_t B = int4_oracle_packed_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            float sf = int4_oracle_float_from_half(scales[n * G + k / group]);
+            out[n * K + k] = (float)nibble_value(packed + n * B, k) * sf;
+        }
+}
+
+/*
+ * binary16 output: the exact binary32 product rounded to the nearest
+ * binary16 (ties to even); magnitudes of 65520 and more become infinities.
+ */
+void int4_oracle_dequantize_half(const uint8_t *packed, const uint16_t *scales,
+                                 int64_t N, int64_t K, int64_t group, uint16_t *out)
+{
+    int64_t G = int4_oracle_num_groups(K, group);
+    int64_t B = int4_oracle_packed_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            float sf = int4_oracle_float_from_half(scales[n * G + k / group]);
+            out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k) * sf);
+        }
+}

@@ -390,4 +390,63 @@ def pin_p3_correctness_pattern(lib):
     assert float(np.abs(y - brute.int4_matmul(x, p, s, K, 128)).max()) < 1e-3
 
 
+# ---------------------------------------------------------------- dequantize
+
+def _dq(lib, p, s, K, g, dtype=np.float32):
+    return oracle.dequantize_int4(p, s, K, g, dtype=dtype, lib=lib)
+
+
+def pin_dequantize_p4_example(lib):
+    """P4's layout example [1,-1,7,-7], g=4: scale 1, so w_hat = w exactly, in
+    both output precisions."""
+    w = np.array([[1.0, -1.0, 7.0, -7.0]], np.float32)
+    p, s, K = _q(lib, w, 4)
+    assert _dq(lib, p, s, K, 4).tolist() == [[1.0, -1.0, 7.0, -7.0]]
+    assert _dq(lib, p, s, K, 4, np.float16).astype(np.float32).tolist() == [[1.0, -1.0, 7.0, -7.0]]
+
+
+def pin_dequantize_vs_brute(lib):
+    """w_hat equals the NumPy reconstruction (unpack, repeat the scales, multiply
+    in float64) exactly in float32, and NumPy's own float16 rounding of it
+    (ties to even) in float16; ragged groups, odd K, g = 1 .. 128."""
+    rng = np.random.default_rng(21)
+    for (N, K, g) in [(3, 1, 1), (5, 9, 2), (7, 31, 3), (4, 45, 5), (6, 64, 4), (9, 301, 128),
+                      (8, 256, 32), (5, 129, 64), (3, 7, 128)]:
+        w = rng.normal(size=(N, K)).astype(np.float32)
+        p, s, _ = _q(lib, w, g)
+        ref = brute.dequantize(p, s, K, g)
+        got = _dq(lib, p, s, K, g)
+        assert got.dtype == np.float32 and np.array_equal(got.astype(np.float64), ref), (N, K, g)
+        h = _dq(lib, p, s, K, g, np.float16)
+        assert np.array_equal(h.view(np.uint16), ref.astype(np.float16).view(np.uint16)), (N, K, g)
+
+
+def pin_dequantize_round_trip_and_idempotence(lib):
+    """P4's visible round-trip test through w_hat (|w_hat - w| <= half a step),
+    and Q(w_hat) = Q(w) bit for bit (the grid points are fixed points)."""
+    for seed in range(20):
+        w = np.random.default_rng(seed).normal(size=(8, 256)).astype(np.float32)
+        p, s, K = _q(lib, w, 128)
+        wh = _dq(lib, p, s, K, 128)
+        sf = np.repeat(s.astype(np.float32), 128, 1)
+        assert np.all(np.abs(wh - w) <= 0.5 * sf + 1e-3 * sf + 1e-6), seed
+        p2, s2, _ = _q(lib, wh, 128)
+        assert np.array_equal(p2, p) and np.array_equal(s2.view(np.uint16), s.view(np.uint16)), seed
+
+
+def pin_dequantize_extremes(lib):
+    """Subnormal scales give exact subnormal w_hat (c2's row of -8 * 2^-24);
+    the largest binary16 scale times -8 overflows binary16 to -inf but is exact
+    in float32."""
+    w = np.full((1, 6), -8 * TINY, np.float32)
+    p, s, K = _q(lib, w, 6)
+    assert np.array_equal(_dq(lib, p, s, K, 6), w)
+    assert np.array_equal(_dq(lib, p, s, K, 6, np.float16).astype(np.float32), w)
+    packed = np.array([[0x08]], np.uint8)                  # q = -8, then 0
+    scales = np.array([[0x7BFF]], np.uint16).view(np.float16)   # 65504
+    assert _dq(lib, packed, scales, 2, 2).tolist() == [[-524032.0, 0.0]]
+    h = _dq(lib, packed, scales, 2, 2, np.float16)
+    assert np.isneginf(h[0, 0]) and h[0, 1] == 0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

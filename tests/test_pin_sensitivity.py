@@ -55,6 +55,15 @@ MUTANTS = [
      "if (e < -14)\n        e = -14;", "if (e < -14)\n        return sign;"),
     ("half_overflow_threshold",
      "if (a >= 65520.0)", "if (a > 65504.0)"),
+    ("dequantize_swaps_nibbles",
+     "out[n * K + k] = (float)nibble_value(packed + n * B, k) * sf;",
+     "out[n * K + k] = (float)nibble_value(packed + n * B, k ^ 1) * sf;"),
+    ("dequantize_scale_of_next_group",
+     "float sf = int4_oracle_float_from_half(scales[n * G + k / group]);\n            out[n * K + k] = (float)",
+     "float sf = int4_oracle_float_from_half(scales[n * G + (k + 1) / group < G ? n * G + (k + 1) / group : 0]);\n            out[n * K + k] = (float)"),
+    ("dequantize_half_from_unscaled",
+     "out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k) * sf);",
+     "out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k));"),
     ("widen_subnormal_wrong",
      "v = ldexp((double)frac, -24);", "v = ldexp((double)(1024 + frac), -25);"),
 ]
