@@ -19,6 +19,11 @@ M = 2048 rate (2*M*N*K flops over the phase's time) is reported beside it,
 each as a fraction of the MI355X peak (HBM 8 TB/s; dense fp16 MFMA
 2.5 PFLOP/s).
 
+After the timed steps the fused matmul is compared, per shape and outside
+the step, with the unfused baseline the engine page measures it against:
+int4_dequantize to a float16 w_hat, then a library fp16 GEMM (torch's
+F.linear, hipBLASLt) on it ("unfused_baseline"; --no-unfused skips it).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
 
 --copy-probe adds, after the timed region, three plain device-to-device
@@ -111,6 +116,93 @@ def measured_traffic():
     return {k: v["traffic_bytes_per_launch"] for k, v in t.get("phases", {}).items()}
 
 
+def unfused_comparison(mats, pool, reps=20):
+    """Fused int4_matmul against dequantize-to-fp16 + library GEMM, per shape,
+    at M = 1 (weights from the HBM rotation pool) and M = 2048. Each variant is
+    captured in a HIP graph of `reps` calls and replayed; the best of three
+    replays counts. Returns microseconds per call and the HBM bytes each
+    variant moves for the weights."""
+    import torch
+    import torch.nn.functional as F
+    import dequantizing_gemm_amd as dq
+
+    L = dq.lib
+
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) * 1e3 / reps)
+        return best
+
+    out = {}
+    for M_, key in ((M_DECODE, "m1"), (M_PREFILL, "m2048")):
+        tot = {"fused_us": 0.0, "dequant_us": 0.0, "gemm_us": 0.0}
+        per = {}
+        for i, m in enumerate(mats):
+            N, K = m["N"], m["K"]
+            x = m["x1"] if M_ == M_DECODE else m["xp"]
+            y = m["y1"] if M_ == M_DECODE else m["yp"]
+            what = torch.empty((N, K), dtype=torch.float16, device=x.device)
+            copies = [pool[r][i] for r in range(len(pool))] if M_ == M_DECODE else [(m["packed"], m["scales"])]
+            it = {"k": 0}
+
+            def nxt():
+                p, s_ = copies[it["k"] % len(copies)]
+                it["k"] += 1
+                return p, s_
+
+            def fused():
+                p, s_ = nxt()
+                assert L.int4_matmul(x.data_ptr(), 1, M_, p.data_ptr(), s_.data_ptr(), N, K, GROUP,
+                                     y.data_ptr(), cur()) == 0
+
+            def dequant():
+                p, s_ = nxt()
+                assert L.int4_dequantize(p.data_ptr(), s_.data_ptr(), N, K, GROUP, 1, what.data_ptr(),
+                                         cur()) == 0
+
+            def gemm():
+                F.linear(x, what)
+
+            t_f, t_d, t_g = timed(fused), timed(dequant), timed(gemm)
+            per[m["name"]] = {"fused_us": round(t_f, 3), "dequant_us": round(t_d, 3),
+                              "gemm_us": round(t_g, 3)}
+            tot["fused_us"] += t_f
+            tot["dequant_us"] += t_d
+            tot["gemm_us"] += t_g
+            del what
+        unf = tot["dequant_us"] + tot["gemm_us"]
+        w_bytes = sum(packed_weight_bytes(m["N"], m["K"]) for m in mats)
+        fp16_bytes = sum(2 * m["N"] * m["K"] for m in mats)
+        out[key] = {"M": M_, "fused_us": round(tot["fused_us"], 3),
+                    "unfused_us": round(unf, 3), "dequant_us": round(tot["dequant_us"], 3),
+                    "gemm_us": round(tot["gemm_us"], 3),
+                    "fused_speedup": round(unf / tot["fused_us"], 3),
+                    "weight_bytes_fused": w_bytes,
+                    "weight_bytes_unfused": w_bytes + 2 * fp16_bytes,
+                    "per_shape": per}
+    out["note"] = ("three c4 shapes summed; unfused = int4_dequantize to fp16 w_hat (written to HBM) "
+                   "+ F.linear(x, w_hat) (hipBLASLt fp16 GEMM, fp16 output); fused = int4_matmul "
+                   "(fp32 output); weights from the HBM rotation pool at M = 1")
+    return out
+
+
 def packed_weight_bytes(N, K, g=GROUP):
     return N * ((K + 1) // 2) + 2 * N * ((K + g - 1) // g)
 
@@ -157,6 +249,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -310,6 +403,9 @@ def main():
         "rooflines": roofs,
         "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
     }
+    if not args.no_unfused:
+        print("bench: fused vs dequantize-then-GEMM", file=sys.stderr, flush=True)
+        line["unfused_baseline"] = unfused_comparison(mats, pool)
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -1,13 +1,17 @@
 """INT4 group quantization and fused dequantizing matmul for MI355X (gfx950).
 
 Thin binding over the C ABI in ``include/int4dq.h`` (``libint4dq.so``, built
-in-tree by ``dequantizing_gemm_amd.build``). The functions keep the names and
+in-tree by ``dequantizing_gemm_amd/build.py``). The functions keep the names and
 signatures of the drill page "Implement INT4 group quantization, nibble
 packing and a dequantizing matmul" (statement):
 
     quantize_int4(w, group=128) -> (packed, scales, K)
     unpack_int4(packed, K) -> int8 [N, K]
     int4_matmul(x, packed, scales, K, group=128) -> float32 [M, N]
+
+plus dequantize_int4(packed, scales, K, group=128, dtype=float16) -> w_hat [N, K],
+the reconstruction q * scale that an unfused dequantize-then-GEMM would
+materialise.
 
 All tensors are torch tensors on the GPU; torch provides the device memory and
 the stream (work is enqueued on ``torch.cuda.current_stream()``). Every step of
@@ -22,13 +26,14 @@ import os
 
 import torch
 
-__all__ = ["quantize_int4", "unpack_int4", "int4_matmul", "int4_matmul_path", "matmul_select",
+__all__ = ["quantize_int4", "unpack_int4", "dequantize_int4", "int4_matmul", "int4_matmul_path", "matmul_select",
            "num_groups", "packed_bytes", "lib", "LIB_PATH", "Int4Error", "PATHS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4dq.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 X_F32, X_F16 = 0, 1
+OUT_F32, OUT_F16 = 0, 1
 PATHS = {"auto": 0, "generic": 1, "skinny": 2, "tiled": 3, "gemv": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
@@ -39,6 +44,7 @@ SIGNATURES = {
     "int4_packed_bytes": (_i64, [_i64, _i64]),
     "int4_quantize": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "int4_unpack": (_int, [_vp, _i64, _i64, _vp, _vp]),
+    "int4_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "int4_matmul": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "int4_matmul_path": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "int4_matmul_select": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -53,7 +59,7 @@ class Int4Error(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m dequantizing_gemm_amd.build` (hipcc, gfx950)")
+                          "`python dequantizing_gemm_amd/build.py` (hipcc, gfx950)")
     cdll = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(cdll, name)
@@ -124,6 +130,27 @@ def unpack_int4(packed: torch.Tensor, K: int) -> torch.Tensor:
     with torch.cuda.device(packed.device):
         rc = lib.int4_unpack(packed.data_ptr(), N, K, out.data_ptr(), _stream(packed))
     _raise(rc, "int4_unpack")
+    return out
+
+
+def dequantize_int4(packed: torch.Tensor, scales: torch.Tensor, K: int, group: int = 128,
+                    dtype: torch.dtype = torch.float16) -> torch.Tensor:
+    """w_hat [N, K] = q * scale as float32 (exact) or float16 (nearest even)."""
+    _gpu(packed, "packed", torch.uint8)
+    _gpu(scales, "scales", torch.float16)
+    N = packed.shape[0]
+    if packed.shape[1] != (K + 1) // 2:
+        raise ValueError(f"packed has {packed.shape[1]} bytes per row, K={K} needs {(K + 1) // 2}")
+    if tuple(scales.shape) != (N, num_groups(K, group)):
+        raise ValueError(f"scales shape {tuple(scales.shape)} != {(N, num_groups(K, group))}")
+    if dtype not in (torch.float32, torch.float16):
+        raise ValueError(f"dtype must be float32 or float16 (got {dtype})")
+    out = torch.empty((N, K), dtype=dtype, device=packed.device)
+    with torch.cuda.device(packed.device):
+        rc = lib.int4_dequantize(packed.data_ptr(), scales.data_ptr(), N, K, group,
+                                 OUT_F16 if dtype == torch.float16 else OUT_F32, out.data_ptr(),
+                                 _stream(packed))
+    _raise(rc, "int4_dequantize")
     return out
 
 

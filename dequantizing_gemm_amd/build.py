@@ -1,6 +1,8 @@
 """Build libint4dq.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: ``python -m dequantizing_gemm_amd.build`` (or ``__graft_entry__.build()``).
+Usage: ``python dequantizing_gemm_amd/build.py`` (or ``__graft_entry__.build()``). It
+is run by path, not as ``-m``: importing the package loads the library, which
+may be missing or older than the sources being built.
 Object files go to ``_build/`` at the repository root; the shared library is
 written next to this file, where the binding loads it.
 """
@@ -33,8 +35,8 @@ HIPFLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-SOURCES = ["api.cpp", "quantize.hip", "unpack.hip", "matmul_generic.hip", "matmul_skinny.hip",
-           "matmul_tiled.hip", "matmul_gemv.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "unpack.hip", "dequantize.hip", "matmul_generic.hip",
+           "matmul_skinny.hip", "matmul_tiled.hip", "matmul_gemv.hip"]
 
 # The tiled and gemv kernels read or rescale their MFMA accumulators with VALU
 # ops; selecting the VGPR form of the MFMA instructions keeps the accumulators

@@ -103,6 +103,21 @@ int int4_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* out, void* 
   return hip_status(int4dq::launch_unpack(packed, N, K, out, (hipStream_t)stream), "int4_unpack launch");
 }
 
+int int4_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
+                    int64_t group, int out_dtype, void* out, void* stream) {
+  if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "int4_dequantize: N and K must be >= 1 (got N=%lld K=%lld)", (long long)N, (long long)K);
+  if (group < 1) return fail(INT4DQ_EINVAL, "int4_dequantize: group must be >= 1 (got %lld)", (long long)group);
+  if (out_dtype != INT4DQ_OUT_F32 && out_dtype != INT4DQ_OUT_F16)
+    return fail(INT4DQ_EINVAL, "int4_dequantize: unknown out_dtype %d", out_dtype);
+  int64_t t;
+  if (!mul_ok(N, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(N, (K + group - 1) / group, &t) || !mul_ok(t, 2, &t))
+    return fail(INT4DQ_EINVAL, "int4_dequantize: sizes overflow int64");
+  if (!packed || !scales || !out) return fail(INT4DQ_EINVAL, "int4_dequantize: packed, scales and out must be non-NULL");
+  return hip_status(int4dq::launch_dequantize(packed, scales, N, K, group, out_dtype == INT4DQ_OUT_F16, out,
+                                              (hipStream_t)stream),
+                    "int4_dequantize launch");
+}
+
 int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                      const uint16_t* scales, int64_t N, int64_t K, int64_t group, float* y,
                      int path, void* stream) {

@@ -14,6 +14,9 @@ hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, 
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* out,
                          hipStream_t stream);
 
+hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
+                             int64_t group, bool half, void* out, hipStream_t stream);
+
 hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                                  const uint16_t* scales, int64_t N, int64_t K, int64_t group,
                                  float* y, hipStream_t stream);

@@ -50,6 +50,10 @@ extern "C" {
 #define INT4DQ_X_F32 0         /* IEEE binary32 */
 #define INT4DQ_X_F16 1         /* IEEE binary16 */
 
+/* Element type of the output of int4_dequantize. */
+#define INT4DQ_OUT_F32 0       /* IEEE binary32 */
+#define INT4DQ_OUT_F16 1       /* IEEE binary16 */
+
 /* Kernel selection for int4_matmul_path (int4_matmul always uses AUTO). */
 #define INT4DQ_PATH_AUTO    0  /* choose by M, dtype and alignment */
 #define INT4DQ_PATH_GENERIC 1  /* VALU kernel, any shape, any group, fp32 or fp16 x */
@@ -98,6 +102,22 @@ int int4_quantize(const float *w, int64_t N, int64_t K, int64_t group,
  *   Errors: EINVAL if N or K < 1, a pointer is NULL, or sizes overflow.
  */
 int int4_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *out, void *stream);
+
+/*
+ * Dequantize (drill page, statement: the reconstruction w_hat = q * scale;
+ * "Build a Blockwise INT4 Inference Engine": the materialised weights of the
+ * unfused dequantize-then-GEMM baseline that the fused matmul avoids).
+ *   packed  in : [N, ceil(K/2)] bytes, scales in: [N, G] binary16, as written
+ *                by int4_quantize with the same K and group.
+ *   out     out: [N, K] of out_dtype. INT4DQ_OUT_F32: q * scale exactly (q has
+ *                4 significant bits and the scale 11). INT4DQ_OUT_F16: that
+ *                exact product rounded to the nearest binary16, ties to even
+ *                (magnitudes from 65520 up become infinities).
+ *   Errors: EINVAL if N, K or group < 1, a pointer is NULL, out_dtype is
+ *   unknown, or sizes overflow.
+ */
+int int4_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, int64_t K,
+                    int64_t group, int out_dtype, void *out, void *stream);
 
 /*
  * int4_matmul (drill page, statement):

@@ -14,9 +14,8 @@ HEADER = os.path.join(ROOT, "include", "int4dq.h")
 
 
 def _lib():
-    from dequantizing_gemm_amd import build as hipbuild
-    if not os.path.exists(hipbuild.LIB):
-        hipbuild.build()
+    import __graft_entry__
+    __graft_entry__._ensure_built()
     import dequantizing_gemm_amd as dq
     return dq
 
@@ -28,7 +27,7 @@ def _declared():
 
 
 def test_header_declares_the_abi():
-    assert _declared() == sorted(["int4_num_groups", "int4_packed_bytes", "int4_quantize",
+    assert _declared() == sorted(["int4_num_groups", "int4_packed_bytes", "int4_quantize", "int4_dequantize",
                                   "int4_unpack", "int4_matmul", "int4_matmul_path",
                                   "int4_matmul_select", "int4_last_error"])
 
@@ -79,6 +78,22 @@ def test_unpack_rejects():
     assert dq.lib.int4_unpack(None, 2, 8, FAKE, None) == dq.EINVAL
     assert dq.lib.int4_unpack(FAKE, 2, 8, None, None) == dq.EINVAL
     assert dq.lib.int4_unpack(FAKE, 2 ** 40, 2 ** 40, FAKE, None) == dq.EINVAL
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((FAKE, FAKE, 0, 8, 4, 1, FAKE, None), "N and K"),
+    ((FAKE, FAKE, 4, 0, 4, 1, FAKE, None), "N and K"),
+    ((FAKE, FAKE, 4, 8, 0, 1, FAKE, None), "group"),
+    ((FAKE, FAKE, 4, 8, 4, 2, FAKE, None), "out_dtype"),
+    ((None, FAKE, 4, 8, 4, 1, FAKE, None), "non-NULL"),
+    ((FAKE, None, 4, 8, 4, 1, FAKE, None), "non-NULL"),
+    ((FAKE, FAKE, 4, 8, 4, 0, None, None), "non-NULL"),
+    ((FAKE, FAKE, 2 ** 40, 2 ** 30, 4, 0, FAKE, None), "overflow"),
+])
+def test_dequantize_rejects(args, needle):
+    dq = _lib()
+    assert dq.lib.int4_dequantize(*args) == dq.EINVAL
+    assert needle in dq.lib.int4_last_error().decode()
 
 
 @pytest.mark.parametrize("kw,needle", [

@@ -201,6 +201,63 @@ def test_guard_bytes(dq):
     check_matmul(yh[pad:-pad].reshape(M, N), x, pr, sr, K, g, what="guarded")
 
 
+# --------------------------------------------------------- dequantize parity
+
+@pytest.mark.parametrize("key,case", ALL_CASES, ids=[f"{k}-{c.name}" for k, c in ALL_CASES])
+def test_dequantize_bit_exact(dq, key, case):
+    """w_hat = q * scale on every config's matrices: float32 exactly, float16
+    rounded to nearest even, both bit for bit against the oracle."""
+    _, w, p_ref, s_ref = _case_data(key, case.name)
+    say(f"case: dequantize {key} {case.name} [{case.N},{case.K}] g={case.group}")
+    pd, sd = dev(p_ref), dev(s_ref)
+    for dt, npdt in ((torch.float32, np.float32), (torch.float16, np.float16)):
+        got = host(dq.dequantize_int4(pd, sd, case.K, case.group, dtype=dt))
+        ref = oracle.dequantize_int4(p_ref, s_ref, case.K, case.group, dtype=npdt)
+        view = np.uint32 if npdt == np.float32 else np.uint16
+        assert np.array_equal(got.view(view), ref.view(view)), f"{key}/{case.name} {npdt.__name__}"
+
+
+@pytest.mark.parametrize("N,K,g,off", [(7, 301, 1, 0), (9, 33, 3, 0), (6, 200, 96, 0), (5, 64, 32, 1),
+                                       (40, 1000, 7, 0), (3, 4096, 128, 2), (130, 96, 48, 0)])
+def test_dequantize_ragged_and_unaligned(dq, N, K, g, off):
+    """The element-wise kernel: odd K, groups that are not multiples of 32, and
+    packed data or output at offsets that are not 16-byte aligned."""
+    say(f"case: dequantize ragged N={N} K={K} g={g} offset={off}")
+    w = np.random.default_rng(N * K).normal(size=(N, K)).astype(np.float32)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    B = (K + 1) // 2
+    pbuf = torch.zeros(N * B + off, dtype=torch.uint8, device="cuda")
+    pbuf[off:] = dev(pr).reshape(-1)
+    sd = dev(sr)
+    for dt, npdt in ((torch.float32, np.float32), (torch.float16, np.float16)):
+        obuf = torch.full((N * K + off,), 7.0, dtype=dt, device="cuda")
+        rc = dq.lib.int4_dequantize(pbuf.data_ptr() + off, sd.data_ptr(), N, K, g,
+                                    dq.OUT_F16 if dt == torch.float16 else dq.OUT_F32,
+                                    obuf.data_ptr() + off * obuf.element_size(),
+                                    torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, dq.lib.int4_last_error()
+        got = host(obuf)
+        assert np.all(got[:off] == 7.0)
+        ref = oracle.dequantize_int4(pr, sr, K, g, dtype=npdt)
+        view = np.uint32 if npdt == np.float32 else np.uint16
+        assert np.array_equal(got[off:].reshape(N, K).view(view), ref.view(view)), npdt.__name__
+
+
+def test_dequantize_extremes(dq):
+    """Subnormal scales (c2's -8 * 2^-24 row) and binary16 overflow of
+    -8 * 65504 in the float16 output, through both kernels."""
+    say("case: dequantize extremes")
+    for K, g in ((64, 32), (6, 6)):
+        packed = np.full((2, K // 2), 0x88, np.uint8)                  # every code -8
+        scales = np.array([[0x0001] * (K // g), [0x7BFF] * (K // g)], np.uint16).view(np.float16)
+        for dt, npdt in ((torch.float32, np.float32), (torch.float16, np.float16)):
+            got = host(dq.dequantize_int4(dev(packed), dev(scales), K, g, dtype=dt))
+            ref = oracle.dequantize_int4(packed, scales, K, g, dtype=npdt)
+            view = np.uint32 if npdt == np.float32 else np.uint16
+            assert np.array_equal(got.view(view), ref.view(view)), (K, npdt.__name__)
+        assert float(got[0, 0]) == -8 * 2.0 ** -24 and np.isneginf(got[1, 0])
+
+
 # ------------------------------------------------------------- matmul parity
 
 MM_CASES = [(k, c, M) for (k, c) in ALL_CASES for M in c.Ms]
