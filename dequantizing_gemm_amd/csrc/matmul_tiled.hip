@@ -11,7 +11,9 @@
 //
 // Block tile 256 (rows of x) x 128 (weight rows), 256 threads = 2 x 2
 // wavefronts, one per SIMD, each owning 128 x 64 outputs as 4 x 2 tiles of
-// v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 VGPRs). Larger wave tiles
+// v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 VGPRs); for a few hundred
+// rows of x the block keeps 128 or 64 rows (2 x 2 or 1 x 2 tiles per
+// wavefront) so that the grid still covers every CU. Larger wave tiles
 // than 64 x 64 halve the LDS bytes read per MFMA, which bounds this kernel.
 // K advances in sub-steps of BK = min(group, 64) codes:
 //  * x tiles [256 x BK] fp16 go global -> LDS by DMA (global_load_lds, 16 B
@@ -72,46 +74,63 @@ __device__ __forceinline__ void unroll(F&& f) {
   }
 }
 
-constexpr int kTileM = 256, kTileN = 128, kThreads = 256;
+constexpr int kTileN = 128, kThreads = 256;
 }  // namespace
 
 // BK: codes per sub-step (32 or 64). SPG: sub-steps per group (1, 2, 4 or 8),
-// or 0: any power of two 2^gshift, decided at run time.
-template <int BK, int SPG>
+// or 0: any power of two 2^gshift, decided at run time. TM: 32-row MFMA tiles
+// per wavefront in M (4, 2 or 1: block tiles of 256, 128 or 64 rows; the
+// smaller ones keep every CU busy when M is a few hundred rows).
+template <int BK, int SPG, int TM>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int gshift,
     float* __restrict__ y) {
-  constexpr int BM = kTileM, BN = kTileN, WN = 2, NW = 4;
-  constexpr int WMT = 128, WNT = 64, TM = 4, TN = 2;   // wave tile, in 32x32 MFMA tiles
+  constexpr int BM = 64 * TM, BN = kTileN, WN = 2, NW = 4;
+  constexpr int WMT = 32 * TM, WNT = 64, TN = 2;       // wave tile; TM x TN 32x32 MFMA tiles
   constexpr int KS = BK / 16;                  // MFMA k-steps per sub-step
   constexpr int PIECES = BK / 8;               // 16-byte pieces per x row per stage
   constexpr int RPB = 16 / PIECES;             // x rows per 256-byte bank period
-  constexpr int NXS = 4, D = 3;                // x ring stages, x prefetch distance
+  // x ring stages and prefetch distance; packed super-tile slots. (Deeper
+  // rings for the small tiles -- 8 stages, 4 slots -- measured no faster: with
+  // 64-row tiles a block is bound by its own instruction stream, not latency.)
+  constexpr int NXS = 4, D = NXS - 1;
+  constexpr int WS = 2;
   constexpr int A_BYTES = BM * BK * 2;         // one x stage
   constexpr int XDMA = BM * PIECES / (64 * NW);// x DMA instructions per wave per sub-step
   constexpr int RPI = 64 / PIECES;             // x rows per DMA instruction
   constexpr int SUB = 256 / BK;                // sub-steps per packed super-tile
-  constexpr int U = 2 * SUB;                   // sub-steps per unrolled body
+  constexpr int U = WS * SUB;                  // sub-steps per unrolled body
   constexpr int W_BYTES = BN * 128;            // one packed super-tile
   constexpr int WDMA = W_BYTES / 1024 / NW;    // W DMA instructions per wave per super-tile
   static_assert(BK == 32 || BK == 64, "sub-step");
+  static_assert(TM == 1 || TM == 2 || TM == 4, "wave tile");
+  static_assert(XDMA >= 1 && XDMA * 64 * NW == BM * PIECES, "x DMA split");
   static_assert(SPG == 0 || U % SPG == 0, "sub-steps per group");
-  static_assert(NXS * A_BYTES + 2 * W_BYTES <= 160 * 1024, "LDS");
+  static_assert(NXS * A_BYTES + WS * W_BYTES <= 160 * 1024, "LDS");
+  static_assert(U % NXS == 0 && SUB * (WS - 1) >= D && D % SUB != 0, "ring indices and weight lead");
   // Sub-step t issues x(t+D), s(t+D) when t+D opens a group (every sub-step
-  // when SPG is decided at run time), and super-tile t/SUB + 1 when t is the
-  // first sub-step of a super-tile. Sizes by position in the unrolled body.
+  // when SPG is decided at run time), and super-tile t/SUB + WS - 1 when t is
+  // the first sub-step of a super-tile. Sizes by position in the unrolled body.
   constexpr auto s_used = [](int j) { return SPG == 0 || (((j % U) + U) % U) % SPG == 0; };
   constexpr auto group_loads = [s_used](int j) {
     const int jj = ((j % U) + U) % U;
     return XDMA + (s_used(jj + D) ? TN : 0) + (jj % SUB == 0 ? WDMA : 0);
+  };
+  // Sub-step t needs x(t+1) and s(t+1) (loaded by the group of t+1-D; the
+  // super-tile of t+1 was loaded earlier still): the groups of t+2-D .. t-1 may
+  // still be in flight.
+  constexpr auto newer_loads = [group_loads](int j) {
+    int n = 0;
+    for (int i = 1; i <= D - 2; ++i) n += group_loads(j - i);
+    return n;
   };
 
   // One array for both rings: with stages and slots at constant offsets the
   // compiler can tell the DMA targets from the regions being read. Every LDS
   // address is written as an offset from the array itself (not from a pointer
   // variable into it), which keeps the DMA destinations scalar.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NXS * A_BYTES + 2 * W_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NXS * A_BYTES + WS * W_BYTES];
   constexpr int W_LDS = NXS * A_BYTES;         // offset of the packed-weight slots
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -252,21 +271,31 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     }
   };
 
-  // Prologue: load groups of the virtual sub-steps -3 (x0, s0, super-tile 0),
-  // -2 (x1, s1) and -1 (x2, s2); wait for the first, then read sub-step 0's
-  // k-step-0 fragments and packed words.
-  issue_x(0, 0);
-  issue_s(0, 0);
-  issue_w(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue_x(1, 1);
-  if constexpr (s_used(1)) issue_s(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  issue_x(2, 2);
-  if constexpr (s_used(2)) issue_s(2, 2);
-  __builtin_amdgcn_sched_barrier(0);
-  constexpr int prologue_newer = 2 * XDMA + (s_used(1) ? TN : 0) + (s_used(2) ? TN : 0);
-  wait_vmcnt<prologue_newer>();
+  // Prologue: the load groups of the virtual sub-steps -D .. -1, built like
+  // the steady state's (x(t+D), s(t+D), super-tile t/SUB + WS - 1 where t is
+  // a multiple of SUB), the first one also carrying the super-tiles that the
+  // steady state would have loaded before it. Then wait for that first group
+  // and read sub-step 0's k-step-0 fragments and packed words.
+  constexpr int catch_up = WS - (D + SUB - 1) / SUB;   // super-tiles 0 .. catch_up-1
+  unroll<0, D>([&](auto I_) {
+    constexpr int t = decltype(I_)::value - D;
+    issue_x(t + D, (t + D) % NXS);
+    if constexpr (t == -D) {
+      issue_s(0, 0);
+#pragma unroll
+      for (int st = 0; st < catch_up; ++st) issue_w(st, st % WS);
+    } else {
+      if constexpr (s_used(t + D)) issue_s(t + D, (t + D) % NXS);
+      if constexpr (t % SUB == 0) issue_w(t / SUB + WS - 1, (t / SUB + WS - 1) % WS);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  constexpr auto prologue_newer = [group_loads]() {
+    int n = 0;
+    for (int i = 1; i <= D - 1; ++i) n += group_loads(-i);
+    return n;
+  };
+  wait_vmcnt<prologue_newer()>();
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_a(0, 0, af);
@@ -277,15 +306,13 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   for (int b = 0; b < TN; ++b) srun[b] = half_bits_to_float((uint16_t)sr[0][b]);
 
   // Sub-step t = t0 + J, t0 a multiple of U: x stage J % NXS, W slot
-  // (J / SUB) % 2, scale slot J % NXS, all compile-time.
+  // (J / SUB) % WS, scale slot J % NXS, all compile-time.
   auto substep = [&](auto J_, int t) {
     constexpr int J = decltype(J_)::value;
-    constexpr int ws = (J / SUB) % 2, xs = J % NXS;
+    constexpr int ws = (J / SUB) % WS, xs = J % NXS;
     constexpr int J1 = (J + 1) % U;
-    constexpr int xs1 = J1 % NXS, ws1 = (J1 / SUB) % 2, u1 = J1 % SUB;
-    // The group of sub-step t-2 (x(t+1), s(t+1), the super-tile of t+1) has
-    // landed once only the group of t-1 is newer.
-    wait_vmcnt<group_loads(J - 1)>();
+    constexpr int xs1 = J1 % NXS, ws1 = (J1 / SUB) % WS, u1 = J1 % SUB;
+    wait_vmcnt<newer_loads(J)>();
     lds_barrier();                             // data of t+1 visible; stages of t-1 free
     // Keep every use of the awaited data below the wait: a use hoisted above
     // it makes the compiler add a wait of its own, and with LDS DMA in flight
@@ -293,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     __builtin_amdgcn_sched_barrier(0);
     issue_x(t + D, (J + D) % NXS);             // into the stage of t-1
     if constexpr (s_used(J + D)) issue_s(t + D, (J + D) % NXS);
-    if constexpr (J % SUB == 0) issue_w(t / SUB + 1, ws ^ 1);
+    if constexpr (J % SUB == 0) issue_w(t / SUB + WS - 1, (ws + WS - 1) % WS);
     half8_t bcur[TN];
     expand_b(wp, 0, bcur);
     __builtin_amdgcn_sched_barrier(0);
@@ -415,15 +442,22 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   const int BK = tiled_bk(group);
   const int G = (int)((K + group - 1) / group);
   if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
-  const int64_t blocks = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
+  const int64_t ntiles = (N + kTileN - 1) / kTileN;
+  // Block rows: 256 unless that leaves most CUs idle (a few hundred rows of x);
+  // then 128 or 64, whichever first gives about one block per CU.
+  int TM = 4;
+  while (TM > 1 && ((M + 64 * TM - 1) / (64 * TM)) * ntiles < 200) TM /= 2;
+  const int64_t blocks = ((M + 64 * TM - 1) / (64 * TM)) * ntiles;
   if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
   int gs = 0;                                  // group = BK << gs
   while ((int64_t(BK) << gs) < group) ++gs;
-  auto kernel = matmul_tiled_kernel<32, 1>;
-  if (BK == 64)
-    kernel = gs == 0 ? matmul_tiled_kernel<64, 1> : gs == 1 ? matmul_tiled_kernel<64, 2>
-           : gs == 2 ? matmul_tiled_kernel<64, 4> : gs == 3 ? matmul_tiled_kernel<64, 8>
-                     : matmul_tiled_kernel<64, 0>;
+#define INT4DQ_TILED_PICK(TMV)                                                                  \
+  (BK == 32 ? matmul_tiled_kernel<32, 1, TMV>                                                   \
+   : gs == 0 ? matmul_tiled_kernel<64, 1, TMV> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV>     \
+   : gs == 2 ? matmul_tiled_kernel<64, 4, TMV> : gs == 3 ? matmul_tiled_kernel<64, 8, TMV>      \
+             : matmul_tiled_kernel<64, 0, TMV>)
+  const auto kernel = TM == 4 ? INT4DQ_TILED_PICK(4) : TM == 2 ? INT4DQ_TILED_PICK(2) : INT4DQ_TILED_PICK(1);
+#undef INT4DQ_TILED_PICK
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const _Float16*>(x), (int)M, packed, scales, (int)N, (int)K, G, gs, y);
   return hipGetLastError();
