@@ -65,6 +65,8 @@ def _declare(lib):
     lib.int4_oracle_unpack.restype = None
     lib.int4_oracle_matmul.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp, vp]
     lib.int4_oracle_matmul.restype = None
+    lib.int4_oracle_matmul_ex.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp, ctypes.c_int, vp, vp]
+    lib.int4_oracle_matmul_ex.restype = None
     lib.int4_oracle_dequantize.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.int4_oracle_dequantize.restype = None
     lib.int4_oracle_dequantize_half.argtypes = [vp, vp, i64, i64, i64, vp]
@@ -118,6 +120,29 @@ def int4_matmul(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, K: int,
     bound = np.empty((M, N), dtype=np.float64) if with_bound else None
     lib.int4_oracle_matmul(_ptr(x), M, _ptr(packed), _ptr(s16), N, K, group, _ptr(y),
                            _ptr(bound) if with_bound else None)
+    return (y, bound) if with_bound else y
+
+
+def int4_matmul_ex(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, K: int,
+                   group: int = 128, bias: np.ndarray | None = None, relu: bool = False,
+                   with_bound: bool = False, lib=None):
+    """y [M, N] float32 = act(x @ dequantize(W).T + bias): the matmul sum and the
+    bias in double, rounded once, then ReLU (v > 0 ? v : +0) if asked."""
+    lib = lib or load()
+    x = np.ascontiguousarray(np.asarray(x).astype(np.float32))
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    s16 = np.ascontiguousarray(np.asarray(scales).view(np.uint16))
+    M = x.shape[0]
+    N = packed.shape[0]
+    assert x.shape[1] == K and packed.shape[1] == (K + 1) // 2
+    assert s16.shape == (N, (K + group - 1) // group)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    assert b is None or b.shape == (N,)
+    y = np.empty((M, N), dtype=np.float32)
+    bound = np.empty((M, N), dtype=np.float64) if with_bound else None
+    lib.int4_oracle_matmul_ex(_ptr(x), M, _ptr(packed), _ptr(s16), N, K, group,
+                              _ptr(b) if b is not None else None, int(bool(relu)), _ptr(y),
+                              _ptr(bound) if with_bound else None)
     return (y, bound) if with_bound else y
 
 

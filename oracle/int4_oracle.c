@@ -204,35 +204,15 @@ void int4_oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *out
  * bound: optional [M, N] binary64, sum over k of |x[m,k] * q[n,k] * scale|,
  *        the magnitude against which the tolerance is stated.
  */
+void int4_oracle_matmul_ex(const float *x, int64_t M, const uint8_t *packed,
+                           const uint16_t *scales, int64_t N, int64_t K, int64_t group,
+                           const float *bias, int relu, float *y, double *bound);
+
 void int4_oracle_matmul(const float *x, int64_t M, const uint8_t *packed,
                         const uint16_t *scales, int64_t N, int64_t K, int64_t group,
                         float *y, double *bound)
 {
-    int64_t G = int4_oracle_num_groups(K, group);
-    int64_t B = int4_oracle_packed_row_bytes(K);
-    for (int64_t m = 0; m < M; ++m) {
-        const float *xrow = x + m * K;
-        for (int64_t n = 0; n < N; ++n) {
-            const uint8_t *prow = packed + n * B;
-            double acc = 0.0, mag = 0.0;
-            for (int64_t gi = 0; gi < G; ++gi) {
-                int64_t k0 = gi * group;
-                int64_t k1 = k0 + group < K ? k0 + group : K;
-                double part = 0.0, part_abs = 0.0;
-                for (int64_t k = k0; k < k1; ++k) {
-                    double p = (double)xrow[k] * (double)nibble_value(prow, k);
-                    part += p;
-                    part_abs += fabs(p);
-                }
-                double sf = (double)int4_oracle_float_from_half(scales[n * G + gi]);
-                acc += sf * part;
-                mag += fabs(sf) * part_abs;
-            }
-            y[m * N + n] = (float)acc;
-            if (bound)
-                bound[m * N + n] = mag;
-        }
-    }
+    int4_oracle_matmul_ex(x, M, packed, scales, N, K, group, NULL, 0, y, bound);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -271,4 +251,56 @@ void int4_oracle_dequantize_half(const uint8_t *packed, const uint16_t *scales,
             float sf = int4_oracle_float_from_half(scales[n * G + k / group]);
             out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k) * sf);
         }
+}
+
+/* ------------------------------------------------------------------------ */
+/* int4_matmul with the engine page's epilogue ("Build a Blockwise INT4     */
+/* Inference Engine", fused GEMM kernel and the Python layer's forward):    */
+/*   y = act(x @ dequantize(W).T + bias), act = identity or ReLU.           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The matmul sum follows the statement's order (per group: x times the
+ * group's integer codes, then the group's scale), accumulated in double.
+ * bias: optional [N] binary32 (NULL: none), added in double; the result is
+ * rounded once to binary32. relu: 0 or 1; ReLU keeps a value greater than
+ * zero and gives +0 otherwise (the engine page's `acc > 0 ? acc : 0`).
+ * bound: optional [M, N] binary64, sum over k of |x[m,k] * q[n,k] * scale|
+ * (the bias is exact and adds nothing to it). int4_oracle_matmul above is
+ * this function with no bias and no activation.
+ */
+void int4_oracle_matmul_ex(const float *x, int64_t M, const uint8_t *packed,
+                           const uint16_t *scales, int64_t N, int64_t K, int64_t group,
+                           const float *bias, int relu, float *y, double *bound)
+{
+    int64_t G = int4_oracle_num_groups(K, group);
+    int64_t B = int4_oracle_packed_row_bytes(K);
+    for (int64_t m = 0; m < M; ++m) {
+        const float *xrow = x + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *prow = packed + n * B;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t gi = 0; gi < G; ++gi) {
+                int64_t k0 = gi * group;
+                int64_t k1 = k0 + group < K ? k0 + group : K;
+                double part = 0.0, part_abs = 0.0;
+                for (int64_t k = k0; k < k1; ++k) {
+                    double p = (double)xrow[k] * (double)nibble_value(prow, k);
+                    part += p;
+                    part_abs += fabs(p);
+                }
+                double sf = (double)int4_oracle_float_from_half(scales[n * G + gi]);
+                acc += sf * part;
+                mag += fabs(sf) * part_abs;
+            }
+            if (bias)
+                acc += (double)bias[n];
+            float v = (float)acc;
+            if (relu)
+                v = v > 0.0f ? v : 0.0f;
+            y[m * N + n] = v;
+            if (bound)
+                bound[m * N + n] = mag;
+        }
+    }
 }

@@ -449,4 +449,44 @@ def pin_dequantize_extremes(lib):
     assert np.isneginf(h[0, 0]) and h[0, 1] == 0
 
 
+# ------------------------------------------------------------------ epilogue
+
+def _mmx(lib, x, p, s, K, g, bias=None, relu=False, bound=False):
+    return oracle.int4_matmul_ex(x, p, s, K, g, bias=bias, relu=relu, with_bound=bound, lib=lib)
+
+
+def pin_epilogue_engine_forward(lib):
+    """The engine page's layer forward, x @ W_dq.T + bias then ReLU, written in
+    NumPy over the brute-force reconstruction (float64, rounded once): equal to
+    the oracle's fused epilogue up to that rounding, on ragged shapes."""
+    rng = np.random.default_rng(31)
+    for (M, N, K, g) in [(4, 64, 256, 128), (3, 48, 301, 128), (5, 9, 31, 3), (2, 17, 129, 64)]:
+        w = rng.normal(size=(N, K)).astype(np.float32)
+        x = rng.normal(size=(M, K)).astype(np.float32)
+        b = rng.normal(size=N).astype(np.float32)
+        p, s, _ = _q(lib, w, g)
+        ref = x.astype(np.float64) @ brute.dequantize(p, s, K, g).T + b.astype(np.float64)
+        y, bnd = _mmx(lib, x, p, s, K, g, bias=b, relu=False, bound=True)
+        assert np.all(np.abs(y - ref) <= 1e-6 * (bnd + np.abs(b)) + 1e-30), (M, N, K, g)
+        yr = _mmx(lib, x, p, s, K, g, bias=b, relu=True)
+        assert np.array_equal(yr, np.where(y > 0, y, np.float32(0))), (M, N, K, g)
+        assert np.all(yr >= 0) and np.array_equal(np.signbit(yr), np.zeros_like(yr, bool))
+
+
+def pin_epilogue_reduces_to_matmul(lib):
+    """No bias and no activation is int4_matmul itself; a zero bias changes
+    nothing; ReLU of a result that is negative everywhere (a large negative
+    bias) is exactly zero."""
+    rng = np.random.default_rng(32)
+    M, N, K, g = 3, 40, 200, 64
+    w = rng.normal(size=(N, K)).astype(np.float32)
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    p, s, _ = _q(lib, w, g)
+    y = _mm(lib, x, p, s, K, g)
+    assert np.array_equal(_mmx(lib, x, p, s, K, g), y)
+    assert np.array_equal(_mmx(lib, x, p, s, K, g, bias=np.zeros(N, np.float32)), y)
+    big = np.full(N, -1e6, np.float32)
+    assert np.all(_mmx(lib, x, p, s, K, g, bias=big, relu=True) == 0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

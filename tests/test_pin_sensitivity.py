@@ -64,6 +64,12 @@ MUTANTS = [
     ("dequantize_half_from_unscaled",
      "out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k) * sf);",
      "out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k));"),
+    ("epilogue_bias_dropped",
+     "            acc += (double)bias[n];", "            acc += 0.0;"),
+    ("epilogue_relu_keeps_negatives",
+     "v = v > 0.0f ? v : 0.0f;", "v = v > 0.0f ? v : v;"),
+    ("epilogue_bias_of_wrong_column",
+     "            acc += (double)bias[n];", "            acc += (double)bias[(n + 1) % N];"),
     ("widen_subnormal_wrong",
      "v = ldexp((double)frac, -24);", "v = ldexp((double)(1024 + frac), -25);"),
 ]
