@@ -33,6 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4dq.s
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 X_F32, X_F16 = 0, 1
+ACT_NONE, ACT_RELU = 0, 1
 OUT_F32, OUT_F16 = 0, 1
 PATHS = {"auto": 0, "generic": 1, "skinny": 2, "tiled": 3, "gemv": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
@@ -46,7 +47,8 @@ SIGNATURES = {
     "int4_unpack": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "int4_dequantize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "int4_matmul": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
-    "int4_matmul_path": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "int4_matmul_ex": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp]),
+    "int4_matmul_path": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp]),
     "int4_matmul_select": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp]),
     "int4_last_error": (ctypes.c_char_p, []),
 }
@@ -174,8 +176,10 @@ def _matmul_args(x, packed, scales, K, group):
 
 
 def int4_matmul_path(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
-                     group: int = 128, path: str = "auto", out: torch.Tensor | None = None):
-    """y [M, N] float32 = x @ dequantize(W).T through a chosen kernel (see PATHS)."""
+                     group: int = 128, path: str = "auto", out: torch.Tensor | None = None,
+                     bias: torch.Tensor | None = None, relu: bool = False):
+    """y [M, N] float32 = act(x @ dequantize(W).T + bias) through a chosen kernel
+    (see PATHS); no bias and no ReLU unless given."""
     M, N, xd = _matmul_args(x, packed, scales, K, group)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
@@ -183,17 +187,26 @@ def int4_matmul_path(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
         _gpu(out, "out", torch.float32)
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out shape {tuple(out.shape)} != {(M, N)}")
+    bptr = None
+    if bias is not None:
+        _gpu(bias, "bias", torch.float32, ndim=1)
+        if bias.shape[0] != N or bias.device != x.device:
+            raise ValueError(f"bias must be [N] = [{N}] on {x.device}")
+        bptr = bias.data_ptr()
     with torch.cuda.device(x.device):
         rc = lib.int4_matmul_path(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), N, K,
-                                  group, out.data_ptr(), PATHS[path], _stream(x))
+                                  group, bptr, ACT_RELU if relu else ACT_NONE, out.data_ptr(),
+                                  PATHS[path], _stream(x))
     _raise(rc, "int4_matmul")
     return out
 
 
 def int4_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
-                group: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
-    """y [M, N] float32 = x @ dequantize(W).T, one group at a time (integer-first)."""
-    return int4_matmul_path(x, packed, scales, K, group, "auto", out)
+                group: int = 128, out: torch.Tensor | None = None, *,
+                bias: torch.Tensor | None = None, relu: bool = False) -> torch.Tensor:
+    """y [M, N] float32 = x @ dequantize(W).T, one group at a time (integer-first);
+    with the engine page's epilogue act(... + bias) when bias or relu is given."""
+    return int4_matmul_path(x, packed, scales, K, group, "auto", out, bias, relu)
 
 
 def matmul_select(x, packed, scales, K, group=128) -> str:

@@ -119,10 +119,13 @@ int int4_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, in
 }
 
 int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
-                     const uint16_t* scales, int64_t N, int64_t K, int64_t group, float* y,
-                     int path, void* stream) {
+                     const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                     const float* bias, int act, float* y, int path, void* stream) {
   int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
   if (rc != INT4DQ_OK) return rc;
+  if (act != INT4DQ_ACT_NONE && act != INT4DQ_ACT_RELU)
+    return fail(INT4DQ_EINVAL, "int4_matmul: unknown activation %d", act);
+  const int4dq::Epilogue ep{bias, act == INT4DQ_ACT_RELU ? 1 : 0};
   if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_GEMV)
     return fail(INT4DQ_EINVAL, "int4_matmul_path: unknown path %d", path);
   if (M == 0) return ok();
@@ -132,23 +135,23 @@ int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packe
     case INT4DQ_PATH_SKINNY: {
       const char* why = int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
-      return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, N, K, group, y, s),
+      return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, N, K, group, y, ep, s),
                         "int4_matmul skinny launch");
     }
     case INT4DQ_PATH_GEMV: {
       const char* why = int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
-      return hip_status(int4dq::launch_matmul_gemv(x, packed, scales, N, K, group, y, s),
+      return hip_status(int4dq::launch_matmul_gemv(x, packed, scales, N, K, group, y, ep, s),
                         "int4_matmul gemv launch");
     }
     case INT4DQ_PATH_TILED: {
       const char* why = int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
-      return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, N, K, group, y, s),
+      return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, N, K, group, y, ep, s),
                         "int4_matmul tiled launch");
     }
     default:
-      return hip_status(int4dq::launch_matmul_generic(x, x_dtype, M, packed, scales, N, K, group, y, s),
+      return hip_status(int4dq::launch_matmul_generic(x, x_dtype, M, packed, scales, N, K, group, y, ep, s),
                         "int4_matmul generic launch");
   }
 }
@@ -156,7 +159,15 @@ int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packe
 int int4_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                 const uint16_t* scales, int64_t N, int64_t K, int64_t group, float* y,
                 void* stream) {
-  return int4_matmul_path(x, x_dtype, M, packed, scales, N, K, group, y, INT4DQ_PATH_AUTO, stream);
+  return int4_matmul_path(x, x_dtype, M, packed, scales, N, K, group, nullptr, INT4DQ_ACT_NONE, y,
+                          INT4DQ_PATH_AUTO, stream);
+}
+
+int int4_matmul_ex(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                   const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                   const float* bias, int act, float* y, void* stream) {
+  return int4_matmul_path(x, x_dtype, M, packed, scales, N, K, group, bias, act, y,
+                          INT4DQ_PATH_AUTO, stream);
 }
 
 int int4_matmul_select(const void* x, int x_dtype, int64_t M, const uint8_t* packed,

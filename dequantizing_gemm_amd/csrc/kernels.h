@@ -8,6 +8,18 @@
 
 namespace int4dq {
 
+// Output step of every matmul kernel (the engine page's fused kernel and
+// layer forward): y = act(v + bias[n]) with act = identity or ReLU; ReLU keeps
+// a value greater than zero and gives +0 otherwise.
+struct Epilogue {
+  const float* bias;   // [N] binary32, or nullptr
+  int relu;            // 0 or 1
+  __device__ __forceinline__ float operator()(float v, int64_t n) const {
+    if (bias) v += bias[n];
+    return relu ? (v > 0.0f ? v : 0.0f) : v;
+  }
+};
+
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
                            uint16_t* scales, hipStream_t stream);
 
@@ -19,24 +31,25 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, int6
 
 hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                                  const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                                 float* y, hipStream_t stream);
+                                 float* y, Epilogue ep, hipStream_t stream);
 
 // nullptr if the kernel takes these arguments, else the reason it does not.
 const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
                                       const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                                float* y, hipStream_t stream);
+                                float* y, Epilogue ep, hipStream_t stream);
 
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
                                     const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
-                              int64_t N, int64_t K, int64_t group, float* y, hipStream_t stream);
+                              int64_t N, int64_t K, int64_t group, float* y, Epilogue ep,
+                              hipStream_t stream);
 
 const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
                                      int64_t K, int64_t group);
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
                                const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                               float* y, hipStream_t stream);
+                               float* y, Epilogue ep, hipStream_t stream);
 
 }  // namespace int4dq

@@ -93,7 +93,7 @@ template <int RW>
 __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int group, int gsh,
-    float* __restrict__ y) {
+    float* __restrict__ y, Epilogue ep) {
   __shared__ float red[kGemvMaxChunks][RW];
   const int lane = threadIdx.x & 63;
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
   if ((int)threadIdx.x < RW && n0 + (int)threadIdx.x < N) {
     float sum = 0.0f;
     for (int cc = 0; cc < nchunks; ++cc) sum += red[cc][threadIdx.x];
-    y[n0 + threadIdx.x] = sum;
+    y[n0 + threadIdx.x] = ep(sum, n0 + threadIdx.x);
   }
 }
 
@@ -198,7 +198,7 @@ template <int CM, int GS, int W>
 __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int group, int gsh,
-    float* __restrict__ y) {
+    float* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
   constexpr int NT = 64 * W, ROWS = 4 * W;     // threads, rows per block
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   // Sum the 16 slices (lanes 4b+j, b = 0..15) of each of the 4 rows.
 #pragma unroll
   for (int off = 4; off < 64; off <<= 1) acc += __shfl_xor(acc, off);
-  if (b == 0 && n0 + 4 * wave + j < N) y[n0 + 4 * wave + j] = acc;
+  if (b == 0 && n0 + 4 * wave + j < N) y[n0 + 4 * wave + j] = ep(acc, n0 + 4 * wave + j);
 }
 
 // ---------------------------------------------------------------------------
@@ -327,7 +327,7 @@ template <int C>
 __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int group,
-    float* __restrict__ y) {
+    float* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
   constexpr int P = 2;                         // rows in flight per wavefront
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
     k0 += P;
   } while (k0 < R);
   wait_vmcnt_gemv<0>();
-  if (lane < R) y[r0 + lane * TW] = yv;
+  if (lane < R) y[r0 + lane * TW] = ep(yv, r0 + lane * TW);
 }
 
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
@@ -460,7 +460,8 @@ const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
 }
 
 hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
-                              int64_t N, int64_t K, int64_t group, float* y, hipStream_t stream) {
+                              int64_t N, int64_t K, int64_t group, float* y, Epilogue ep,
+                              hipStream_t stream) {
   const int G = (int)((K + group - 1) / group);
   int gsh = 0;                                                 // log2(group / 32), or -1
   while ((32ll << gsh) < group) ++gsh;
@@ -475,7 +476,7 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
     const dim3 grid((unsigned)blocks), block(64 * kRowWaves);
 #define INT4DQ_GEMV_ROWS(CC)                                                                     \
   hipLaunchKernelGGL(matmul_gemv_rows_kernel<CC>, grid, block, 0, stream, xh0, packed, scales,  \
-                     (int)N, (int)K, G, (int)group, y)
+                     (int)N, (int)K, G, (int)group, y, ep)
     switch (chunks) {
       case 1: INT4DQ_GEMV_ROWS(1); break;
       case 2: INT4DQ_GEMV_ROWS(2); break;
@@ -498,7 +499,7 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
     const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<CMV, 0, W> : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, W> \
                     : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, W> : matmul_gemv_mfma_kernel<CMV, 3, W>;       \
     hipLaunchKernelGGL(kern, g16, b256, 0, stream, xh0, packed, scales, (int)N, (int)K, G,     \
-                       (int)group, gsh, y);                                                     \
+                       (int)group, gsh, y, ep);                                                     \
   } while (0)
     if (cols <= 2) INT4DQ_GEMV_MFMA(2);
     else if (cols <= 4) INT4DQ_GEMV_MFMA(4);
@@ -519,13 +520,13 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
   const _Float16* xh = static_cast<const _Float16*>(x);
   const dim3 grid((unsigned)blocks), block(64 * chunks);
   if (rw == 8)
-    hipLaunchKernelGGL(matmul_gemv_kernel<8>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y);
+    hipLaunchKernelGGL(matmul_gemv_kernel<8>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
   else if (rw == 4)
-    hipLaunchKernelGGL(matmul_gemv_kernel<4>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y);
+    hipLaunchKernelGGL(matmul_gemv_kernel<4>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
   else if (rw == 2)
-    hipLaunchKernelGGL(matmul_gemv_kernel<2>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y);
+    hipLaunchKernelGGL(matmul_gemv_kernel<2>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
   else
-    hipLaunchKernelGGL(matmul_gemv_kernel<1>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y);
+    hipLaunchKernelGGL(matmul_gemv_kernel<1>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ template <typename XT>
 __global__ __launch_bounds__(256) void matmul_generic_kernel(
     const XT* __restrict__ x, int64_t M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int64_t N, int64_t K, int64_t group, int64_t G,
-    float* __restrict__ y) {
+    float* __restrict__ y, Epilogue ep) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t out = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (out >= M * N) return;                        // whole wavefronts only
@@ -47,21 +47,21 @@ __global__ __launch_bounds__(256) void matmul_generic_kernel(
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) y[m * N + n] = acc;
+  if (lane == 0) y[m * N + n] = ep(acc, n);
 }
 
 hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                                  const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                                 float* y, hipStream_t stream) {
+                                 float* y, Epilogue ep, hipStream_t stream) {
   const int64_t G = (K + group - 1) / group;
   const int64_t outs = M * N;
   const dim3 grid((unsigned)((outs + 3) / 4)), block(256);
   if (x_dtype == 0)
     hipLaunchKernelGGL(matmul_generic_kernel<float>, grid, block, 0, stream,
-                       static_cast<const float*>(x), M, packed, scales, N, K, group, G, y);
+                       static_cast<const float*>(x), M, packed, scales, N, K, group, G, y, ep);
   else
     hipLaunchKernelGGL(matmul_generic_kernel<_Float16>, grid, block, 0, stream,
-                       static_cast<const _Float16*>(x), M, packed, scales, N, K, group, G, y);
+                       static_cast<const _Float16*>(x), M, packed, scales, N, K, group, G, y, ep);
   return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ template <int KB, int WAVES, int U, int MR>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int kb_shift,
-    float* __restrict__ y) {
+    float* __restrict__ y, Epilogue ep) {
   typedef typename WLoad<KB>::T wvec_t;
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
   constexpr int XB = U < 4 ? U : 4;           // K-blocks per batch of direct x loads
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) s += red[w * 256 + src];
-    if (n0 + nn < N) y[(int64_t)m * N + n0 + nn] = s;
+    if (n0 + nn < N) y[(int64_t)m * N + n0 + nn] = ep(s, n0 + nn);
   }
 }
 
@@ -246,52 +246,52 @@ constexpr size_t kSkinnyLdsMax = 64 * 1024;
 
 template <int KB, int WAVES, int U, int MR>
 static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      int N, int K, int G, int kbs, float* y, hipStream_t stream) {
+                      int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
   hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR>), dim3((unsigned)((N + 15) / 16)),
                      dim3(WAVES * 64), skinny_lds(WAVES, U, KB, MR), stream, x, M, packed, scales,
-                     N, K, G, kbs, y);
+                     N, K, G, kbs, y, ep);
 }
 
 template <int KB, int WAVES, int U>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                       int N, int K, int G, int kbs, float* y, hipStream_t stream) {
+                       int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
   const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
   if (M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax)
-    launch_mr<KB, WAVES, U, 0>(x, M, packed, scales, N, K, G, kbs, y, stream);
+    launch_mr<KB, WAVES, U, 0>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
   else if (MR == 1)
-    launch_mr<KB, WAVES, U, 1>(x, M, packed, scales, N, K, G, kbs, y, stream);
+    launch_mr<KB, WAVES, U, 1>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
   else if (MR == 2)
-    launch_mr<KB, WAVES, U, 2>(x, M, packed, scales, N, K, G, kbs, y, stream);
+    launch_mr<KB, WAVES, U, 2>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
   else
-    launch_mr<KB, WAVES, U, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
+    launch_mr<KB, WAVES, U, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
 }
 
 // Waves per block and K-blocks per wave for nkb K-blocks: the fewest waves
 // (<= 16) that cover K with at most 4 K-blocks each, else 16 waves with up to 8.
 template <int KB>
 static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      int N, int K, int G, int kbs, float* y, hipStream_t stream) {
+                      int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
   const int nkb = K / KB;
-  if (nkb <= 4 * 2) launch_one<KB, 4, 2>(x, M, packed, scales, N, K, G, kbs, y, stream);
-  else if (nkb <= 4 * 4) launch_one<KB, 4, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
-  else if (nkb <= 8 * 4) launch_one<KB, 8, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
-  else if (nkb <= 16 * 4) launch_one<KB, 16, 4>(x, M, packed, scales, N, K, G, kbs, y, stream);
-  else if (nkb <= 16 * 6) launch_one<KB, 16, 6>(x, M, packed, scales, N, K, G, kbs, y, stream);
-  else launch_one<KB, 16, 8>(x, M, packed, scales, N, K, G, kbs, y, stream);
+  if (nkb <= 4 * 2) launch_one<KB, 4, 2>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 4 * 4) launch_one<KB, 4, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 8 * 4) launch_one<KB, 8, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 16 * 4) launch_one<KB, 16, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 16 * 6) launch_one<KB, 16, 6>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+  else launch_one<KB, 16, 8>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
 }
 
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                                float* y, hipStream_t stream) {
+                                float* y, Epilogue ep, hipStream_t stream) {
   const int KB = skinny_kb(group);
   const int G = (int)((K + group - 1) / group);
   int kbs = 0;
   while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);
   switch (KB) {
-    case 128: launch_kb<128>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, stream); break;
-    case 64: launch_kb<64>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, stream); break;
-    default: launch_kb<32>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, stream); break;
+    case 128: launch_kb<128>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, ep, stream); break;
+    case 64: launch_kb<64>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, ep, stream); break;
+    default: launch_kb<32>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, ep, stream); break;
   }
   return hipGetLastError();
 }

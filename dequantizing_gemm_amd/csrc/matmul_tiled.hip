@@ -85,7 +85,7 @@ template <int BK, int SPG, int TM>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int gshift,
-    float* __restrict__ y) {
+    float* __restrict__ y, Epilogue ep) {
   constexpr int BM = 64 * TM, BN = kTileN, WN = 2, NW = 4;
   constexpr int WMT = 32 * TM, WNT = 64, TN = 2;       // wave tile; TM x TN 32x32 MFMA tiles
   constexpr int KS = BK / 16;                  // MFMA k-steps per sub-step
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (m < M && n < N) y[(int64_t)m * N + n] = acc[a][b][i] * srun[b];
+        if (m < M && n < N) y[(int64_t)m * N + n] = ep(acc[a][b][i] * srun[b], n);
       }
   }
 }
@@ -438,7 +438,7 @@ const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* 
 
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
                                const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                               float* y, hipStream_t stream) {
+                               float* y, Epilogue ep, hipStream_t stream) {
   const int BK = tiled_bk(group);
   const int G = (int)((K + group - 1) / group);
   if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
@@ -459,7 +459,7 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   const auto kernel = TM == 4 ? INT4DQ_TILED_PICK(4) : TM == 2 ? INT4DQ_TILED_PICK(2) : INT4DQ_TILED_PICK(1);
 #undef INT4DQ_TILED_PICK
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     static_cast<const _Float16*>(x), (int)M, packed, scales, (int)N, (int)K, G, gs, y);
+                     static_cast<const _Float16*>(x), (int)M, packed, scales, (int)N, (int)K, G, gs, y, ep);
   return hipGetLastError();
 }
 

@@ -54,6 +54,10 @@ extern "C" {
 #define INT4DQ_OUT_F32 0       /* IEEE binary32 */
 #define INT4DQ_OUT_F16 1       /* IEEE binary16 */
 
+/* Output activation of int4_matmul_ex / int4_matmul_path. */
+#define INT4DQ_ACT_NONE 0      /* y = v */
+#define INT4DQ_ACT_RELU 1      /* y = v > 0 ? v : +0 */
+
 /* Kernel selection for int4_matmul_path (int4_matmul always uses AUTO). */
 #define INT4DQ_PATH_AUTO    0  /* choose by M, dtype and alignment */
 #define INT4DQ_PATH_GENERIC 1  /* VALU kernel, any shape, any group, fp32 or fp16 x */
@@ -140,15 +144,30 @@ int int4_matmul(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
                 float *y, void *stream);
 
 /*
- * int4_matmul with an explicit kernel choice (INT4DQ_PATH_*), for testing
+ * int4_matmul with the output step of the engine page's fused kernel and
+ * layer forward ("Build a Blockwise INT4 Inference Engine"):
+ *   y = act(x @ dequantize(W).T + bias)
+ *   bias in : [N] binary32 added to every row, or NULL for none.
+ *   act     : INT4DQ_ACT_NONE or INT4DQ_ACT_RELU (v > 0 ? v : +0).
+ * The matmul part is int4_matmul's; the bias is one binary32 add after it.
+ * Each output is within 2e-3 * sum_k |x[m,k] * q[n,k] * scale| + 2^-22 * |y|
+ * of act applied to the exact sum plus bias rounded once.
+ * Errors: those of int4_matmul, and EINVAL for an unknown act.
+ */
+int int4_matmul_ex(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                   const uint16_t *scales, int64_t N, int64_t K, int64_t group,
+                   const float *bias, int act, float *y, void *stream);
+
+/*
+ * int4_matmul_ex with an explicit kernel choice (INT4DQ_PATH_*), for testing
  * one kernel against another on the same shapes. Same arguments, results
- * and errors as int4_matmul, plus EUNSUPPORTED when the forced kernel cannot
- * take this dtype, shape, group or alignment (the reason is in
+ * and errors as int4_matmul_ex, plus EUNSUPPORTED when the forced kernel
+ * cannot take this dtype, shape, group or alignment (the reason is in
  * int4_last_error()).
  */
 int int4_matmul_path(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
                      const uint16_t *scales, int64_t N, int64_t K, int64_t group,
-                     float *y, int path, void *stream);
+                     const float *bias, int act, float *y, int path, void *stream);
 
 /*
  * Kernel that int4_matmul would run for these arguments (an INT4DQ_PATH_*

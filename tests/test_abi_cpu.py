@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == sorted(["int4_num_groups", "int4_packed_bytes", "int4_quantize", "int4_dequantize",
-                                  "int4_unpack", "int4_matmul", "int4_matmul_path",
+                                  "int4_unpack", "int4_matmul", "int4_matmul_ex", "int4_matmul_path",
                                   "int4_matmul_select", "int4_last_error"])
 
 
@@ -124,7 +124,11 @@ def test_matmul_m0_is_noop_and_bad_path():
     dq = _lib()
     # M = 0 returns OK without touching the GPU (no pointer is dereferenced)
     assert dq.lib.int4_matmul(None, 1, 0, FAKE, FAKE, 16, 256, 128, None, None) == dq.OK
-    assert dq.lib.int4_matmul_path(FAKE, 1, 4, FAKE, FAKE, 16, 256, 128, FAKE, 9, None) == dq.EINVAL
+    assert dq.lib.int4_matmul_path(FAKE, 1, 4, FAKE, FAKE, 16, 256, 128, None, 0, FAKE, 9, None) == dq.EINVAL
+    # an unknown activation is rejected before anything is enqueued
+    assert dq.lib.int4_matmul_ex(FAKE, 1, 4, FAKE, FAKE, 16, 256, 128, None, 5, FAKE, None) == dq.EINVAL
+    assert "activation" in dq.lib.int4_last_error().decode()
+    assert dq.lib.int4_matmul_ex(None, 1, 0, FAKE, FAKE, 16, 256, 128, FAKE, 1, None, None) == dq.OK
 
 
 def test_kernel_selection_rules():

@@ -346,6 +346,37 @@ def test_matmul_gemv_rows_one_hot_exact(dq):
         assert np.array_equal(y[0].astype(np.float64), col), f"k={k}"
 
 
+@pytest.mark.parametrize("N,K,g,M,path", [(300, 1024, 128, 1, "gemv"), (200, 768, 32, 1, "gemv"),
+                                          (12300, 8224, 32, 1, "gemv"), (77, 4096, 96, 1, "gemv"),
+                                          (200, 768, 64, 5, "skinny"), (48, 4096, 128, 16, "skinny"),
+                                          (300, 1024, 128, 130, "tiled"), (129, 256, 32, 600, "tiled"),
+                                          (640, 2048, 128, 520, "tiled"), (10880, 256, 64, 300, "tiled"),
+                                          (4096, 256, 128, 1600, "tiled"), (40, 1000, 7, 6, "generic")])
+def test_matmul_epilogue(dq, N, K, g, M, path):
+    """The engine page's epilogue act(x @ w_hat.T + bias) through every kernel
+    (all three M = 1 variants, the 64/128/256-row tiles, the generic kernel):
+    within 2e-3 * bound + 2^-22 * |y| of the oracle, ReLU giving +0 for every
+    non-positive value."""
+    say(f"case: epilogue {path} N={N} K={K} g={g} M={M}")
+    rng = np.random.default_rng(N + M)
+    w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
+    x = rng.normal(size=(M, K)).astype(np.float16 if path != "generic" else np.float32)
+    b = rng.normal(0, 0.5, size=N).astype(np.float32)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    pd, sd, xd, bd = dev(pr), dev(sr), dev(x), dev(b)
+    rows = sample_rows_cols(M, N, K)[0] if M > 64 else np.arange(M)
+    for relu in (False, True):
+        y = host(dq.int4_matmul_path(xd, pd, sd, K, g, path, bias=bd, relu=relu))[rows]
+        ref, bound = oracle.int4_matmul_ex(x[rows], pr, sr, K, g, bias=b, relu=relu, with_bound=True)
+        err = np.abs(y.astype(np.float64) - ref)
+        ok = err <= TOL * bound + 2.0 ** -22 * np.abs(ref) + 1e-30
+        assert ok.all(), f"{path} relu={relu}: {int((~ok).sum())} outputs out of tolerance"
+        if relu:
+            assert np.all(y >= 0) and not np.signbit(y).any()
+    y0 = host(dq.int4_matmul_path(xd, pd, sd, K, g, path))
+    assert np.array_equal(host(dq.int4_matmul_path(xd, pd, sd, K, g, path, bias=torch.zeros_like(bd))), y0)
+
+
 def test_matmul_fp32_x(dq):
     say("case: binary32 activations, c1/c2 shapes and a [40,1000] g=7 matrix")
     for (N, K, g, M) in [(64, 256, 128, 4), (48, 301, 128, 3), (40, 1000, 7, 6)]:
