@@ -70,32 +70,41 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 // natural order (codes_to_half_natural, 12 ops per 8 codes). Staging moves one
 // copy of x per wave instead of one 16-byte load per lane and MFMA, and is used
 // for small M where the slices fit LDS.
-template <int KB, int WAVES, int U, int MR>
+// RG > 1 (MR == 0 only): the block owns RG groups of 16 weight rows, and each
+// activation fragment a lane loads serves all RG of them, which divides the
+// activation traffic per weight byte by RG (x is re-read by every block).
+template <int KB, int WAVES, int U, int MR, int RG>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, int N, int K, int G, int kb_shift,
     float* __restrict__ y, Epilogue ep) {
   typedef typename WLoad<KB>::T wvec_t;
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
-  constexpr int XB = U < 4 ? U : 4;           // K-blocks per batch of direct x loads
+  constexpr int XB = RG > 1 ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
+  static_assert(MR == 0 || RG == 1, "row groups with direct x loads only");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float* red = reinterpret_cast<float*>(lds);                  // [WAVES][64][4]
+  float* red = reinterpret_cast<float*>(lds);                  // [WAVES][RG][64][4]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 15, h = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int nrow = (n0 + col < N) ? n0 + col : N - 1;       // tail rows: read, discard
+  const int n0 = blockIdx.x * 16 * RG;
   const int xrow = col < M ? col : M - 1;                    // rows >= M: discarded
-  const uint8_t* prow = packed + (int64_t)nrow * (K >> 1) + h * (KB / 8);
-  const uint16_t* srow = scales + (int64_t)nrow * G;
+  const uint8_t* prow[RG];
+  const uint16_t* srow[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int nrow = (n0 + 16 * r + col < N) ? n0 + 16 * r + col : N - 1;   // tail rows: read, discard
+    prow[r] = packed + (int64_t)nrow * (K >> 1) + h * (KB / 8);
+    srow[r] = scales + (int64_t)nrow * G;
+  }
   const int nkb = K / KB;
 
   // Weight and scale loads of the wave's share, K-block by K-block. They are
   // issued after the (smaller) x staging loads, so that each K-block's
   // compute waits only for its own weights (loads return in order).
-  wvec_t wv[U];
-  uint32_t sraw[U];
+  wvec_t wv[RG][U];
+  uint32_t sraw[RG][U];
   // Straight-line, unconditional loads: a K-block index past the end is
   // clamped to the wave's last valid one (the value is loaded and ignored), so
   // no branch splits the sequence and no use is scheduled between the loads.
@@ -103,18 +112,24 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   // and with the weights issued after them that wait does not cover the weights.
   auto load_w = [&]() {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
-      sraw[u] = srow[j >> kb_shift];
-    }
+    for (int r = 0; r < RG; ++r)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
-      wv[u] = __builtin_nontemporal_load(reinterpret_cast<const wvec_t*>(prow + j * (KB / 2)));
-    }
+      for (int u = 0; u < U; ++u) {
+        const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
+        sraw[r][u] = srow[r][j >> kb_shift];
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
+        wv[r][u] = __builtin_nontemporal_load(reinterpret_cast<const wvec_t*>(prow[r] + j * (KB / 2)));
+      }
   };
 
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t acc[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (MR > 0) {
     // Wave-private region: [MR][U][KB] halves, spread order within each 8.
     _Float16* xw = reinterpret_cast<_Float16*>(lds + WAVES * 64 * 4 * sizeof(float)) +
@@ -159,10 +174,10 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
           half2_t hw[4];
-          codes_to_half_spread(word_at<KB>(wv[u], i), hw);
+          codes_to_half_spread(word_at<KB>(wv[0][u], i), hw);
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], as_half8(hw), d, 0, 0, 0);
         }
-        acc += half_bits_to_float((uint16_t)sraw[u]) * d;
+        acc[0] += half_bits_to_float((uint16_t)sraw[0][u]) * d;
       }
     }
   } else {
@@ -186,29 +201,36 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
       for (int v = 0; v < XB; ++v) {
         const int u = b + v;
         if (u < U && wave + u * WAVES < nkb) {
-          float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int i = 0; i < DW; ++i) {
-            half2_t hw[4];
-            codes_to_half_natural(word_at<KB>(wv[u], i), hw);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[v][i], as_half8(hw), d, 0, 0, 0);
+          for (int r = 0; r < RG; ++r) {
+            float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < DW; ++i) {
+              half2_t hw[4];
+              codes_to_half_natural(word_at<KB>(wv[r][u], i), hw);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[v][i], as_half8(hw), d, 0, 0, 0);
+            }
+            acc[r] += half_bits_to_float((uint16_t)sraw[r][u]) * d;
           }
-          acc += half_bits_to_float((uint16_t)sraw[u]) * d;
         }
       }
     }
   }
 
-  // Sum the waves' 16x16 partial tiles. Lane l holds rows 4*(l/16) + r of column l%16.
-  *reinterpret_cast<float4_t*>(red + (wave * 64 + lane) * 4) = acc;
+  // Sum the waves' 16x16 partial tiles. Lane l holds rows 4*(l/16) + i of column l%16.
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+    *reinterpret_cast<float4_t*>(red + ((wave * RG + r) * 64 + lane) * 4) = acc[r];
   __syncthreads();
-  if (tid < 16 * M) {
-    const int m = tid >> 4, nn = tid & 15;
+  for (int t = tid; t < 16 * M * RG; t += WAVES * 64) {
+    const int r = t / (16 * M), rem = t - r * 16 * M;
+    const int m = rem >> 4, nn = rem & 15;
     const int src = ((m >> 2) * 16 + nn) * 4 + (m & 3);
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s += red[w * 256 + src];
-    if (n0 + nn < N) y[(int64_t)m * N + n0 + nn] = ep(s, n0 + nn);
+    for (int w = 0; w < WAVES; ++w) s += red[(w * RG + r) * 256 + src];
+    const int n = n0 + 16 * r + nn;
+    if (n < N) y[(int64_t)m * N + n] = ep(s, n);
   }
 }
 
@@ -239,16 +261,16 @@ const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
 
 // Bytes of LDS a launch uses: the reduction buffer, plus the wave-private x
 // slices of MR rows when they are staged.
-static size_t skinny_lds(int waves, int U, int KB, int MR) {
-  return (size_t)waves * 64 * 4 * sizeof(float) + (size_t)waves * MR * U * KB * 2;
+static size_t skinny_lds(int waves, int U, int KB, int MR, int RG = 1) {
+  return (size_t)waves * RG * 64 * 4 * sizeof(float) + (size_t)waves * MR * U * KB * 2;
 }
 constexpr size_t kSkinnyLdsMax = 64 * 1024;
 
-template <int KB, int WAVES, int U, int MR>
+template <int KB, int WAVES, int U, int MR, int RG = 1>
 static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                       int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
-  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR>), dim3((unsigned)((N + 15) / 16)),
-                     dim3(WAVES * 64), skinny_lds(WAVES, U, KB, MR), stream, x, M, packed, scales,
+  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG>), dim3((unsigned)((N + 16 * RG - 1) / (16 * RG))),
+                     dim3(WAVES * 64), skinny_lds(WAVES, U, KB, MR, RG), stream, x, M, packed, scales,
                      N, K, G, kbs, y, ep);
 }
 
@@ -256,6 +278,23 @@ template <int KB, int WAVES, int U>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                        int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
   const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
+  // Direct x loads: as many row groups per block as keep about one block per
+  // CU (x is re-read by every block, so fewer, wider blocks move less of it).
+  // (Only where the weight registers of RG groups fit without spilling: 16
+  // waves per block leave 128 VGPRs per lane.)
+  constexpr bool rg4 = WAVES <= 8, rg2 = WAVES <= 8 || U <= 6;
+  if constexpr (rg4) {
+    if (M > 4 && N >= 256 * 16 * 4) {
+      launch_mr<KB, WAVES, U, 0, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+      return;
+    }
+  }
+  if constexpr (rg2) {
+    if (M > 4 && N >= 256 * 16 * 2) {
+      launch_mr<KB, WAVES, U, 0, 2>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+      return;
+    }
+  }
   if (M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax)
     launch_mr<KB, WAVES, U, 0>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
   else if (MR == 1)

@@ -278,7 +278,8 @@ def test_matmul_configs(dq, key, case, M):
 
 @pytest.mark.parametrize("N,K,g,M", [(200, 768, 64, 1), (200, 768, 32, 5), (48, 4096, 128, 16),
                                      (136, 1024, 256, 3), (50, 512, 128, 200), (300, 1024, 128, 130),
-                                     (129, 256, 32, 257), (64, 2048, 64, 100)])
+                                     (129, 256, 32, 257), (64, 2048, 64, 100),
+                                     (16400, 2048, 128, 7), (8200, 1024, 64, 9), (9000, 8192, 128, 16)])
 def test_matmul_kernels_agree(dq, N, K, g, M):
     """Every kernel that takes a shape matches the oracle on it (ragged M and N tails)."""
     w = np.random.default_rng(N + K).normal(0, 0.02, size=(N, K)).astype(np.float32)
