@@ -65,11 +65,13 @@ def _declare(lib):
     lib.int4_oracle_unpack.restype = None
     lib.int4_oracle_matmul.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp, vp]
     lib.int4_oracle_matmul.restype = None
-    lib.int4_oracle_matmul_ex.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp, ctypes.c_int, vp, vp]
+    lib.int4_oracle_matmul_ex.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, vp, vp]
     lib.int4_oracle_matmul_ex.restype = None
-    lib.int4_oracle_dequantize.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.int4_oracle_quantize_affine.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    lib.int4_oracle_quantize_affine.restype = None
+    lib.int4_oracle_dequantize.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.int4_oracle_dequantize.restype = None
-    lib.int4_oracle_dequantize_half.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.int4_oracle_dequantize_half.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.int4_oracle_dequantize_half.restype = None
     return lib
 
@@ -88,6 +90,28 @@ def quantize_int4(w: np.ndarray, group: int = 128, lib=None):
     scales = np.empty((N, G), dtype=np.uint16)
     lib.int4_oracle_quantize(_ptr(w), N, K, group, _ptr(packed), _ptr(scales))
     return packed, scales.view(np.float16), K
+
+
+def quantize_int4_affine(w: np.ndarray, group: int = 128, lib=None):
+    """w [N, K] float32 -> (packed uint8 [N, ceil(K/2)] unsigned codes,
+    scales float16 [N, G], zero points uint8 [N, G], K)."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    G = (K + group - 1) // group
+    packed = np.empty((N, (K + 1) // 2), dtype=np.uint8)
+    scales = np.empty((N, G), dtype=np.uint16)
+    zeros = np.empty((N, G), dtype=np.uint8)
+    lib.int4_oracle_quantize_affine(_ptr(w), N, K, group, _ptr(packed), _ptr(scales), _ptr(zeros))
+    return packed, scales.view(np.float16), zeros, K
+
+
+def _zeros_arg(zeros, N, K, group):
+    if zeros is None:
+        return None, None
+    z = np.ascontiguousarray(zeros, dtype=np.uint8)
+    assert z.shape == (N, (K + group - 1) // group)
+    return z, _ptr(z)
 
 
 def unpack_int4(packed: np.ndarray, K: int, lib=None) -> np.ndarray:
@@ -125,9 +149,10 @@ def int4_matmul(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, K: int,
 
 def int4_matmul_ex(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, K: int,
                    group: int = 128, bias: np.ndarray | None = None, relu: bool = False,
-                   with_bound: bool = False, lib=None):
+                   with_bound: bool = False, zeros: np.ndarray | None = None, lib=None):
     """y [M, N] float32 = act(x @ dequantize(W).T + bias): the matmul sum and the
-    bias in double, rounded once, then ReLU (v > 0 ? v : +0) if asked."""
+    bias in double, rounded once, then ReLU (v > 0 ? v : +0) if asked. With
+    ``zeros`` the codes are affine (integer weight = code - zero point)."""
     lib = lib or load()
     x = np.ascontiguousarray(np.asarray(x).astype(np.float32))
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
@@ -140,29 +165,32 @@ def int4_matmul_ex(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, K: int
     assert b is None or b.shape == (N,)
     y = np.empty((M, N), dtype=np.float32)
     bound = np.empty((M, N), dtype=np.float64) if with_bound else None
-    lib.int4_oracle_matmul_ex(_ptr(x), M, _ptr(packed), _ptr(s16), N, K, group,
+    z, zp = _zeros_arg(zeros, N, K, group)
+    lib.int4_oracle_matmul_ex(_ptr(x), M, _ptr(packed), _ptr(s16), zp, N, K, group,
                               _ptr(b) if b is not None else None, int(bool(relu)), _ptr(y),
                               _ptr(bound) if with_bound else None)
     return (y, bound) if with_bound else y
 
 
 def dequantize_int4(packed: np.ndarray, scales: np.ndarray, K: int, group: int = 128,
-                    dtype=np.float32, lib=None) -> np.ndarray:
+                    dtype=np.float32, zeros: np.ndarray | None = None, lib=None) -> np.ndarray:
     """w_hat [N, K] = q * scale, as float32 (exact) or float16 (the exact
-    product rounded to nearest even, by the oracle's own binary16 rounding)."""
+    product rounded to nearest even, by the oracle's own binary16 rounding).
+    With ``zeros`` the codes are affine: w_hat = (code - zero point) * scale."""
     lib = lib or load()
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     s16 = np.ascontiguousarray(np.asarray(scales).view(np.uint16))
     N = packed.shape[0]
     assert packed.shape[1] == (K + 1) // 2
     assert s16.shape == (N, (K + group - 1) // group)
+    z, zp = _zeros_arg(zeros, N, K, group)
     if np.dtype(dtype) == np.float32:
         out = np.empty((N, K), dtype=np.float32)
-        lib.int4_oracle_dequantize(_ptr(packed), _ptr(s16), N, K, group, _ptr(out))
+        lib.int4_oracle_dequantize(_ptr(packed), _ptr(s16), zp, N, K, group, _ptr(out))
         return out
     if np.dtype(dtype) == np.float16:
         out = np.empty((N, K), dtype=np.uint16)
-        lib.int4_oracle_dequantize_half(_ptr(packed), _ptr(s16), N, K, group, _ptr(out))
+        lib.int4_oracle_dequantize_half(_ptr(packed), _ptr(s16), zp, N, K, group, _ptr(out))
         return out.view(np.float16)
     raise ValueError(f"dtype {dtype}: float32 or float16")
 

@@ -28,6 +28,11 @@
  *     integer weights first, then that group's scale; accumulated in double
  *     and rounded once to binary32.
  *
+ * Also here, each with its own source named where it is defined: the
+ * dequantization w_hat = q * scale, the layer epilogue act(y + bias), and the
+ * affine (zero-point) variant of the codes from "Build a Blockwise INT4
+ * Inference Engine", step 2.
+ *
  * Build: cc -O2 -std=c99 -fno-fast-math -ffp-contract=off -shared -fPIC.
  * No SIMD intrinsics, no threads, no blocking or reordering of the loops
  * beyond what the definition states.
@@ -175,13 +180,97 @@ void int4_oracle_quantize(const float *w, int64_t N, int64_t K, int64_t group,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Affine (asymmetric) variant ("Build a Blockwise INT4 Inference Engine",  */
+/* step 2: per-group scale and zero point, q = round(w / scale + zp)        */
+/* clipped to [0, 15]; "Quantizing a Language Model From Scratch", affine   */
+/* quantization: S = (max - min) / 15, w' = S (q - Z)).                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * Readings, where the engine page's listing leaves them open or goes wrong:
+ *   - the range is [min(lo, 0), max(hi, 0)] over the group, so that zero is
+ *     always inside it and exact (the lmquant page's point about Z); for the
+ *     usual group that straddles zero this is the page's min and max;
+ *   - scale = (hi - lo) / 15 in binary32, stored as binary16 like the
+ *     symmetric scales; every later step uses the stored scale widened;
+ *   - zp = clip(round(-lo / scale), 0, 15) with a binary32 division and ties
+ *     to even; stored as one byte per group;
+ *   - q = clip(round(w / scale + zp), 0, 15): w / scale is a binary32
+ *     division, zp is added exactly and the sum rounded half to even (the page
+ *     adds an integer zero point to a float32 quotient in NumPy, which widens
+ *     the sum to float64);
+ *   - a group whose binary16 scale is zero gets zp = 0 and codes 0.
+ * Codes are unsigned nibbles in the same layout as the symmetric codes.
+ */
+static int quantize_one_affine(float w, float sf, int zp)
+{
+    if (sf == 0.0f)
+        return 0;
+    float t = w / sf;                           /* binary32 division */
+    double r = rint((double)t + (double)zp);    /* exact sum, half to even */
+    if (r < 0.0) r = 0.0;
+    if (r > 15.0) r = 15.0;
+    return (int)r;
+}
+
+void int4_oracle_quantize_affine(const float *w, int64_t N, int64_t K, int64_t group,
+                                 uint8_t *packed, uint16_t *scales, uint8_t *zeros)
+{
+    int64_t G = int4_oracle_num_groups(K, group);
+    int64_t B = int4_oracle_packed_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n) {
+        const float *row = w + n * K;
+        uint8_t *prow = packed + n * B;
+        memset(prow, 0, (size_t)B);
+        for (int64_t gi = 0; gi < G; ++gi) {
+            int64_t k0 = gi * group;
+            int64_t k1 = k0 + group < K ? k0 + group : K;
+            float lo = 0.0f, hi = 0.0f;             /* the range includes zero */
+            for (int64_t k = k0; k < k1; ++k) {
+                if (row[k] < lo) lo = row[k];
+                if (row[k] > hi) hi = row[k];
+            }
+            float s32 = (hi - lo) / 15.0f;
+            uint16_t sh = int4_oracle_half_from_float(s32);
+            scales[n * G + gi] = sh;
+            float sf = int4_oracle_float_from_half(sh);
+            int zp = 0;
+            if (sf != 0.0f) {
+                float z = rintf(-lo / sf);
+                zp = z < 0.0f ? 0 : (z > 15.0f ? 15 : (int)z);
+            }
+            zeros[n * G + gi] = (uint8_t)zp;
+            for (int64_t k = k0; k < k1; ++k) {
+                uint8_t nib = (uint8_t)quantize_one_affine(row[k], sf, zp);
+                prow[k / 2] |= (uint8_t)(nib << (4 * (int)(k & 1)));  /* even: low nibble */
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* unpack_int4 (drill page, statement): int8 [N, K], sign-extended.         */
 /* ------------------------------------------------------------------------ */
 
+/* The 4-bit code of element k of a packed row (even k: low nibble). */
+static int raw_nibble(const uint8_t *prow, int64_t k)
+{
+    return (prow[k / 2] >> (4 * (int)(k % 2))) & 0xF;
+}
+
 static int nibble_value(const uint8_t *prow, int64_t k)
 {
-    int v = (prow[k / 2] >> (4 * (int)(k % 2))) & 0xF;
+    int v = raw_nibble(prow, k);
     return v >= 8 ? v - 16 : v;                 /* sign extension of a 4-bit code */
+}
+
+/* Integer weight of element k of a row: the sign-extended code, or with zero
+ * points (zp: that row's array of them, NULL for symmetric codes) the
+ * unsigned code minus its group's zero point. */
+static int weight_int(const uint8_t *prow, int64_t k, const uint8_t *zp, int64_t group)
+{
+    if (!zp)
+        return nibble_value(prow, k);
+    return raw_nibble(prow, k) - (int)zp[k / group];
 }
 
 void int4_oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *out)
@@ -205,14 +294,14 @@ void int4_oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *out
  *        the magnitude against which the tolerance is stated.
  */
 void int4_oracle_matmul_ex(const float *x, int64_t M, const uint8_t *packed,
-                           const uint16_t *scales, int64_t N, int64_t K, int64_t group,
-                           const float *bias, int relu, float *y, double *bound);
+                           const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                           int64_t group, const float *bias, int relu, float *y, double *bound);
 
 void int4_oracle_matmul(const float *x, int64_t M, const uint8_t *packed,
                         const uint16_t *scales, int64_t N, int64_t K, int64_t group,
                         float *y, double *bound)
 {
-    int4_oracle_matmul_ex(x, M, packed, scales, N, K, group, NULL, 0, y, bound);
+    int4_oracle_matmul_ex(x, M, packed, scales, NULL, N, K, group, NULL, 0, y, bound);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -222,10 +311,11 @@ void int4_oracle_matmul(const float *x, int64_t M, const uint8_t *packed,
 /* ------------------------------------------------------------------------ */
 
 /*
- * binary32 output. q has at most 4 significant bits and the widened scale at
- * most 11, so the binary32 product is exact.
+ * zeros: NULL for symmetric codes, else [N, G] zero points of affine codes
+ * (the value is code - zp). binary32 output: the integer has at most 5
+ * significant bits and the widened scale 11, so the product is exact.
  */
-void int4_oracle_dequantize(const uint8_t *packed, const uint16_t *scales,
+void int4_oracle_dequantize(const uint8_t *packed, const uint16_t *scales, const uint8_t *zeros,
                             int64_t N, int64_t K, int64_t group, float *out)
 {
     int64_t G = int4_oracle_num_groups(K, group);
@@ -233,7 +323,8 @@ void int4_oracle_dequantize(const uint8_t *packed, const uint16_t *scales,
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
             float sf = int4_oracle_float_from_half(scales[n * G + k / group]);
-            out[n * K + k] = (float)nibble_value(packed + n * B, k) * sf;
+            int q = weight_int(packed + n * B, k, zeros ? zeros + n * G : NULL, group);
+            out[n * K + k] = (float)q * sf;
         }
 }
 
@@ -242,14 +333,16 @@ void int4_oracle_dequantize(const uint8_t *packed, const uint16_t *scales,
  * binary16 (ties to even); magnitudes of 65520 and more become infinities.
  */
 void int4_oracle_dequantize_half(const uint8_t *packed, const uint16_t *scales,
-                                 int64_t N, int64_t K, int64_t group, uint16_t *out)
+                                 const uint8_t *zeros, int64_t N, int64_t K, int64_t group,
+                                 uint16_t *out)
 {
     int64_t G = int4_oracle_num_groups(K, group);
     int64_t B = int4_oracle_packed_row_bytes(K);
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
             float sf = int4_oracle_float_from_half(scales[n * G + k / group]);
-            out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k) * sf);
+            int q = weight_int(packed + n * B, k, zeros ? zeros + n * G : NULL, group);
+            out[n * K + k] = int4_oracle_half_from_float((float)q * sf);
         }
 }
 
@@ -262,6 +355,8 @@ void int4_oracle_dequantize_half(const uint8_t *packed, const uint16_t *scales,
 /*
  * The matmul sum follows the statement's order (per group: x times the
  * group's integer codes, then the group's scale), accumulated in double.
+ * zeros: NULL for symmetric codes, else [N, G] zero points (affine codes,
+ * integer weight = code - zp).
  * bias: optional [N] binary32 (NULL: none), added in double; the result is
  * rounded once to binary32. relu: 0 or 1; ReLU keeps a value greater than
  * zero and gives +0 otherwise (the engine page's `acc > 0 ? acc : 0`).
@@ -270,8 +365,8 @@ void int4_oracle_dequantize_half(const uint8_t *packed, const uint16_t *scales,
  * this function with no bias and no activation.
  */
 void int4_oracle_matmul_ex(const float *x, int64_t M, const uint8_t *packed,
-                           const uint16_t *scales, int64_t N, int64_t K, int64_t group,
-                           const float *bias, int relu, float *y, double *bound)
+                           const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                           int64_t group, const float *bias, int relu, float *y, double *bound)
 {
     int64_t G = int4_oracle_num_groups(K, group);
     int64_t B = int4_oracle_packed_row_bytes(K);
@@ -285,7 +380,8 @@ void int4_oracle_matmul_ex(const float *x, int64_t M, const uint8_t *packed,
                 int64_t k1 = k0 + group < K ? k0 + group : K;
                 double part = 0.0, part_abs = 0.0;
                 for (int64_t k = k0; k < k1; ++k) {
-                    double p = (double)xrow[k] * (double)nibble_value(prow, k);
+                    double p = (double)xrow[k] *
+                               (double)weight_int(prow, k, zeros ? zeros + n * G : NULL, group);
                     part += p;
                     part_abs += fabs(p);
                 }

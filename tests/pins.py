@@ -392,8 +392,8 @@ def pin_p3_correctness_pattern(lib):
 
 # ---------------------------------------------------------------- dequantize
 
-def _dq(lib, p, s, K, g, dtype=np.float32):
-    return oracle.dequantize_int4(p, s, K, g, dtype=dtype, lib=lib)
+def _dq(lib, p, s, K, g, dtype=np.float32, zeros=None):
+    return oracle.dequantize_int4(p, s, K, g, dtype=dtype, zeros=zeros, lib=lib)
 
 
 def pin_dequantize_p4_example(lib):
@@ -451,8 +451,9 @@ def pin_dequantize_extremes(lib):
 
 # ------------------------------------------------------------------ epilogue
 
-def _mmx(lib, x, p, s, K, g, bias=None, relu=False, bound=False):
-    return oracle.int4_matmul_ex(x, p, s, K, g, bias=bias, relu=relu, with_bound=bound, lib=lib)
+def _mmx(lib, x, p, s, K, g, bias=None, relu=False, bound=False, zeros=None):
+    return oracle.int4_matmul_ex(x, p, s, K, g, bias=bias, relu=relu, with_bound=bound,
+                                 zeros=zeros, lib=lib)
 
 
 def pin_epilogue_engine_forward(lib):
@@ -487,6 +488,119 @@ def pin_epilogue_reduces_to_matmul(lib):
     assert np.array_equal(_mmx(lib, x, p, s, K, g, bias=np.zeros(N, np.float32)), y)
     big = np.full(N, -1e6, np.float32)
     assert np.all(_mmx(lib, x, p, s, K, g, bias=big, relu=True) == 0)
+
+
+# ------------------------------------------------------------- affine codes
+# "Build a Blockwise INT4 Inference Engine", step 2 (q = round(w / scale + zp)
+# in [0, 15], w_hat = (q - zp) * scale) and "Quantizing a Language Model From
+# Scratch", affine quantization (S = (max - min) / 15; Z makes 0.0 exact).
+
+def _qa(lib, w, g):
+    return oracle.quantize_int4_affine(np.asarray(w, np.float32), g, lib=lib)
+
+
+def pin_affine_hand_example(lib):
+    """Worked by hand from the engine page's formula: w = [-1, 0.5, 14, 3], g = 4.
+    Range [-1, 14] -> scale 15/15 = 1, zp = round(1/1) = 1; codes round(w + 1)
+    with ties to even: 0, round(1.5) = 2, 15, 4 -> bytes 0x20, 0x4F; w_hat =
+    (q - 1) * 1 = [-1, 1, 14, 3]. (Rounding w / scale first and then adding zp
+    would give code 1 for 0.5.)"""
+    p, s, z, K = _qa(lib, [[-1.0, 0.5, 14.0, 3.0]], 4)
+    assert p.tolist() == [[0x20, 0x4F]], p
+    assert s.astype(np.float32).tolist() == [[1.0]] and z.tolist() == [[1]]
+    assert _dq(lib, p, s, K, 4, zeros=z).tolist() == [[-1.0, 1.0, 14.0, 3.0]]
+
+
+def pin_affine_constant_groups(lib):
+    """A zero group: scale 0, zero point 0, codes 0, w_hat 0. A constant group
+    c > 0: range [0, c], zp 0, every code 15, w_hat = 15 * scale. A constant
+    group -c: range [-c, 0], zp 15, every code 0, w_hat = -15 * scale."""
+    w = np.array([[0.0] * 4 + [3.0] * 4 + [-3.0] * 3], np.float32)
+    p, s, z, K = _qa(lib, w, 4)
+    assert s.view(np.uint16).tolist() == [[0x0000, 0x3266, 0x3266]], s   # 0x3266: binary16 nearest 0.2
+    assert z.tolist() == [[0, 0, 15]]
+    codes = np.stack([p & 0xF, p >> 4], 2).reshape(1, -1)[:, :K]
+    assert codes.tolist() == [[0] * 4 + [15] * 4 + [0] * 3]
+    assert p[0, -1] >> 4 == 0                          # pad nibble of odd K
+    assert _dq(lib, p, s, K, 4, zeros=z).tolist() == [[0.0] * 4 + [2.999267578125] * 4 + [-2.999267578125] * 3]
+
+
+def pin_affine_vs_brute(lib):
+    """Codes, scales and zero points equal the NumPy affine quantizer bit for bit
+    (NumPy's own float16 rounding and rint); w_hat equals its float64
+    reconstruction exactly; ragged groups, odd K, skewed groups that do not
+    straddle zero."""
+    rng = np.random.default_rng(41)
+    for (N, K, g) in [(3, 1, 1), (5, 9, 2), (7, 31, 3), (4, 45, 5), (6, 64, 4), (9, 301, 128),
+                      (8, 256, 32), (5, 129, 64), (3, 7, 128)]:
+        for shift in (0.0, 3.0, -3.0):
+            w = (rng.normal(size=(N, K)) + shift).astype(np.float32)
+            p, s, z, _ = _qa(lib, w, g)
+            bp, bs, bz, _ = brute.quantize_int4_affine(w, g)
+            assert np.array_equal(p, bp), (N, K, g, shift)
+            assert np.array_equal(s.view(np.uint16), bs.view(np.uint16)), (N, K, g, shift)
+            assert np.array_equal(z, bz), (N, K, g, shift)
+            ref = brute.dequantize_affine(p, s, z, K, g)
+            assert np.array_equal(_dq(lib, p, s, K, g, zeros=z).astype(np.float64), ref)
+            h = _dq(lib, p, s, K, g, np.float16, zeros=z)
+            assert np.array_equal(h.view(np.uint16), ref.astype(np.float16).view(np.uint16))
+
+
+def pin_affine_round_trip_bound(lib):
+    """Every w_hat lies within half a step of w (the range [min(lo,0), max(hi,0)]
+    is covered by the grid (q - zp) * scale, q = 0..15, up to the binary16
+    rounding of the scale), and an exact 0.0 comes back as exactly 0.0 (the
+    zero point's purpose), for centred and shifted groups."""
+    rng = np.random.default_rng(42)
+    for shift in (0.0, 0.7, -0.7, 5.0, -5.0):
+        w = (rng.normal(size=(16, 512)) + shift).astype(np.float32)
+        w[:, ::37] = 0.0
+        p, s, z, K = _qa(lib, w, 128)
+        wh = _dq(lib, p, s, K, 128, zeros=z)
+        sf = np.repeat(s.astype(np.float64), 128, 1)
+        err = np.abs(wh.astype(np.float64) - w)
+        assert np.all(err <= 0.5 * sf + 16 * 2.0 ** -10 * sf + 1e-7), (shift, float(err.max()))
+        assert np.all(wh[:, ::37] == 0.0), shift
+
+
+def pin_affine_matches_symmetric_at_zp8(lib):
+    """Symmetric codes v in [-8, 7] are the affine codes u = v + 8 = nibble ^ 8
+    with every zero point 8: affine dequantize and matmul of (packed ^ 0x88,
+    zeros = 8) equal the symmetric ones exactly."""
+    rng = np.random.default_rng(43)
+    for (M, N, K, g) in [(3, 20, 256, 128), (2, 9, 31, 3), (4, 17, 129, 64)]:
+        w = rng.normal(size=(N, K)).astype(np.float32)
+        x = rng.normal(size=(M, K)).astype(np.float32)
+        p, s, _ = _q(lib, w, g)
+        pa = p ^ np.uint8(0x88)
+        if K % 2:
+            pa[:, -1] &= 0x0F                            # the pad nibble stays zero
+        z8 = np.full(s.shape, 8, np.uint8)
+        assert np.array_equal(_dq(lib, pa, s, K, g, zeros=z8), _dq(lib, p, s, K, g))
+        assert np.array_equal(_mmx(lib, x, pa, s, K, g, zeros=z8), _mmx(lib, x, p, s, K, g))
+
+
+def pin_affine_matmul(lib):
+    """Affine matmul = float64 x @ w_hat.T of the NumPy reconstruction, rounded
+    once (within 1e-6 of the sum of magnitudes), with bias and ReLU; a one-hot
+    x picks one w_hat column exactly; the engine page's test pattern (4 x 8 x
+    256, block 128, W * 0.5, bias, ReLU) within its 1e-3."""
+    rng = np.random.default_rng(44)
+    for (M, N, K, g) in [(4, 8, 256, 128), (3, 48, 301, 128), (5, 9, 31, 3), (2, 17, 129, 64)]:
+        w = (rng.normal(size=(N, K)) * 0.5 + 0.3).astype(np.float32)
+        x = rng.normal(size=(M, K)).astype(np.float32)
+        b = rng.normal(size=N).astype(np.float32)
+        p, s, z, _ = _qa(lib, w, g)
+        wh = brute.dequantize_affine(p, s, z, K, g)
+        ref = x.astype(np.float64) @ wh.T + b.astype(np.float64)
+        y, bnd = _mmx(lib, x, p, s, K, g, bias=b, bound=True, zeros=z)
+        assert np.all(np.abs(y - ref) <= 1e-6 * (bnd + np.abs(b)) + 1e-30), (M, N, K, g)
+        yr = _mmx(lib, x, p, s, K, g, bias=b, relu=True, zeros=z)
+        assert float(np.abs(yr - np.maximum(ref, 0)).max()) < 1e-3
+        for k in (0, K // 2, K - 1):
+            e = np.zeros((1, K), np.float32)
+            e[0, k] = 1.0
+            assert np.array_equal(_mmx(lib, e, p, s, K, g, zeros=z)[0], wh[:, k].astype(np.float32))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

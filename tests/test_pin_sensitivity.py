@@ -39,8 +39,8 @@ MUTANTS = [
     ("unpack_no_sign_extension",
      "return v >= 8 ? v - 16 : v;", "return v;"),
     ("unpack_high_nibble_first",
-     "int v = (prow[k / 2] >> (4 * (int)(k % 2))) & 0xF;",
-     "int v = (prow[k / 2] >> (4 * (int)(1 - k % 2))) & 0xF;"),
+     "return (prow[k / 2] >> (4 * (int)(k % 2))) & 0xF;",
+     "return (prow[k / 2] >> (4 * (int)(1 - k % 2))) & 0xF;"),
     ("matmul_scale_ignores_row",
      "int4_oracle_float_from_half(scales[n * G + gi]);", "int4_oracle_float_from_half(scales[gi]);"),
     ("matmul_drops_partial_group",
@@ -56,14 +56,25 @@ MUTANTS = [
     ("half_overflow_threshold",
      "if (a >= 65520.0)", "if (a > 65504.0)"),
     ("dequantize_swaps_nibbles",
-     "out[n * K + k] = (float)nibble_value(packed + n * B, k) * sf;",
-     "out[n * K + k] = (float)nibble_value(packed + n * B, k ^ 1) * sf;"),
+     "            out[n * K + k] = (float)q * sf;",
+     "            out[n * K + k] = (float)weight_int(packed + n * B, k ^ 1, zeros ? zeros + n * G : NULL, group) * sf;"),
     ("dequantize_scale_of_next_group",
-     "float sf = int4_oracle_float_from_half(scales[n * G + k / group]);\n            out[n * K + k] = (float)",
-     "float sf = int4_oracle_float_from_half(scales[n * G + (k + 1) / group < G ? n * G + (k + 1) / group : 0]);\n            out[n * K + k] = (float)"),
+     "float sf = int4_oracle_float_from_half(scales[n * G + k / group]);\n            int q = weight_int(packed + n * B, k, zeros ? zeros + n * G : NULL, group);\n            out[n * K + k] = (float)q",
+     "float sf = int4_oracle_float_from_half(scales[n * G + ((k + 1) / group < G ? (k + 1) / group : 0)]);\n            int q = weight_int(packed + n * B, k, zeros ? zeros + n * G : NULL, group);\n            out[n * K + k] = (float)q"),
     ("dequantize_half_from_unscaled",
-     "out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k) * sf);",
-     "out[n * K + k] = int4_oracle_half_from_float((float)nibble_value(packed + n * B, k));"),
+     "out[n * K + k] = int4_oracle_half_from_float((float)q * sf);",
+     "out[n * K + k] = int4_oracle_half_from_float((float)q);"),
+    ("affine_zero_point_added_after_rounding",
+     "double r = rint((double)t + (double)zp);", "double r = rint((double)t) + (double)zp;"),
+    ("affine_range_excludes_zero",
+     "float lo = 0.0f, hi = 0.0f;             /* the range includes zero */",
+     "float lo = row[k0], hi = row[k0];"),
+    ("affine_zero_point_sign",
+     "float z = rintf(-lo / sf);", "float z = rintf(lo / sf);"),
+    ("affine_code_ignores_zero_point",
+     "    return raw_nibble(prow, k) - (int)zp[k / group];", "    return raw_nibble(prow, k);"),
+    ("affine_scale_over_16",
+     "float s32 = (hi - lo) / 15.0f;", "float s32 = (hi - lo) / 16.0f;"),
     ("epilogue_bias_dropped",
      "            acc += (double)bias[n];", "            acc += 0.0;"),
     ("epilogue_relu_keeps_negatives",
