@@ -180,12 +180,21 @@ def unfused_comparison(mats, pool, reps=20):
             def gemm():
                 F.linear(x, what)
 
+            bias = torch.randn(N, device=x.device)
+
+            def fused_bias_relu():
+                p, s_ = nxt()
+                assert L.int4_matmul_ex(x.data_ptr(), 1, M_, p.data_ptr(), s_.data_ptr(), N, K, GROUP,
+                                        bias.data_ptr(), 1, y.data_ptr(), cur()) == 0
+
             t_f, t_d, t_g = timed(fused), timed(dequant), timed(gemm)
+            t_e = timed(fused_bias_relu)
             per[m["name"]] = {"fused_us": round(t_f, 3), "dequant_us": round(t_d, 3),
-                              "gemm_us": round(t_g, 3)}
+                              "gemm_us": round(t_g, 3), "fused_bias_relu_us": round(t_e, 3)}
             tot["fused_us"] += t_f
             tot["dequant_us"] += t_d
             tot["gemm_us"] += t_g
+            tot["fused_bias_relu_us"] = tot.get("fused_bias_relu_us", 0.0) + t_e
             del what
         unf = tot["dequant_us"] + tot["gemm_us"]
         w_bytes = sum(packed_weight_bytes(m["N"], m["K"]) for m in mats)
@@ -193,13 +202,15 @@ def unfused_comparison(mats, pool, reps=20):
         out[key] = {"M": M_, "fused_us": round(tot["fused_us"], 3),
                     "unfused_us": round(unf, 3), "dequant_us": round(tot["dequant_us"], 3),
                     "gemm_us": round(tot["gemm_us"], 3),
+                    "fused_bias_relu_us": round(tot["fused_bias_relu_us"], 3),
                     "fused_speedup": round(unf / tot["fused_us"], 3),
                     "weight_bytes_fused": w_bytes,
                     "weight_bytes_unfused": w_bytes + 2 * fp16_bytes,
                     "per_shape": per}
     out["note"] = ("three c4 shapes summed; unfused = int4_dequantize to fp16 w_hat (written to HBM) "
                    "+ F.linear(x, w_hat) (hipBLASLt fp16 GEMM, fp16 output); fused = int4_matmul "
-                   "(fp32 output); weights from the HBM rotation pool at M = 1")
+                   "(fp32 output); fused_bias_relu = int4_matmul_ex with a bias and ReLU; "
+                   "weights from the HBM rotation pool at M = 1")
     return out
 
 

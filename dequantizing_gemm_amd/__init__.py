@@ -11,7 +11,13 @@ packing and a dequantizing matmul" (statement):
 
 plus dequantize_int4(packed, scales, K, group=128, dtype=float16) -> w_hat [N, K],
 the reconstruction q * scale that an unfused dequantize-then-GEMM would
-materialise.
+materialise, and the affine form of the codes ("Build a Blockwise INT4
+Inference Engine", step 2):
+
+    quantize_int4_affine(w, group=128) -> (packed, scales, zeros, K)
+
+whose ``zeros`` are passed to dequantize_int4 / int4_matmul / int4_matmul_path
+as ``zeros=``.
 
 All tensors are torch tensors on the GPU; torch provides the device memory and
 the stream (work is enqueued on ``torch.cuda.current_stream()``). Every step of
@@ -26,7 +32,8 @@ import os
 
 import torch
 
-__all__ = ["quantize_int4", "unpack_int4", "dequantize_int4", "int4_matmul", "int4_matmul_path", "matmul_select",
+__all__ = ["quantize_int4", "quantize_int4_affine", "unpack_int4", "dequantize_int4", "int4_matmul",
+           "int4_matmul_path", "matmul_select",
            "num_groups", "packed_bytes", "lib", "LIB_PATH", "Int4Error", "PATHS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4dq.so")
@@ -50,6 +57,10 @@ SIGNATURES = {
     "int4_matmul_ex": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp]),
     "int4_matmul_path": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp]),
     "int4_matmul_select": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "int4_quantize_affine": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "int4_dequantize_affine": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
+    "int4_matmul_affine": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp,
+                                  _int, _vp]),
     "int4_last_error": (ctypes.c_char_p, []),
 }
 
@@ -122,6 +133,33 @@ def quantize_int4(w: torch.Tensor, group: int = 128):
     return packed, scales, K
 
 
+def quantize_int4_affine(w: torch.Tensor, group: int = 128):
+    """w [N, K] float32 -> (packed uint8 [N, ceil(K/2)] unsigned codes, scales
+    float16 [N, G], zero points uint8 [N, G], K)."""
+    _gpu(w, "w", torch.float32)
+    N, K = w.shape
+    G = num_groups(K, group)
+    if G < 1:
+        raise ValueError(f"invalid K={K} / group={group}")
+    packed = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=w.device)
+    with torch.cuda.device(w.device):
+        rc = lib.int4_quantize_affine(w.data_ptr(), N, K, group, packed.data_ptr(),
+                                      scales.data_ptr(), zeros.data_ptr(), _stream(w))
+    _raise(rc, "int4_quantize_affine")
+    return packed, scales, zeros, K
+
+
+def _zeros_ptr(zeros, N, K, group, device):
+    if zeros is None:
+        return None
+    _gpu(zeros, "zeros", torch.uint8)
+    if tuple(zeros.shape) != (N, num_groups(K, group)) or zeros.device != device:
+        raise ValueError(f"zeros must be uint8 [{N}, {num_groups(K, group)}] on {device}")
+    return zeros.data_ptr()
+
+
 def unpack_int4(packed: torch.Tensor, K: int) -> torch.Tensor:
     """packed uint8 [N, ceil(K/2)] -> int8 [N, K], sign-extended."""
     _gpu(packed, "packed", torch.uint8)
@@ -136,8 +174,10 @@ def unpack_int4(packed: torch.Tensor, K: int) -> torch.Tensor:
 
 
 def dequantize_int4(packed: torch.Tensor, scales: torch.Tensor, K: int, group: int = 128,
-                    dtype: torch.dtype = torch.float16) -> torch.Tensor:
-    """w_hat [N, K] = q * scale as float32 (exact) or float16 (nearest even)."""
+                    dtype: torch.dtype = torch.float16,
+                    zeros: torch.Tensor | None = None) -> torch.Tensor:
+    """w_hat [N, K] = q * scale as float32 (exact) or float16 (nearest even);
+    with ``zeros`` (affine codes) w_hat = (u - zero point) * scale."""
     _gpu(packed, "packed", torch.uint8)
     _gpu(scales, "scales", torch.float16)
     N = packed.shape[0]
@@ -147,11 +187,16 @@ def dequantize_int4(packed: torch.Tensor, scales: torch.Tensor, K: int, group: i
         raise ValueError(f"scales shape {tuple(scales.shape)} != {(N, num_groups(K, group))}")
     if dtype not in (torch.float32, torch.float16):
         raise ValueError(f"dtype must be float32 or float16 (got {dtype})")
+    zp = _zeros_ptr(zeros, N, K, group, packed.device)
     out = torch.empty((N, K), dtype=dtype, device=packed.device)
+    od = OUT_F16 if dtype == torch.float16 else OUT_F32
     with torch.cuda.device(packed.device):
-        rc = lib.int4_dequantize(packed.data_ptr(), scales.data_ptr(), N, K, group,
-                                 OUT_F16 if dtype == torch.float16 else OUT_F32, out.data_ptr(),
-                                 _stream(packed))
+        if zp is None:
+            rc = lib.int4_dequantize(packed.data_ptr(), scales.data_ptr(), N, K, group, od,
+                                     out.data_ptr(), _stream(packed))
+        else:
+            rc = lib.int4_dequantize_affine(packed.data_ptr(), scales.data_ptr(), zp, N, K, group,
+                                            od, out.data_ptr(), _stream(packed))
     _raise(rc, "int4_dequantize")
     return out
 
@@ -177,9 +222,10 @@ def _matmul_args(x, packed, scales, K, group):
 
 def int4_matmul_path(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
                      group: int = 128, path: str = "auto", out: torch.Tensor | None = None,
-                     bias: torch.Tensor | None = None, relu: bool = False):
+                     bias: torch.Tensor | None = None, relu: bool = False,
+                     zeros: torch.Tensor | None = None):
     """y [M, N] float32 = act(x @ dequantize(W).T + bias) through a chosen kernel
-    (see PATHS); no bias and no ReLU unless given."""
+    (see PATHS); no bias and no ReLU unless given; affine codes with ``zeros``."""
     M, N, xd = _matmul_args(x, packed, scales, K, group)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
@@ -193,20 +239,28 @@ def int4_matmul_path(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
         if bias.shape[0] != N or bias.device != x.device:
             raise ValueError(f"bias must be [N] = [{N}] on {x.device}")
         bptr = bias.data_ptr()
+    zp = _zeros_ptr(zeros, N, K, group, x.device)
+    act = ACT_RELU if relu else ACT_NONE
     with torch.cuda.device(x.device):
-        rc = lib.int4_matmul_path(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), N, K,
-                                  group, bptr, ACT_RELU if relu else ACT_NONE, out.data_ptr(),
-                                  PATHS[path], _stream(x))
+        if zp is None:
+            rc = lib.int4_matmul_path(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), N,
+                                      K, group, bptr, act, out.data_ptr(), PATHS[path], _stream(x))
+        else:
+            rc = lib.int4_matmul_affine(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(),
+                                        zp, N, K, group, bptr, act, out.data_ptr(), PATHS[path],
+                                        _stream(x))
     _raise(rc, "int4_matmul")
     return out
 
 
 def int4_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
                 group: int = 128, out: torch.Tensor | None = None, *,
-                bias: torch.Tensor | None = None, relu: bool = False) -> torch.Tensor:
+                bias: torch.Tensor | None = None, relu: bool = False,
+                zeros: torch.Tensor | None = None) -> torch.Tensor:
     """y [M, N] float32 = x @ dequantize(W).T, one group at a time (integer-first);
-    with the engine page's epilogue act(... + bias) when bias or relu is given."""
-    return int4_matmul_path(x, packed, scales, K, group, "auto", out, bias, relu)
+    with the engine page's epilogue act(... + bias) when bias or relu is given,
+    and affine codes when zeros is given."""
+    return int4_matmul_path(x, packed, scales, K, group, "auto", out, bias, relu, zeros)
 
 
 def matmul_select(x, packed, scales, K, group=128) -> str:

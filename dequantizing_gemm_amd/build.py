@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,15 +46,39 @@ EXTRA = {"matmul_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
          "matmul_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
+# Every kernel's resource-usage remark is read back: a kernel that uses scratch
+# memory (register spills, or a register array moved to the stack) fails the
+# build, since on these kernels that means a several-fold slowdown.
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def _scratch_users(stderr: str) -> list[str]:
+    out = []
+    for block in re.split(r"remark: [^\n]*?Function Name: ", stderr)[1:]:
+        name = block.split()[0]
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", block)
+        if m and int(m.group(1)) > 0:
+            out.append(f"{name} ({m.group(1)} B/lane)")
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *HIPFLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *HIPFLAGS, *EXTRA.get(src, []), *RESOURCE_REMARKS, *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
-    # the host pass warns that it does not know the packed-fp32 feature: harmless
-    noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    spills = _scratch_users(r.stderr)
+    if spills:
+        raise RuntimeError(f"kernels in {src} use scratch memory: " + "; ".join(spills))
+    # the host pass warns that it does not know the packed-fp32 feature: harmless;
+    # the resource remarks were read above
+    noise = [ln for ln in r.stderr.splitlines()
+             if "packed-fp32-ops" not in ln and "kernel-resource-usage" not in ln and ln.strip()
+             and not ln.lstrip().startswith(("|", "^"))
+             and not re.match(r"\s*\d+ \|", ln)]
     if noise:
         sys.stderr.write("\n".join(noise) + "\n")
     return obj

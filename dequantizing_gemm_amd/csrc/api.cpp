@@ -59,12 +59,34 @@ int check_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
   return INT4DQ_OK;
 }
 
+// Shared body of int4_matmul_path and int4_matmul_affine (zeros: nullptr for
+// symmetric codes).
+int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
+                const float* bias, int act, float* y, int path, void* stream);
+
 int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t N,
                 int64_t K, int64_t group) {
   if (!int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_GEMV;
   if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_SKINNY;
   if (!int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group)) return INT4DQ_PATH_TILED;
   return INT4DQ_PATH_GENERIC;
+}
+
+int dequantize_impl(const char* fn, const uint8_t* packed, const uint16_t* scales,
+                    const uint8_t* zeros, int64_t N, int64_t K, int64_t group, int out_dtype,
+                    void* out, void* stream) {
+  if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "%s: N and K must be >= 1 (got N=%lld K=%lld)", fn, (long long)N, (long long)K);
+  if (group < 1) return fail(INT4DQ_EINVAL, "%s: group must be >= 1 (got %lld)", fn, (long long)group);
+  if (out_dtype != INT4DQ_OUT_F32 && out_dtype != INT4DQ_OUT_F16)
+    return fail(INT4DQ_EINVAL, "%s: unknown out_dtype %d", fn, out_dtype);
+  int64_t t;
+  if (!mul_ok(N, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(N, (K + group - 1) / group, &t) || !mul_ok(t, 2, &t))
+    return fail(INT4DQ_EINVAL, "%s: sizes overflow int64", fn);
+  if (!packed || !scales || !out) return fail(INT4DQ_EINVAL, "%s: packed, scales and out must be non-NULL", fn);
+  return hip_status(int4dq::launch_dequantize(packed, scales, zeros, N, K, group, out_dtype == INT4DQ_OUT_F16,
+                                              out, (hipStream_t)stream),
+                    "int4_dequantize launch");
 }
 
 }  // namespace
@@ -105,55 +127,42 @@ int int4_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* out, void* 
 
 int int4_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
                     int64_t group, int out_dtype, void* out, void* stream) {
-  if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "int4_dequantize: N and K must be >= 1 (got N=%lld K=%lld)", (long long)N, (long long)K);
-  if (group < 1) return fail(INT4DQ_EINVAL, "int4_dequantize: group must be >= 1 (got %lld)", (long long)group);
-  if (out_dtype != INT4DQ_OUT_F32 && out_dtype != INT4DQ_OUT_F16)
-    return fail(INT4DQ_EINVAL, "int4_dequantize: unknown out_dtype %d", out_dtype);
+  return dequantize_impl("int4_dequantize", packed, scales, nullptr, N, K, group, out_dtype, out, stream);
+}
+
+int int4_dequantize_affine(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                           int64_t N, int64_t K, int64_t group, int out_dtype, void* out,
+                           void* stream) {
+  if (!zeros) return fail(INT4DQ_EINVAL, "int4_dequantize_affine: zeros must be non-NULL");
+  return dequantize_impl("int4_dequantize_affine", packed, scales, zeros, N, K, group, out_dtype, out, stream);
+}
+
+int int4_quantize_affine(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
+                         uint16_t* scales, uint8_t* zeros, void* stream) {
+  if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "int4_quantize_affine: N and K must be >= 1 (got N=%lld K=%lld)", (long long)N, (long long)K);
+  if (group < 1) return fail(INT4DQ_EINVAL, "int4_quantize_affine: group must be >= 1 (got %lld)", (long long)group);
   int64_t t;
   if (!mul_ok(N, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(N, (K + group - 1) / group, &t) || !mul_ok(t, 2, &t))
-    return fail(INT4DQ_EINVAL, "int4_dequantize: sizes overflow int64");
-  if (!packed || !scales || !out) return fail(INT4DQ_EINVAL, "int4_dequantize: packed, scales and out must be non-NULL");
-  return hip_status(int4dq::launch_dequantize(packed, scales, N, K, group, out_dtype == INT4DQ_OUT_F16, out,
-                                              (hipStream_t)stream),
-                    "int4_dequantize launch");
+    return fail(INT4DQ_EINVAL, "int4_quantize_affine: sizes overflow int64");
+  if (!w || !packed || !scales || !zeros)
+    return fail(INT4DQ_EINVAL, "int4_quantize_affine: w, packed, scales and zeros must be non-NULL");
+  return hip_status(int4dq::launch_quantize_affine(w, N, K, group, packed, scales, zeros, (hipStream_t)stream),
+                    "int4_quantize_affine launch");
 }
 
 int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                      const uint16_t* scales, int64_t N, int64_t K, int64_t group,
                      const float* bias, int act, float* y, int path, void* stream) {
-  int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
-  if (rc != INT4DQ_OK) return rc;
-  if (act != INT4DQ_ACT_NONE && act != INT4DQ_ACT_RELU)
-    return fail(INT4DQ_EINVAL, "int4_matmul: unknown activation %d", act);
-  const int4dq::Epilogue ep{bias, act == INT4DQ_ACT_RELU ? 1 : 0};
-  if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_GEMV)
-    return fail(INT4DQ_EINVAL, "int4_matmul_path: unknown path %d", path);
-  if (M == 0) return ok();
-  if (path == INT4DQ_PATH_AUTO) path = choose_path(x, x_dtype, M, packed, N, K, group);
-  const hipStream_t s = (hipStream_t)stream;
-  switch (path) {
-    case INT4DQ_PATH_SKINNY: {
-      const char* why = int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group);
-      if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
-      return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, N, K, group, y, ep, s),
-                        "int4_matmul skinny launch");
-    }
-    case INT4DQ_PATH_GEMV: {
-      const char* why = int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group);
-      if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
-      return hip_status(int4dq::launch_matmul_gemv(x, packed, scales, N, K, group, y, ep, s),
-                        "int4_matmul gemv launch");
-    }
-    case INT4DQ_PATH_TILED: {
-      const char* why = int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group);
-      if (why) return fail(INT4DQ_EUNSUPPORTED, "int4_matmul_path: %s", why);
-      return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, N, K, group, y, ep, s),
-                        "int4_matmul tiled launch");
-    }
-    default:
-      return hip_status(int4dq::launch_matmul_generic(x, x_dtype, M, packed, scales, N, K, group, y, ep, s),
-                        "int4_matmul generic launch");
-  }
+  return matmul_impl("int4_matmul_path", x, x_dtype, M, packed, scales, nullptr, N, K, group, bias,
+                     act, y, path, stream);
+}
+
+int int4_matmul_affine(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                       const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                       int64_t group, const float* bias, int act, float* y, int path, void* stream) {
+  if (!zeros) return fail(INT4DQ_EINVAL, "int4_matmul_affine: zeros must be non-NULL");
+  return matmul_impl("int4_matmul_affine", x, x_dtype, M, packed, scales, zeros, N, K, group, bias,
+                     act, y, path, stream);
 }
 
 int int4_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
@@ -180,3 +189,45 @@ int int4_matmul_select(const void* x, int x_dtype, int64_t M, const uint8_t* pac
 const char* int4_last_error(void) { return g_err; }
 
 }  // extern "C"
+
+namespace {
+
+int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
+                const float* bias, int act, float* y, int path, void* stream) {
+  int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
+  if (rc != INT4DQ_OK) return rc;
+  if (act != INT4DQ_ACT_NONE && act != INT4DQ_ACT_RELU)
+    return fail(INT4DQ_EINVAL, "%s: unknown activation %d", fn, act);
+  const int4dq::Epilogue ep{bias, act == INT4DQ_ACT_RELU ? 1 : 0};
+  if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_GEMV)
+    return fail(INT4DQ_EINVAL, "%s: unknown path %d", fn, path);
+  if (M == 0) return ok();
+  if (path == INT4DQ_PATH_AUTO) path = choose_path(x, x_dtype, M, packed, N, K, group);
+  const hipStream_t s = (hipStream_t)stream;
+  switch (path) {
+    case INT4DQ_PATH_SKINNY: {
+      const char* why = int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group);
+      if (why) return fail(INT4DQ_EUNSUPPORTED, "%s: %s", fn, why);
+      return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, zeros, N, K, group, y, ep, s),
+                        "int4_matmul skinny launch");
+    }
+    case INT4DQ_PATH_GEMV: {
+      const char* why = int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group);
+      if (why) return fail(INT4DQ_EUNSUPPORTED, "%s: %s", fn, why);
+      return hip_status(int4dq::launch_matmul_gemv(x, packed, scales, zeros, N, K, group, y, ep, s),
+                        "int4_matmul gemv launch");
+    }
+    case INT4DQ_PATH_TILED: {
+      const char* why = int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group);
+      if (why) return fail(INT4DQ_EUNSUPPORTED, "%s: %s", fn, why);
+      return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, zeros, N, K, group, y, ep, s),
+                        "int4_matmul tiled launch");
+    }
+    default:
+      return hip_status(int4dq::launch_matmul_generic(x, x_dtype, M, packed, scales, zeros, N, K, group, y, ep, s),
+                        "int4_matmul generic launch");
+  }
+}
+
+}  // namespace

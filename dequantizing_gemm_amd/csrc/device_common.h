@@ -71,6 +71,56 @@ __device__ __forceinline__ void codes_to_half_natural(uint32_t d, half2_t out[4]
   }
 }
 
+// ---------------------------------------------------------------------------
+// Affine codes ("Build a Blockwise INT4 Inference Engine", step 2: an unsigned
+// code u in [0, 15] and a per-group zero point zp, value u - zp).
+//
+// The same bit trick without the flip of bit 3 gives 1024 + u (and
+// 1024 + 16u, i.e. 64 + u after the 1/16 scaling), so a per-group bias of
+// -(1024 + zp) (resp. -(64 + zp)) leaves u - zp exactly. For zp in [0, 15]
+// the binary16 patterns are -(1024 + zp) = 0xE400 | zp and -(64 + zp) =
+// 0xD400 | (zp << 4): the bias words are a few integer ops per group.
+// ---------------------------------------------------------------------------
+
+// Natural-order bias pair {-(1024 + zp), -(64 + zp)} (low, high half).
+__device__ __forceinline__ uint32_t zp_bias_natural(uint32_t zp) {
+  return 0xD400E400u | zp | (zp << 20);
+}
+// Spread-order bias pairs: {-(1024 + zp)} x 2 and {-(64 + zp)} x 2.
+__device__ __forceinline__ uint32_t zp_bias_lo(uint32_t zp) { return 0xE400E400u | zp | (zp << 16); }
+__device__ __forceinline__ uint32_t zp_bias_hi(uint32_t zp) {
+  return 0xD400D400u | (zp << 4) | (zp << 20);
+}
+
+// codes_to_half_spread for affine codes: (c0 - zp, c4 - zp), ... (9 VALU ops
+// per 8 codes, like the symmetric form).
+__device__ __forceinline__ void codes_to_half_spread_zp(uint32_t d, half2_t out[4], uint32_t blo,
+                                                        uint32_t bhi) {
+  const uint32_t v = d >> 8;
+  const half2_t b0 = __builtin_bit_cast(half2_t, blo), b1 = __builtin_bit_cast(half2_t, bhi);
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  out[0] = __builtin_bit_cast(half2_t, (d & 0x000F000Fu) | 0x64006400u) + b0;
+  out[1] = __builtin_elementwise_fma(
+      __builtin_bit_cast(half2_t, (d & 0x00F000F0u) | 0x64006400u), sixteenth, b1);
+  out[2] = __builtin_bit_cast(half2_t, (v & 0x000F000Fu) | 0x64006400u) + b0;
+  out[3] = __builtin_elementwise_fma(
+      __builtin_bit_cast(half2_t, (v & 0x00F000F0u) | 0x64006400u), sixteenth, b1);
+}
+
+// codes_to_half_natural for affine codes: (c0 - zp, c1 - zp), ... with the
+// bias pair from zp_bias_natural.
+__device__ __forceinline__ void codes_to_half_natural_zp(uint32_t d, half2_t out[4], uint32_t bnat) {
+  const half2_t scale = {(_Float16)1.0f, (_Float16)0.0625f};
+  const half2_t bias = __builtin_bit_cast(half2_t, bnat);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t sel = (uint32_t)b | 0x0C000C00u | ((uint32_t)b << 16);
+    const uint32_t dup = __builtin_amdgcn_perm(0u, d, sel);
+    out[b] = __builtin_elementwise_fma(
+        __builtin_bit_cast(half2_t, (dup & 0x00F0000Fu) | 0x64006400u), scale, bias);
+  }
+}
+
 // Rearrange 8 consecutive fp16 activations (x0..x7, natural order in 4 words)
 // into the spread order (x0,x4),(x1,x5),(x2,x6),(x3,x7).
 __device__ __forceinline__ u32x4_t spread_perm_x(u32x4_t n) {

@@ -23,33 +23,41 @@ struct Epilogue {
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
                            uint16_t* scales, hipStream_t stream);
 
+// Affine codes (unsigned nibbles, one zero point byte per group).
+hipError_t launch_quantize_affine(const float* w, int64_t N, int64_t K, int64_t group,
+                                  uint8_t* packed, uint16_t* scales, uint8_t* zeros,
+                                  hipStream_t stream);
+
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* out,
                          hipStream_t stream);
 
-hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
-                             int64_t group, bool half, void* out, hipStream_t stream);
+// zeros: nullptr for symmetric codes, else [N, G] zero points (affine codes),
+// here and in every matmul launcher below.
+hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                             int64_t N, int64_t K, int64_t group, bool half, void* out,
+                             hipStream_t stream);
 
 hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
-                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
                                  float* y, Epilogue ep, hipStream_t stream);
 
 // nullptr if the kernel takes these arguments, else the reason it does not.
 const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
                                       const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
-                                const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
                                 float* y, Epilogue ep, hipStream_t stream);
 
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
                                     const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
-                              int64_t N, int64_t K, int64_t group, float* y, Epilogue ep,
+                              const uint8_t* zeros, int64_t N, int64_t K, int64_t group, float* y, Epilogue ep,
                               hipStream_t stream);
 
 const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
                                      int64_t K, int64_t group);
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
-                               const uint16_t* scales, int64_t N, int64_t K, int64_t group,
+                               const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
                                float* y, Epilogue ep, hipStream_t stream);
 
 }  // namespace int4dq

@@ -12,9 +12,9 @@
 // kernels here are pure streams of the packed weights, and the way they read
 // them decides their speed. Three variants, chosen by the launcher:
 //
-//  * large matrices (packed weights >= 48 MB, K <= 16384): whole rows per
-//    wavefront, 1 KB of one row per load, 4x4x4 MFMAs used on their diagonal
-//    (matmul_gemv_rows_kernel, below);
+//  * large matrices (packed weights >= 48 MB, K <= 16384; K <= 14336 for
+//    affine codes): whole rows per wavefront, 1 KB of one row per load,
+//    4x4x4 MFMAs used on their diagonal (matmul_gemv_rows_kernel, below);
 //  * K <= 12288 with group = 32 << p: 4 rows x 256 bytes per load, which is
 //    directly the B operand of v_mfma_f32_4x4x4f16 (matmul_gemv_mfma_kernel);
 //  * everything else (K <= 32768, group a multiple of 32): the VALU kernel
@@ -35,6 +35,10 @@
 //    LDS: deterministic, no atomics.
 //  * Lanes past the end of a row (last chunk) read the row's last 16 bytes
 //    and contribute zero; rows past N are read as row N-1 and not written.
+//
+// Affine codes ("Build a Blockwise INT4 Inference Engine", step 2): every
+// variant has an AFF form that also loads the group's zero point next to its
+// scale and expands codes to u - zp (codes_to_half_spread_zp, same op count).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -89,11 +93,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 }  // namespace
 
-template <int RW>
+template <int RW, bool AFF>
 __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int N, int K, int G, int group, int gsh,
-    float* __restrict__ y, Epilogue ep) {
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
+    int group, int gsh, float* __restrict__ y, Epilogue ep) {
   __shared__ float red[kGemvMaxChunks][RW];
   const int lane = threadIdx.x & 63;
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -120,9 +124,13 @@ __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
   // (scheduling barriers keep the three groups in this order: the compiler
   // would otherwise sink a load below the first use of an earlier one)
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t s[RW];
+  uint32_t s[RW], z[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) s[r] = (scales + (int64_t)row_of(r) * G)[gi];
+  if constexpr (AFF) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) z[r] = (zeros + (int64_t)row_of(r) * G)[gi];
+  }
   __builtin_amdgcn_sched_barrier(0);
   u32x4_t w[RW];
 #pragma unroll
@@ -153,7 +161,8 @@ __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half2_t hw[4];
-      codes_to_half_spread(w[r][i], hw);
+      if constexpr (AFF) codes_to_half_spread_zp(w[r][i], hw, zp_bias_lo(z[r]), zp_bias_hi(z[r]));
+      else codes_to_half_spread(w[r][i], hw);
 #pragma unroll
       for (int j = 0; j < 4; ++j) p = __builtin_amdgcn_fdot2(hw[j], __builtin_bit_cast(half2_t, xs[i][j]), p, false);
     }
@@ -194,11 +203,11 @@ __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
 // CM: column blocks (256 bytes) per row, >= ceil(K / 512). GS: min(gsh, 3)
 // (group = 32 << gsh), which bounds the groups per row and so the scale
 // entries each thread stages.
-template <int CM, int GS, int W>
+template <int CM, int GS, int W, bool AFF>
 __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int N, int K, int G, int group, int gsh,
-    float* __restrict__ y, Epilogue ep) {
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
+    int group, int gsh, float* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
   constexpr int NT = 64 * W, ROWS = 4 * W;     // threads, rows per block
@@ -209,6 +218,7 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   // branch here would make the compiler wait for every load at its join).
   __shared__ __attribute__((aligned(16))) uint32_t xsp[XPT * NT * 4];   // x, spread order
   __shared__ uint16_t ssh[SPT * NT];                                  // scales of the block's rows
+  __shared__ uint8_t zsh[AFF ? SPT * NT : 1];                         // their zero points
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -228,11 +238,19 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   // the block's rows' scales are contiguous from row n0 (rows past N: clamped)
   const uint16_t* sblk = scales + (int64_t)n0 * G;
   const int slast = (N - n0 < ROWS ? N - n0 : ROWS) * G - 1;
-  uint32_t sv[SPT];
+  uint32_t sv[SPT], zv[SPT];
 #pragma unroll
   for (int t = 0; t < SPT; ++t) {
     const int e = t * NT + tid;
     sv[t] = sblk[(uint32_t)(e < slast ? e : slast)];
+  }
+  if constexpr (AFF) {
+    const uint8_t* zblk = zeros + (int64_t)n0 * G;
+#pragma unroll
+    for (int t = 0; t < SPT; ++t) {
+      const int e = t * NT + tid;
+      zv[t] = zblk[(uint32_t)(e < slast ? e : slast)];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // Phase 2: the lane's 16 bytes of each column block of its row.
@@ -264,6 +282,7 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < SPT; ++t) {
     ssh[t * NT + tid] = (uint16_t)sv[t];
+    if constexpr (AFF) zsh[t * NT + tid] = (uint8_t)zv[t];
   }
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -274,11 +293,13 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   // gsh < 4 and b < 16 adds nothing when gsh >= 4). Lanes whose slice lies
   // past the row end read x units past K, which are zero.
   const uint16_t* srow = ssh + (4 * wave + j) * G + (b >> gsh);
+  const uint8_t* zrow = zsh + (AFF ? (4 * wave + j) * G + (b >> gsh) : 0);
   const uint32_t* xl = xsp + 16 * b;
   float acc = 0.0f;
   static_for<0, CM>([&](auto C_) {
     constexpr int c = decltype(C_)::value;
     const float sc = half_bits_to_float(srow[(16 * c) >> gsh]);
+    const uint32_t zp = AFF ? (uint32_t)zrow[(16 * c) >> gsh] : 0u;
     u32x4_t xa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4_t*>(xl + 256 * c + 4 * i);
@@ -287,7 +308,8 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half2_t hw[4];
-      codes_to_half_spread(w[c][i], hw);
+      if constexpr (AFF) codes_to_half_spread_zp(w[c][i], hw, zp_bias_lo(zp), zp_bias_hi(zp));
+      else codes_to_half_spread(w[c][i], hw);
       const half4_t b0 = __builtin_bit_cast(half4_t, u32x2v_t{__builtin_bit_cast(uint32_t, hw[0]), __builtin_bit_cast(uint32_t, hw[1])});
       const half4_t b1 = __builtin_bit_cast(half4_t, u32x2v_t{__builtin_bit_cast(uint32_t, hw[2]), __builtin_bit_cast(uint32_t, hw[3])});
       const half4_t a0 = __builtin_bit_cast(half4_t, u32x2v_t{xa[i].x, xa[i].y});
@@ -323,17 +345,17 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
 // issued as soon as row k has been consumed, with exact load counts.
 constexpr int kRowWaves = 8;                   // wavefronts per block
 
-template <int C>
+template <int C, bool AFF>
 __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int N, int K, int G, int group,
-    float* __restrict__ y, Epilogue ep) {
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
+    int group, float* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
   constexpr int P = 2;                         // rows in flight per wavefront
   constexpr int NT = 64 * kRowWaves;
   constexpr int XPT = (C * 256 + NT - 1) / NT; // 16-byte x units staged per thread
-  constexpr int LPR = 2 * C;                   // loads per row: C scales, C weight chunks
+  constexpr int LPR = (AFF ? 3 : 2) * C;       // loads per row: C scales, (C zero points,) C weight chunks
   __shared__ __attribute__((aligned(16))) uint32_t xsp[XPT * NT * 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -355,15 +377,20 @@ __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
   const int R = r0 < N ? (N - 1 - r0) / TW + 1 : 0;   // rows of this wavefront (<= 64)
 
   u32x4_t w[P][C];
-  uint32_t sc[P][C];
+  uint32_t sc[P][C], zc[P][C];
   // Loads of the wavefront's k-th row into slot `slot` (a constant at every
   // call); rows past the end read row N-1 and are not stored.
-  auto issue = [&](int k, int slot) {
+  auto issue = [&](int k, int slot) __attribute__((always_inline)) {
     const int r = r0 + k * TW < N ? r0 + k * TW : N - 1;
     const uint8_t* prow = packed + (int64_t)r * RB;
     const uint16_t* srow = scales + (int64_t)r * G;
 #pragma unroll
     for (int c = 0; c < C; ++c) sc[slot][c] = srow[sidx[c]];
+    if constexpr (AFF) {
+      const uint8_t* zrow = zeros + (int64_t)r * G;
+#pragma unroll
+      for (int c = 0; c < C; ++c) zc[slot][c] = zrow[sidx[c]];
+    }
 #pragma unroll
     for (int c = 0; c < C; ++c)
       w[slot][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(prow + (uint32_t)off[c]));
@@ -409,7 +436,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
   // loads below the barrier into the guard.
   int k0 = 0;
   do {
-    static_for<0, P>([&](auto S) {
+    static_for<0, P>([&](auto S) __attribute__((always_inline)) {
       constexpr int sl = decltype(S)::value;
       const int k = k0 + sl;
       wait_vmcnt_gemv<(P - 1) * LPR>();        // row k landed
@@ -418,10 +445,12 @@ __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t zlo = AFF ? zp_bias_lo(zc[sl][c]) : 0u, zhi = AFF ? zp_bias_hi(zc[sl][c]) : 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           half2_t hw[4];
-          codes_to_half_spread(w[sl][c][i], hw);
+          if constexpr (AFF) codes_to_half_spread_zp(w[sl][c][i], hw, zlo, zhi);
+          else codes_to_half_spread(w[sl][c][i], hw);
           const half4_t b0 = __builtin_bit_cast(half4_t, u32x2v_t{__builtin_bit_cast(uint32_t, hw[0]), __builtin_bit_cast(uint32_t, hw[1])});
           const half4_t b1 = __builtin_bit_cast(half4_t, u32x2v_t{__builtin_bit_cast(uint32_t, hw[2]), __builtin_bit_cast(uint32_t, hw[3])});
           const half4_t a0 = __builtin_bit_cast(half4_t, u32x2v_t{xa[c][i].x, xa[c][i].y});
@@ -459,24 +488,26 @@ const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
   return nullptr;
 }
 
-hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
-                              int64_t N, int64_t K, int64_t group, float* y, Epilogue ep,
-                              hipStream_t stream) {
+template <bool AFF>
+static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint16_t* scales,
+                          const uint8_t* zeros, int64_t N, int64_t K, int64_t group, float* y,
+                          Epilogue ep, hipStream_t stream) {
   const int G = (int)((K + group - 1) / group);
   int gsh = 0;                                                 // log2(group / 32), or -1
   while ((32ll << gsh) < group) ++gsh;
   if ((32ll << gsh) != group) gsh = -1;
-  const _Float16* xh0 = static_cast<const _Float16*>(x);
   const int chunks = (int)((K / 2 + 1023) / 1024);            // 1 KB chunks per row
-  if (N * (K / 2) >= (48ll << 20) && chunks <= 8) {
+  // (the AFF form with 8 chunks would exceed 256 VGPRs and spill: it takes the
+  // variants below)
+  if (N * (K / 2) >= (48ll << 20) && chunks <= (AFF ? 7 : 8)) {
     // Large matrix: row streaming. 256 blocks of 8 wavefronts (more if a
     // wavefront would own over 64 rows).
     int64_t blocks = 256;
     while ((N + blocks * kRowWaves - 1) / (blocks * kRowWaves) > 64) blocks *= 2;
     const dim3 grid((unsigned)blocks), block(64 * kRowWaves);
-#define INT4DQ_GEMV_ROWS(CC)                                                                     \
-  hipLaunchKernelGGL(matmul_gemv_rows_kernel<CC>, grid, block, 0, stream, xh0, packed, scales,  \
-                     (int)N, (int)K, G, (int)group, y, ep)
+#define INT4DQ_GEMV_ROWS(CC)                                                                      \
+  hipLaunchKernelGGL((matmul_gemv_rows_kernel<CC, AFF>), grid, block, 0, stream, xh0, packed,    \
+                     scales, zeros, (int)N, (int)K, G, (int)group, y, ep)
     switch (chunks) {
       case 1: INT4DQ_GEMV_ROWS(1); break;
       case 2: INT4DQ_GEMV_ROWS(2); break;
@@ -485,10 +516,12 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
       case 5: INT4DQ_GEMV_ROWS(5); break;
       case 6: INT4DQ_GEMV_ROWS(6); break;
       case 7: INT4DQ_GEMV_ROWS(7); break;
-      default: INT4DQ_GEMV_ROWS(8); break;
+      default:
+        if constexpr (!AFF) INT4DQ_GEMV_ROWS(8);
+        break;
     }
 #undef INT4DQ_GEMV_ROWS
-    return hipGetLastError();
+    return;
   }
   const int cols = (int)((K / 2 + 255) / 256);                // 256-byte column blocks per row
   if (cols <= 24 && gsh >= 0 && g_gemv_mfma) {
@@ -496,10 +529,12 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
     const dim3 g16((unsigned)((N + 4 * W - 1) / (4 * W))), b256(64 * W);
 #define INT4DQ_GEMV_MFMA(CMV)                                                                    \
   do {                                                                                          \
-    const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<CMV, 0, W> : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, W> \
-                    : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, W> : matmul_gemv_mfma_kernel<CMV, 3, W>;       \
-    hipLaunchKernelGGL(kern, g16, b256, 0, stream, xh0, packed, scales, (int)N, (int)K, G,     \
-                       (int)group, gsh, y, ep);                                                     \
+    const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<CMV, 0, W, AFF>                        \
+                    : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, W, AFF>                        \
+                    : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, W, AFF>                        \
+                               : matmul_gemv_mfma_kernel<CMV, 3, W, AFF>;                       \
+    hipLaunchKernelGGL(kern, g16, b256, 0, stream, xh0, packed, scales, zeros, (int)N, (int)K,  \
+                       G, (int)group, gsh, y, ep);                                              \
   } while (0)
     if (cols <= 2) INT4DQ_GEMV_MFMA(2);
     else if (cols <= 4) INT4DQ_GEMV_MFMA(4);
@@ -510,23 +545,26 @@ hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16
     else if (cols <= 22) INT4DQ_GEMV_MFMA(22);
     else INT4DQ_GEMV_MFMA(24);
 #undef INT4DQ_GEMV_MFMA
-    return hipGetLastError();
+    return;
   }
   // Rows per block: enough wavefronts in flight (about 4096) to keep every
   // memory channel busy, up to 4 rows per wavefront.
   const int64_t want = (int64_t)chunks * N / 4096;
   const int rw = want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
   const int64_t blocks = (N + rw - 1) / rw;
-  const _Float16* xh = static_cast<const _Float16*>(x);
   const dim3 grid((unsigned)blocks), block(64 * chunks);
-  if (rw == 8)
-    hipLaunchKernelGGL(matmul_gemv_kernel<8>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
-  else if (rw == 4)
-    hipLaunchKernelGGL(matmul_gemv_kernel<4>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
-  else if (rw == 2)
-    hipLaunchKernelGGL(matmul_gemv_kernel<2>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
-  else
-    hipLaunchKernelGGL(matmul_gemv_kernel<1>, grid, block, 0, stream, xh, packed, scales, (int)N, (int)K, G, (int)group, gsh, y, ep);
+  const auto kern = rw == 8 ? matmul_gemv_kernel<8, AFF> : rw == 4 ? matmul_gemv_kernel<4, AFF>
+                  : rw == 2 ? matmul_gemv_kernel<2, AFF> : matmul_gemv_kernel<1, AFF>;
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, packed, scales, zeros, (int)N, (int)K, G,
+                     (int)group, gsh, y, ep);
+}
+
+hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
+                              const uint8_t* zeros, int64_t N, int64_t K, int64_t group, float* y,
+                              Epilogue ep, hipStream_t stream) {
+  const _Float16* xh = static_cast<const _Float16*>(x);
+  if (zeros) launch_gemv_t<true>(xh, packed, scales, zeros, N, K, group, y, ep, stream);
+  else launch_gemv_t<false>(xh, packed, scales, zeros, N, K, group, y, ep, stream);
   return hipGetLastError();
 }
 

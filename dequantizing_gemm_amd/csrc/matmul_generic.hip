@@ -1,10 +1,13 @@
 // matmul_generic.hip -- general dequantizing matmul (any M, N, K, group,
-// alignment; binary32 or binary16 activations) on the vector ALUs.
+// alignment; binary32 or binary16 activations; symmetric or affine codes) on
+// the vector ALUs.
 //
 // Definition (drill page "Implement INT4 group quantization, nibble packing
 // and a dequantizing matmul", statement, int4_matmul):
 //   y[m, n] = sum over groups gi of scale[n, gi] * (sum over k in gi of x[m, k] * q[n, k])
-// i.e. x times the group's integer codes first, then the group's scale.
+// i.e. x times the group's integer codes first, then the group's scale. With
+// affine codes ("Build a Blockwise INT4 Inference Engine", step 2) the integer
+// weight is the unsigned code minus the group's zero point.
 //
 // One wavefront per output y[m, n]. The wavefront walks the groups of row n;
 // inside a group the 64 lanes stride over k (coalesced reads of x and of the
@@ -21,10 +24,11 @@ namespace int4dq {
 template <typename XT>
 __device__ __forceinline__ float load_x(const XT* p) { return (float)*p; }
 
-template <typename XT>
+template <typename XT, bool AFF>
 __global__ __launch_bounds__(256) void matmul_generic_kernel(
     const XT* __restrict__ x, int64_t M, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int64_t N, int64_t K, int64_t group, int64_t G,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
+    int64_t group, int64_t G,
     float* __restrict__ y, Epilogue ep) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t out = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -38,9 +42,11 @@ __global__ __launch_bounds__(256) void matmul_generic_kernel(
     const int64_t k0 = gi * group;
     const int64_t k1 = k0 + group < K ? k0 + group : K;
     float part = 0.0f;
+    const int zp = AFF ? (int)zeros[n * G + gi] : 0;
     for (int64_t k = k0 + lane; k < k1; k += kWave) {
       const uint32_t byte = pr[k >> 1];
-      const int q = sx4((byte >> (4 * (int)(k & 1))) & 0xFu);
+      const uint32_t u = (byte >> (4 * (int)(k & 1))) & 0xFu;
+      const int q = AFF ? (int)u - zp : sx4(u);
       part = __builtin_fmaf(load_x(xr + k), (float)q, part);
     }
     acc = __builtin_fmaf(half_bits_to_float(sr[gi]), part, acc);
@@ -50,18 +56,28 @@ __global__ __launch_bounds__(256) void matmul_generic_kernel(
   if (lane == 0) y[m * N + n] = ep(acc, n);
 }
 
-hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
-                                 const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                                 float* y, Epilogue ep, hipStream_t stream) {
+template <typename XT, bool AFF>
+static void launch_generic_t(const void* x, int64_t M, const uint8_t* packed,
+                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                             int64_t group, float* y, Epilogue ep, hipStream_t stream) {
   const int64_t G = (K + group - 1) / group;
   const int64_t outs = M * N;
   const dim3 grid((unsigned)((outs + 3) / 4)), block(256);
-  if (x_dtype == 0)
-    hipLaunchKernelGGL(matmul_generic_kernel<float>, grid, block, 0, stream,
-                       static_cast<const float*>(x), M, packed, scales, N, K, group, G, y, ep);
-  else
-    hipLaunchKernelGGL(matmul_generic_kernel<_Float16>, grid, block, 0, stream,
-                       static_cast<const _Float16*>(x), M, packed, scales, N, K, group, G, y, ep);
+  hipLaunchKernelGGL((matmul_generic_kernel<XT, AFF>), grid, block, 0, stream,
+                     static_cast<const XT*>(x), M, packed, scales, zeros, N, K, group, G, y, ep);
+}
+
+hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                                 const uint16_t* scales, const uint8_t* zeros, int64_t N,
+                                 int64_t K, int64_t group, float* y, Epilogue ep,
+                                 hipStream_t stream) {
+  if (x_dtype == 0) {
+    if (zeros) launch_generic_t<float, true>(x, M, packed, scales, zeros, N, K, group, y, ep, stream);
+    else launch_generic_t<float, false>(x, M, packed, scales, zeros, N, K, group, y, ep, stream);
+  } else {
+    if (zeros) launch_generic_t<_Float16, true>(x, M, packed, scales, zeros, N, K, group, y, ep, stream);
+    else launch_generic_t<_Float16, false>(x, M, packed, scales, zeros, N, K, group, y, ep, stream);
+  }
   return hipGetLastError();
 }
 

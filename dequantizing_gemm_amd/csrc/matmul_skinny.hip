@@ -38,6 +38,9 @@
 //    l mod 16): the integer-first order of the statement.
 //  * The waves' partial 16x16 tiles are summed through LDS at the end (the
 //    only barrier); no atomics, results are deterministic.
+//  * Affine codes ("Build a Blockwise INT4 Inference Engine", step 2): the AFF
+//    form loads each K-block's zero point next to its scale and expands the
+//    codes to u - zp (codes_to_half_*_zp, same op counts).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -73,11 +76,11 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 // RG > 1 (MR == 0 only): the block owns RG groups of 16 weight rows, and each
 // activation fragment a lane loads serves all RG of them, which divides the
 // activation traffic per weight byte by RG (x is re-read by every block).
-template <int KB, int WAVES, int U, int MR, int RG>
+template <int KB, int WAVES, int U, int MR, int RG, bool AFF>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int N, int K, int G, int kb_shift,
-    float* __restrict__ y, Epilogue ep) {
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
+    int kb_shift, float* __restrict__ y, Epilogue ep) {
   typedef typename WLoad<KB>::T wvec_t;
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
   constexpr int XB = RG > 1 ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
@@ -92,11 +95,13 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   const int xrow = col < M ? col : M - 1;                    // rows >= M: discarded
   const uint8_t* prow[RG];
   const uint16_t* srow[RG];
+  const uint8_t* zrow[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     const int nrow = (n0 + 16 * r + col < N) ? n0 + 16 * r + col : N - 1;   // tail rows: read, discard
     prow[r] = packed + (int64_t)nrow * (K >> 1) + h * (KB / 8);
     srow[r] = scales + (int64_t)nrow * G;
+    zrow[r] = AFF ? zeros + (int64_t)nrow * G : nullptr;
   }
   const int nkb = K / KB;
 
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   // issued after the (smaller) x staging loads, so that each K-block's
   // compute waits only for its own weights (loads return in order).
   wvec_t wv[RG][U];
-  uint32_t sraw[RG][U];
+  uint32_t sraw[RG][U], zraw[RG][U];
   // Straight-line, unconditional loads: a K-block index past the end is
   // clamped to the wave's last valid one (the value is loaded and ignored), so
   // no branch splits the sequence and no use is scheduled between the loads.
@@ -118,6 +123,15 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
         const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
         sraw[r][u] = srow[r][j >> kb_shift];
       }
+    if constexpr (AFF) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
+          zraw[r][u] = zrow[r][j >> kb_shift];
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -171,10 +185,12 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
         for (int i = 0; i < DW; ++i) a[i] = *reinterpret_cast<const half8_t*>(xa + u * KB + 8 * i);
         float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t zlo = AFF ? zp_bias_lo(zraw[0][u]) : 0u, zhi = AFF ? zp_bias_hi(zraw[0][u]) : 0u;
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
           half2_t hw[4];
-          codes_to_half_spread(word_at<KB>(wv[0][u], i), hw);
+          if constexpr (AFF) codes_to_half_spread_zp(word_at<KB>(wv[0][u], i), hw, zlo, zhi);
+          else codes_to_half_spread(word_at<KB>(wv[0][u], i), hw);
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], as_half8(hw), d, 0, 0, 0);
         }
         acc[0] += half_bits_to_float((uint16_t)sraw[0][u]) * d;
@@ -204,10 +220,12 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
           for (int r = 0; r < RG; ++r) {
             float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint32_t zb = AFF ? zp_bias_natural(zraw[r][u]) : 0u;
 #pragma unroll
             for (int i = 0; i < DW; ++i) {
               half2_t hw[4];
-              codes_to_half_natural(word_at<KB>(wv[r][u], i), hw);
+              if constexpr (AFF) codes_to_half_natural_zp(word_at<KB>(wv[r][u], i), hw, zb);
+              else codes_to_half_natural(word_at<KB>(wv[r][u], i), hw);
               d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[v][i], as_half8(hw), d, 0, 0, 0);
             }
             acc[r] += half_bits_to_float((uint16_t)sraw[r][u]) * d;
@@ -266,17 +284,20 @@ static size_t skinny_lds(int waves, int U, int KB, int MR, int RG = 1) {
 }
 constexpr size_t kSkinnyLdsMax = 64 * 1024;
 
-template <int KB, int WAVES, int U, int MR, int RG = 1>
+template <int KB, int WAVES, int U, int MR, int RG, bool AFF>
 static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
-  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG>), dim3((unsigned)((N + 16 * RG - 1) / (16 * RG))),
-                     dim3(WAVES * 64), skinny_lds(WAVES, U, KB, MR, RG), stream, x, M, packed, scales,
-                     N, K, G, kbs, y, ep);
+                      const uint8_t* zeros, int N, int K, int G, int kbs, float* y, Epilogue ep,
+                      hipStream_t stream) {
+  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG, AFF>),
+                     dim3((unsigned)((N + 16 * RG - 1) / (16 * RG))), dim3(WAVES * 64),
+                     skinny_lds(WAVES, U, KB, MR, RG), stream, x, M, packed, scales, zeros, N, K, G,
+                     kbs, y, ep);
 }
 
-template <int KB, int WAVES, int U>
+template <int KB, int WAVES, int U, bool AFF>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                       int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
+                       const uint8_t* zeros, int N, int K, int G, int kbs, float* y, Epilogue ep,
+                       hipStream_t stream) {
   const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
   // Direct x loads: as many row groups per block as keep about one block per
   // CU (x is re-read by every block, so fewer, wider blocks move less of it).
@@ -285,53 +306,65 @@ static void launch_one(const _Float16* x, int M, const uint8_t* packed, const ui
   constexpr bool rg4 = WAVES <= 8, rg2 = WAVES <= 8 || U <= 6;
   if constexpr (rg4) {
     if (M > 4 && N >= 256 * 16 * 4) {
-      launch_mr<KB, WAVES, U, 0, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+      launch_mr<KB, WAVES, U, 0, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
       return;
     }
   }
   if constexpr (rg2) {
     if (M > 4 && N >= 256 * 16 * 2) {
-      launch_mr<KB, WAVES, U, 0, 2>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+      launch_mr<KB, WAVES, U, 0, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
       return;
     }
   }
   if (M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax)
-    launch_mr<KB, WAVES, U, 0>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 0, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
   else if (MR == 1)
-    launch_mr<KB, WAVES, U, 1>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 1, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
   else if (MR == 2)
-    launch_mr<KB, WAVES, U, 2>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 2, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
   else
-    launch_mr<KB, WAVES, U, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 4, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
 }
 
 // Waves per block and K-blocks per wave for nkb K-blocks: the fewest waves
 // (<= 16) that cover K with at most 4 K-blocks each, else 16 waves with up to 8.
-template <int KB>
+template <int KB, bool AFF>
 static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      int N, int K, int G, int kbs, float* y, Epilogue ep, hipStream_t stream) {
+                      const uint8_t* zeros, int N, int K, int G, int kbs, float* y, Epilogue ep,
+                      hipStream_t stream) {
   const int nkb = K / KB;
-  if (nkb <= 4 * 2) launch_one<KB, 4, 2>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 4 * 4) launch_one<KB, 4, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 8 * 4) launch_one<KB, 8, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 16 * 4) launch_one<KB, 16, 4>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 16 * 6) launch_one<KB, 16, 6>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
-  else launch_one<KB, 16, 8>(x, M, packed, scales, N, K, G, kbs, y, ep, stream);
+  if (nkb <= 4 * 2) launch_one<KB, 4, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 4 * 4) launch_one<KB, 4, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 8 * 4) launch_one<KB, 8, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+  else if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+  else launch_one<KB, 16, 8, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+}
+
+template <bool AFF>
+static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
+                            const uint16_t* scales, const uint8_t* zeros, int N, int K, int G,
+                            int KB, int kbs, float* y, Epilogue ep, hipStream_t stream) {
+  switch (KB) {
+    case 128: launch_kb<128, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
+    case 64: launch_kb<64, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
+    default: launch_kb<32, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
+  }
 }
 
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
-                                const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                                float* y, Epilogue ep, hipStream_t stream) {
+                                const uint16_t* scales, const uint8_t* zeros, int64_t N,
+                                int64_t K, int64_t group, float* y, Epilogue ep,
+                                hipStream_t stream) {
   const int KB = skinny_kb(group);
   const int G = (int)((K + group - 1) / group);
   int kbs = 0;
   while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);
-  switch (KB) {
-    case 128: launch_kb<128>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, ep, stream); break;
-    case 64: launch_kb<64>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, ep, stream); break;
-    default: launch_kb<32>(xh, (int)M, packed, scales, (int)N, (int)K, G, kbs, y, ep, stream); break;
-  }
+  if (zeros)
+    launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, stream);
+  else
+    launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, stream);
   return hipGetLastError();
 }
 

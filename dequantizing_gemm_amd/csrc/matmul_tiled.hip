@@ -48,6 +48,10 @@
 //    (counts known at compile time; the loop is unrolled over two super-tiles
 //    so every stage and slot index is a constant), then one LDS-only barrier.
 //    Scheduling groups interleave LDS reads, code expansion and MFMAs.
+//  * Affine codes ("Build a Blockwise INT4 Inference Engine", step 2; the AFF
+//    form): each group's zero point is loaded with its scale, and its bias
+//    word (codes_to_half_natural_zp) is switched at the group boundary
+//    together with the running scale, so the codes expand to u - zp exactly.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -81,11 +85,11 @@ constexpr int kTileN = 128, kThreads = 256;
 // or 0: any power of two 2^gshift, decided at run time. TM: 32-row MFMA tiles
 // per wavefront in M (4, 2 or 1: block tiles of 256, 128 or 64 rows; the
 // smaller ones keep every CU busy when M is a few hundred rows).
-template <int BK, int SPG, int TM>
+template <int BK, int SPG, int TM, bool AFF>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int N, int K, int G, int gshift,
-    float* __restrict__ y, Epilogue ep) {
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
+    int gshift, float* __restrict__ y, Epilogue ep) {
   constexpr int BM = 64 * TM, BN = kTileN, WN = 2, NW = 4;
   constexpr int WMT = 32 * TM, WNT = 64, TN = 2;       // wave tile; TM x TN 32x32 MFMA tiles
   constexpr int KS = BK / 16;                  // MFMA k-steps per sub-step
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   constexpr auto s_used = [](int j) { return SPG == 0 || (((j % U) + U) % U) % SPG == 0; };
   constexpr auto group_loads = [s_used](int j) {
     const int jj = ((j % U) + U) % U;
-    return XDMA + (s_used(jj + D) ? TN : 0) + (jj % SUB == 0 ? WDMA : 0);
+    return XDMA + (s_used(jj + D) ? (AFF ? 2 : 1) * TN : 0) + (jj % SUB == 0 ? WDMA : 0);
   };
   // Sub-step t needs x(t+1) and s(t+1) (loaded by the group of t+1-D; the
   // super-tile of t+1 was loaded earlier still): the groups of t+2-D .. t-1 may
@@ -175,16 +179,19 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   }
   // --- scales of the lane's two output columns
   const uint16_t* ssrc[TN];
+  const uint8_t* zsrc[TN];
 #pragma unroll
   for (int b = 0; b < TN; ++b) {
     const int n = n0 + wn * WNT + b * 32 + c32;
     ssrc[b] = scales + (int64_t)(n < N ? n : N - 1) * G;
+    zsrc[b] = AFF ? zeros + (int64_t)(n < N ? n : N - 1) * G : nullptr;
   }
   const int spg_log = SPG == 0 ? gshift : SPG == 8 ? 3 : SPG == 4 ? 2 : SPG == 2 ? 1 : 0;
 
   // Loads (an index past the end is clamped to a valid address; such data is
   // never used).
   uint32_t sr[NXS][TN];                        // s(t) in slot t % NXS
+  uint32_t zr[NXS][TN];                        // zero points alike (AFF)
   auto issue_x = [&](int t, int stage) {
     const int tc = t < T ? t : T - 1;
     const char* base = xtile + (int64_t)tc * (2 * BK);
@@ -203,6 +210,10 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     asm volatile("" : "+s"(gi));
 #pragma unroll
     for (int b = 0; b < TN; ++b) sr[slot][b] = ssrc[b][gi];
+    if constexpr (AFF) {
+#pragma unroll
+      for (int b = 0; b < TN; ++b) zr[slot][b] = zsrc[b][gi];
+    }
   };
   auto issue_w = [&](int st, int slot) {
 #pragma unroll
@@ -239,8 +250,9 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
   float srun[TN];
+  uint32_t zb[TN];                             // bias word of the current group (AFF)
 #pragma unroll
-  for (int b = 0; b < TN; ++b) srun[b] = 0.0f;
+  for (int b = 0; b < TN; ++b) srun[b] = 0.0f, zb[b] = 0u;
 
   half8_t af[TM];                              // A fragments of the next k-step
   uint32_t wp[TN][KS];                         // packed words of the current sub-step
@@ -266,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
       half2_t hw[4];
-      codes_to_half_natural(w[b][s], hw);
+      if constexpr (AFF) codes_to_half_natural_zp(w[b][s], hw, zb[b]);
+      else codes_to_half_natural(w[b][s], hw);
       bf[b] = as_half8(hw);
     }
   };
@@ -303,11 +316,16 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   // Sub-step 0 opens the first group: the running scale starts at s(0) (a
   // zero scale leaves it 0, and the accumulator is still 0).
 #pragma unroll
-  for (int b = 0; b < TN; ++b) srun[b] = half_bits_to_float((uint16_t)sr[0][b]);
+  for (int b = 0; b < TN; ++b) {
+    srun[b] = half_bits_to_float((uint16_t)sr[0][b]);
+    if constexpr (AFF) zb[b] = zp_bias_natural(zr[0][b]);
+  }
 
   // Sub-step t = t0 + J, t0 a multiple of U: x stage J % NXS, W slot
   // (J / SUB) % WS, scale slot J % NXS, all compile-time.
-  auto substep = [&](auto J_, int t) {
+  // (always inlined: an outlined sub-step would take the DMA destinations and
+  // the register arrays by reference, i.e. through scratch memory)
+  auto substep = [&](auto J_, int t) __attribute__((always_inline)) {
     constexpr int J = decltype(J_)::value;
     constexpr int ws = (J / SUB) % WS, xs = J % NXS;
     constexpr int J1 = (J + 1) % U;
@@ -367,6 +385,10 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
           // groups' part, far inside the tolerance); srun = 0 gives 0.
           ratio[b] = live ? srun[b] * __builtin_amdgcn_rcpf(sn) : 1.0f;
           srun[b] = live ? sn : srun[b];
+          // The zero-point slot of t+1 holds t+1's group wherever a group can
+          // open there (every sub-step when SPG is decided at run time), so
+          // the bias is switched without a condition.
+          if constexpr (AFF && (SPG == 0 || (J + 1) % SPG == 0)) zb[b] = zp_bias_natural(zr[xs1][b]);
         }
         if constexpr (SPG == 0 || (J + 1) % SPG == 0) {
 #pragma unroll
@@ -437,8 +459,8 @@ const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* 
 }
 
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
-                               const uint16_t* scales, int64_t N, int64_t K, int64_t group,
-                               float* y, Epilogue ep, hipStream_t stream) {
+                               const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                               int64_t group, float* y, Epilogue ep, hipStream_t stream) {
   const int BK = tiled_bk(group);
   const int G = (int)((K + group - 1) / group);
   if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
@@ -451,15 +473,18 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
   int gs = 0;                                  // group = BK << gs
   while ((int64_t(BK) << gs) < group) ++gs;
-#define INT4DQ_TILED_PICK(TMV)                                                                  \
-  (BK == 32 ? matmul_tiled_kernel<32, 1, TMV>                                                   \
-   : gs == 0 ? matmul_tiled_kernel<64, 1, TMV> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV>     \
-   : gs == 2 ? matmul_tiled_kernel<64, 4, TMV> : gs == 3 ? matmul_tiled_kernel<64, 8, TMV>      \
-             : matmul_tiled_kernel<64, 0, TMV>)
-  const auto kernel = TM == 4 ? INT4DQ_TILED_PICK(4) : TM == 2 ? INT4DQ_TILED_PICK(2) : INT4DQ_TILED_PICK(1);
+#define INT4DQ_TILED_PICK(TMV, A)                                                                     \
+  (BK == 32 ? matmul_tiled_kernel<32, 1, TMV, A>                                                      \
+   : gs == 0 ? matmul_tiled_kernel<64, 1, TMV, A> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV, A>     \
+   : gs == 2 ? matmul_tiled_kernel<64, 4, TMV, A> : gs == 3 ? matmul_tiled_kernel<64, 8, TMV, A>      \
+             : matmul_tiled_kernel<64, 0, TMV, A>)
+  const auto kernel =
+      zeros ? (TM == 4 ? INT4DQ_TILED_PICK(4, true) : TM == 2 ? INT4DQ_TILED_PICK(2, true) : INT4DQ_TILED_PICK(1, true))
+            : (TM == 4 ? INT4DQ_TILED_PICK(4, false) : TM == 2 ? INT4DQ_TILED_PICK(2, false) : INT4DQ_TILED_PICK(1, false));
 #undef INT4DQ_TILED_PICK
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     static_cast<const _Float16*>(x), (int)M, packed, scales, (int)N, (int)K, G, gs, y, ep);
+                     static_cast<const _Float16*>(x), (int)M, packed, scales, zeros, (int)N, (int)K, G,
+                     gs, y, ep);
   return hipGetLastError();
 }
 

@@ -170,6 +170,59 @@ int int4_matmul_path(const void *x, int x_dtype, int64_t M, const uint8_t *packe
                      const float *bias, int act, float *y, int path, void *stream);
 
 /*
+ * Affine (asymmetric) variant of the codes ("Build a Blockwise INT4 Inference
+ * Engine", step 2: per-group scale and zero point, codes in [0, 15], value
+ * (q - zp) * scale; "Quantizing a Language Model From Scratch", affine
+ * quantization: the zero point makes 0.0 exact).
+ *
+ * int4_quantize_affine:
+ *   w       in : [N, K] binary32 weights.
+ *   packed  out: [N, ceil(K/2)] bytes, the same nibble layout as int4_quantize
+ *                but each nibble an UNSIGNED code u in [0, 15]; an odd K leaves
+ *                a zero high nibble in the row's last byte.
+ *   scales  out: [N, G] binary16 bit patterns, zeros out: [N, G] bytes.
+ *   For group gi of row n, with lo = min(min w, 0) and hi = max(max w, 0)
+ *   over the group (the range always contains zero):
+ *     scale = binary16((hi - lo) / 15)   subtraction and division in binary32
+ *     zp    = clip(round(-lo / scale), 0, 15)
+ *     u     = clip(round(w / scale + zp), 0, 15)
+ *   where every division uses the stored scale widened to binary32 and is a
+ *   correctly rounded binary32 division, w / scale + zp is formed exactly,
+ *   and round() is ties-to-even. A group whose scale is 0 gets zp = 0 and
+ *   codes 0. Bit-exact with a CPU reference computing the same.
+ *   Errors: EINVAL if N, K or group < 1, a pointer is NULL, or sizes overflow.
+ */
+int int4_quantize_affine(const float *w, int64_t N, int64_t K, int64_t group,
+                         uint8_t *packed, uint16_t *scales, uint8_t *zeros, void *stream);
+
+/*
+ * int4_dequantize for affine codes: out[n, k] = (u[n, k] - zp) * scale of
+ * element k's group, in out_dtype (binary32: exact; binary16: the exact value
+ * rounded to nearest even). zeros: [N, G] bytes, values in [0, 15], as written
+ * by int4_quantize_affine with the same K and group.
+ * Errors: those of int4_dequantize, and EINVAL if zeros is NULL.
+ */
+int int4_dequantize_affine(const uint8_t *packed, const uint16_t *scales, const uint8_t *zeros,
+                           int64_t N, int64_t K, int64_t group, int out_dtype, void *out,
+                           void *stream);
+
+/*
+ * int4_matmul_path for affine codes:
+ *   y = act(x @ dequantize_affine(W).T + bias), one group at a time: x times
+ *   the group's integer weights u - zp first, then the group's scale.
+ * Same arguments, layouts, arithmetic and errors as int4_matmul_path, plus
+ * zeros ([N, G] bytes in [0, 15], as written by int4_quantize_affine; EINVAL if
+ * NULL). Each output is within 2e-3 * sum_k |x[m,k] * (u[n,k] - zp) * scale|
+ * (+ 2^-22 * |y| with a bias) of act applied to the exact result. Every
+ * kernel path (INT4DQ_PATH_*) takes affine codes under the same conditions as
+ * symmetric ones.
+ */
+int int4_matmul_affine(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                       const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                       int64_t group, const float *bias, int act, float *y, int path,
+                       void *stream);
+
+/*
  * Kernel that int4_matmul would run for these arguments (an INT4DQ_PATH_*
  * other than AUTO), or -1 if the arguments are invalid. Enqueues nothing.
  */

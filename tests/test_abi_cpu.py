@@ -29,7 +29,8 @@ def _declared():
 def test_header_declares_the_abi():
     assert _declared() == sorted(["int4_num_groups", "int4_packed_bytes", "int4_quantize", "int4_dequantize",
                                   "int4_unpack", "int4_matmul", "int4_matmul_ex", "int4_matmul_path",
-                                  "int4_matmul_select", "int4_last_error"])
+                                  "int4_matmul_select", "int4_last_error", "int4_quantize_affine",
+                                  "int4_dequantize_affine", "int4_matmul_affine"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -129,6 +130,39 @@ def test_matmul_m0_is_noop_and_bad_path():
     assert dq.lib.int4_matmul_ex(FAKE, 1, 4, FAKE, FAKE, 16, 256, 128, None, 5, FAKE, None) == dq.EINVAL
     assert "activation" in dq.lib.int4_last_error().decode()
     assert dq.lib.int4_matmul_ex(None, 1, 0, FAKE, FAKE, 16, 256, 128, FAKE, 1, None, None) == dq.OK
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((FAKE, 0, 8, 4, FAKE, FAKE, FAKE, None), "N and K"),
+    ((FAKE, 4, 8, 0, FAKE, FAKE, FAKE, None), "group"),
+    ((FAKE, 4, 8, 4, FAKE, FAKE, None, None), "non-NULL"),
+    ((None, 4, 8, 4, FAKE, FAKE, FAKE, None), "non-NULL"),
+    ((FAKE, 2 ** 62, 8, 4, FAKE, FAKE, FAKE, None), "overflow"),
+])
+def test_quantize_affine_rejects(args, needle):
+    dq = _lib()
+    assert dq.lib.int4_quantize_affine(*args) == dq.EINVAL
+    msg = dq.lib.int4_last_error().decode()
+    assert needle in msg and "int4_quantize_affine" in msg
+
+
+def test_affine_entry_points_reject():
+    dq = _lib()
+    L = dq.lib
+    # zeros must be given
+    assert L.int4_dequantize_affine(FAKE, FAKE, None, 4, 8, 4, 0, FAKE, None) == dq.EINVAL
+    assert "zeros" in L.int4_last_error().decode()
+    assert L.int4_matmul_affine(FAKE, 1, 4, FAKE, FAKE, None, 16, 256, 128, None, 0, FAKE, 0, None) == dq.EINVAL
+    assert "zeros" in L.int4_last_error().decode()
+    # the rest of the validation is the symmetric entry points'
+    assert L.int4_dequantize_affine(FAKE, FAKE, FAKE, 4, 8, 4, 2, FAKE, None) == dq.EINVAL
+    assert "out_dtype" in L.int4_last_error().decode()
+    assert L.int4_matmul_affine(FAKE, 1, 4, FAKE, FAKE, FAKE, 16, 256, 128, None, 5, FAKE, 0, None) == dq.EINVAL
+    assert "activation" in L.int4_last_error().decode()
+    assert L.int4_matmul_affine(FAKE, 1, 4, FAKE, FAKE, FAKE, 16, 256, 128, None, 0, FAKE, 9, None) == dq.EINVAL
+    assert "path" in L.int4_last_error().decode()
+    assert L.int4_matmul_affine(FAKE, 7, 4, FAKE, FAKE, FAKE, 16, 256, 128, None, 0, FAKE, 0, None) == dq.EINVAL
+    assert L.int4_matmul_affine(None, 1, 0, FAKE, FAKE, FAKE, 16, 256, 128, None, 0, None, 0, None) == dq.OK
 
 
 def test_kernel_selection_rules():
