@@ -14,10 +14,16 @@ namespace int4dq {
 struct Epilogue {
   const float* bias;   // [N] binary32, or nullptr
   int relu;            // 0 or 1
-  __device__ __forceinline__ float operator()(float v, int64_t n) const {
-    if (bias) v += bias[n];
+  // The bias of output column n (0 when there is none), read once per column
+  // by kernels that store many outputs of one column: the compiler cannot
+  // prove that the stores to y leave the bias unchanged, and would otherwise
+  // reload it before every store.
+  __device__ __forceinline__ float column(int64_t n) const { return bias ? bias[n] : 0.0f; }
+  __device__ __forceinline__ float apply(float v, float b) const {
+    if (bias) v += b;
     return relu ? (v > 0.0f ? v : 0.0f) : v;
   }
+  __device__ __forceinline__ float operator()(float v, int64_t n) const { return apply(v, column(n)); }
 };
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,

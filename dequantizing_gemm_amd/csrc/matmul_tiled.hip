@@ -9,17 +9,19 @@
 // the fusion boundary); here they exist only as exact fp16 integer codes in
 // registers, one MFMA k-step at a time.
 //
-// Block tile 256 (rows of x) x 128 (weight rows), 256 threads = 2 x 2
-// wavefronts, one per SIMD, each owning 128 x 64 outputs as 4 x 2 tiles of
-// v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 VGPRs); for a few hundred
-// rows of x the block keeps 128 or 64 rows (2 x 2 or 1 x 2 tiles per
-// wavefront) so that the grid still covers every CU. Larger wave tiles
-// than 64 x 64 halve the LDS bytes read per MFMA, which bounds this kernel.
+// Block tile 128 (rows of x) x 256 (weight rows), 256 threads = 4 wavefronts
+// side by side along N, one per SIMD, each owning 128 x 64 outputs as 4 x 2
+// tiles of v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 VGPRs). The
+// global -> LDS bytes per sub-step are 16 KB of x and 8 KB of packed weights
+// (a 256 x 128 tile moves 32 KB + 4 KB for the same flops). For a few hundred
+// rows of x the block is 128 x 128 or 64 x 128 instead (2 x 2 wavefronts of
+// 2 x 2 or 1 x 2 tiles) so that the grid still covers the CUs. Wave tiles
+// larger than 64 x 64 halve the LDS bytes read per MFMA.
 // K advances in sub-steps of BK = min(group, 64) codes:
-//  * x tiles [256 x BK] fp16 go global -> LDS by DMA (global_load_lds, 16 B
+//  * x tiles [BM x BK] fp16 go global -> LDS by DMA (global_load_lds, 16 B
 //    per lane, no VGPRs) into a 4-stage ring, three sub-steps ahead.
 //  * Packed weights go global -> LDS by DMA too, in "super-tiles" of 128 B
-//    (256 codes) of each of the block's 128 rows: eight lanes cover a full
+//    (256 codes) of each of the block's weight rows: eight lanes cover a full
 //    128-byte line, and a 2-slot ring loads super-tile j+1 while j is used.
 //  * Each wavefront reads its own packed words (one 16-byte read per 32-column
 //    tile per sub-step) and expands them to exact fp16 codes in registers
@@ -78,19 +80,21 @@ __device__ __forceinline__ void unroll(F&& f) {
   }
 }
 
-constexpr int kTileN = 128, kThreads = 256;
+constexpr int kThreads = 256;
 }  // namespace
 
 // BK: codes per sub-step (32 or 64). SPG: sub-steps per group (1, 2, 4 or 8),
 // or 0: any power of two 2^gshift, decided at run time. TM: 32-row MFMA tiles
-// per wavefront in M (4, 2 or 1: block tiles of 256, 128 or 64 rows; the
-// smaller ones keep every CU busy when M is a few hundred rows).
-template <int BK, int SPG, int TM, bool AFF>
+// per wavefront in M (4, 2 or 1). WN: wavefronts side by side along N (4:
+// block tile 32 TM x 256; 2: 2 x 2 wavefronts, block tile 64 TM x 128). The
+// launcher uses (TM, WN) = (4, 4), (2, 2) and (1, 2).
+template <int BK, int SPG, int TM, bool AFF, int WN>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
     int gshift, float* __restrict__ y, Epilogue ep) {
-  constexpr int BM = 64 * TM, BN = kTileN, WN = 2, NW = 4;
+  constexpr int NW = 4, BM = 32 * TM * (NW / WN), BN = 64 * WN;
+  static_assert(WN == 2 || WN == 4, "wave layout");
   constexpr int WMT = 32 * TM, WNT = 64, TN = 2;       // wave tile; TM x TN 32x32 MFMA tiles
   constexpr int KS = BK / 16;                  // MFMA k-steps per sub-step
   constexpr int PIECES = BK / 8;               // 16-byte pieces per x row per stage
@@ -426,16 +430,30 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 
   // Epilogue: apply the last running scale; lane l holds column l%32 and rows
   // 8*(i/4) + 4*(l/32) + (i%4) of each 32x32 tile (register i).
+  // A block tile inside y (every block but the last row and column of
+  // tiles) stores without per-output bounds checks.
+  const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int b = 0; b < TN; ++b) {
     const int n = n0 + wn * WNT + b * 32 + c32;
+    const float bn = ep.column(n < N ? n : N - 1);
+    if (full) {
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < TM; ++a)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (m < M && n < N) y[(int64_t)m * N + n] = ep(acc[a][b][i] * srun[b], n);
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          y[(int64_t)m * N + n] = ep.apply(acc[a][b][i] * srun[b], bn);
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (m < M && n < N) y[(int64_t)m * N + n] = ep.apply(acc[a][b][i] * srun[b], bn);
+        }
+    }
   }
 }
 
@@ -464,23 +482,28 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   const int BK = tiled_bk(group);
   const int G = (int)((K + group - 1) / group);
   if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
-  const int64_t ntiles = (N + kTileN - 1) / kTileN;
-  // Block rows: 256 unless that leaves most CUs idle (a few hundred rows of x);
-  // then 128 or 64, whichever first gives about one block per CU.
-  int TM = 4;
-  while (TM > 1 && ((M + 64 * TM - 1) / (64 * TM)) * ntiles < 200) TM /= 2;
-  const int64_t blocks = ((M + 64 * TM - 1) / (64 * TM)) * ntiles;
+  // Block tile: the largest of 128 x 256, 128 x 128 and 64 x 128 (rows of x
+  // x weight rows) that still gives the grid 160 blocks or more. Measured on
+  // the 7B-class shapes: 128 x 256 is 7-8% faster than 256 x 128 (x is read
+  // from L2 half as often), and a grid of about 170 large tiles beats one of
+  // 340 smaller ones (M = 512 on [11008, 4096]: 60 us against 78), but 128
+  // blocks on 256 CUs do not.
+  auto grid_of = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  const int TM = grid_of(128, 256) >= 160 ? 4 : grid_of(128, 128) >= 160 ? 2 : 1;
+  const int64_t blocks = TM == 4 ? grid_of(128, 256) : grid_of(32 * TM * 2, 128);
   if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
   int gs = 0;                                  // group = BK << gs
   while ((int64_t(BK) << gs) < group) ++gs;
-#define INT4DQ_TILED_PICK(TMV, A)                                                                     \
-  (BK == 32 ? matmul_tiled_kernel<32, 1, TMV, A>                                                      \
-   : gs == 0 ? matmul_tiled_kernel<64, 1, TMV, A> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV, A>     \
-   : gs == 2 ? matmul_tiled_kernel<64, 4, TMV, A> : gs == 3 ? matmul_tiled_kernel<64, 8, TMV, A>      \
-             : matmul_tiled_kernel<64, 0, TMV, A>)
+#define INT4DQ_TILED_PICK(TMV, A, W)                                                                     \
+  (BK == 32 ? matmul_tiled_kernel<32, 1, TMV, A, W>                                                      \
+   : gs == 0 ? matmul_tiled_kernel<64, 1, TMV, A, W> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV, A, W>   \
+   : gs == 2 ? matmul_tiled_kernel<64, 4, TMV, A, W> : gs == 3 ? matmul_tiled_kernel<64, 8, TMV, A, W>    \
+             : matmul_tiled_kernel<64, 0, TMV, A, W>)
   const auto kernel =
-      zeros ? (TM == 4 ? INT4DQ_TILED_PICK(4, true) : TM == 2 ? INT4DQ_TILED_PICK(2, true) : INT4DQ_TILED_PICK(1, true))
-            : (TM == 4 ? INT4DQ_TILED_PICK(4, false) : TM == 2 ? INT4DQ_TILED_PICK(2, false) : INT4DQ_TILED_PICK(1, false));
+      zeros ? (TM == 4 ? INT4DQ_TILED_PICK(4, true, 4) : TM == 2 ? INT4DQ_TILED_PICK(2, true, 2)
+                                                                 : INT4DQ_TILED_PICK(1, true, 2))
+            : (TM == 4 ? INT4DQ_TILED_PICK(4, false, 4) : TM == 2 ? INT4DQ_TILED_PICK(2, false, 2)
+                                                                  : INT4DQ_TILED_PICK(1, false, 2));
 #undef INT4DQ_TILED_PICK
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const _Float16*>(x), (int)M, packed, scales, zeros, (int)N, (int)K, G,
