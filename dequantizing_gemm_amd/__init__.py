@@ -17,7 +17,8 @@ Inference Engine", step 2):
     quantize_int4_affine(w, group=128) -> (packed, scales, zeros, K)
 
 whose ``zeros`` are passed to dequantize_int4 / int4_matmul / int4_matmul_path
-as ``zeros=``.
+as ``zeros=``; int4_linear(...) is one layer with fp16 or fp32 output, and
+``dequantizing_gemm_amd.linear`` holds the Int4Linear module built on it.
 
 All tensors are torch tensors on the GPU; torch provides the device memory and
 the stream (work is enqueued on ``torch.cuda.current_stream()``). Every step of
@@ -33,7 +34,7 @@ import os
 import torch
 
 __all__ = ["quantize_int4", "quantize_int4_affine", "unpack_int4", "dequantize_int4", "int4_matmul",
-           "int4_matmul_path", "matmul_select",
+           "int4_matmul_path", "int4_linear", "matmul_select",
            "num_groups", "packed_bytes", "lib", "LIB_PATH", "Int4Error", "PATHS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4dq.so")
@@ -42,6 +43,7 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 X_F32, X_F16 = 0, 1
 ACT_NONE, ACT_RELU = 0, 1
 OUT_F32, OUT_F16 = 0, 1
+Y_F32, Y_F16 = 0, 1
 PATHS = {"auto": 0, "generic": 1, "skinny": 2, "tiled": 3, "gemv": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
@@ -61,6 +63,7 @@ SIGNATURES = {
     "int4_dequantize_affine": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "int4_matmul_affine": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp,
                                   _int, _vp]),
+    "int4_linear": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp]),
     "int4_last_error": (ctypes.c_char_p, []),
 }
 
@@ -261,6 +264,38 @@ def int4_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: 
     with the engine page's epilogue act(... + bias) when bias or relu is given,
     and affine codes when zeros is given."""
     return int4_matmul_path(x, packed, scales, K, group, "auto", out, bias, relu, zeros)
+
+
+def int4_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
+                group: int = 128, *, zeros: torch.Tensor | None = None,
+                bias: torch.Tensor | None = None, relu: bool = False,
+                out_dtype: torch.dtype = torch.float32,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """One layer: y [M, N] = act(x @ dequantize(W).T + bias) written as
+    ``out_dtype`` (float32, or float16 rounded to nearest even), symmetric or
+    (with ``zeros``) affine codes; the kernel is chosen as int4_matmul does."""
+    M, N, xd = _matmul_args(x, packed, scales, K, group)
+    if out_dtype not in (torch.float32, torch.float16):
+        raise ValueError(f"out_dtype must be float32 or float16 (got {out_dtype})")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _gpu(out, "out", out_dtype)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out shape {tuple(out.shape)} != {(M, N)}")
+    bptr = None
+    if bias is not None:
+        _gpu(bias, "bias", torch.float32, ndim=1)
+        if bias.shape[0] != N or bias.device != x.device:
+            raise ValueError(f"bias must be [N] = [{N}] on {x.device}")
+        bptr = bias.data_ptr()
+    zp = _zeros_ptr(zeros, N, K, group, x.device)
+    with torch.cuda.device(x.device):
+        rc = lib.int4_linear(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), zp, N, K,
+                             group, bptr, ACT_RELU if relu else ACT_NONE, out.data_ptr(),
+                             Y_F16 if out_dtype == torch.float16 else Y_F32, _stream(x))
+    _raise(rc, "int4_linear")
+    return out
 
 
 def matmul_select(x, packed, scales, K, group=128) -> str:

@@ -43,7 +43,7 @@ int hip_status(hipError_t e, const char* what) {
 
 // Shared validation of int4_matmul arguments; on success fills the sizes.
 int check_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
-                 const uint16_t* scales, int64_t N, int64_t K, int64_t group, const float* y) {
+                 const uint16_t* scales, int64_t N, int64_t K, int64_t group, const void* y) {
   if (M < 0) return fail(INT4DQ_EINVAL, "int4_matmul: M must be >= 0 (got %lld)", (long long)M);
   if (N < 1 || K < 1) return fail(INT4DQ_EINVAL, "int4_matmul: N and K must be >= 1 (got N=%lld K=%lld)", (long long)N, (long long)K);
   if (group < 1) return fail(INT4DQ_EINVAL, "int4_matmul: group must be >= 1 (got %lld)", (long long)group);
@@ -59,11 +59,11 @@ int check_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
   return INT4DQ_OK;
 }
 
-// Shared body of int4_matmul_path and int4_matmul_affine (zeros: nullptr for
-// symmetric codes).
+// Shared body of every matmul entry point (zeros: nullptr for symmetric
+// codes; y of y_dtype).
 int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                const float* bias, int act, float* y, int path, void* stream);
+                const float* bias, int act, void* y, int y_dtype, int path, void* stream);
 
 int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t N,
                 int64_t K, int64_t group) {
@@ -154,7 +154,7 @@ int int4_matmul_path(const void* x, int x_dtype, int64_t M, const uint8_t* packe
                      const uint16_t* scales, int64_t N, int64_t K, int64_t group,
                      const float* bias, int act, float* y, int path, void* stream) {
   return matmul_impl("int4_matmul_path", x, x_dtype, M, packed, scales, nullptr, N, K, group, bias,
-                     act, y, path, stream);
+                     act, y, INT4DQ_Y_F32, path, stream);
 }
 
 int int4_matmul_affine(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
@@ -162,7 +162,14 @@ int int4_matmul_affine(const void* x, int x_dtype, int64_t M, const uint8_t* pac
                        int64_t group, const float* bias, int act, float* y, int path, void* stream) {
   if (!zeros) return fail(INT4DQ_EINVAL, "int4_matmul_affine: zeros must be non-NULL");
   return matmul_impl("int4_matmul_affine", x, x_dtype, M, packed, scales, zeros, N, K, group, bias,
-                     act, y, path, stream);
+                     act, y, INT4DQ_Y_F32, path, stream);
+}
+
+int int4_linear(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
+                const float* bias, int act, void* y, int y_dtype, void* stream) {
+  return matmul_impl("int4_linear", x, x_dtype, M, packed, scales, zeros, N, K, group, bias, act, y,
+                     y_dtype, INT4DQ_PATH_AUTO, stream);
 }
 
 int int4_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
@@ -194,12 +201,14 @@ namespace {
 
 int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                const float* bias, int act, float* y, int path, void* stream) {
+                const float* bias, int act, void* y, int y_dtype, int path, void* stream) {
   int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
   if (rc != INT4DQ_OK) return rc;
   if (act != INT4DQ_ACT_NONE && act != INT4DQ_ACT_RELU)
     return fail(INT4DQ_EINVAL, "%s: unknown activation %d", fn, act);
-  const int4dq::Epilogue ep{bias, act == INT4DQ_ACT_RELU ? 1 : 0};
+  if (y_dtype != INT4DQ_Y_F32 && y_dtype != INT4DQ_Y_F16)
+    return fail(INT4DQ_EINVAL, "%s: unknown y_dtype %d", fn, y_dtype);
+  const int4dq::Epilogue ep{bias, act == INT4DQ_ACT_RELU ? 1 : 0, y_dtype == INT4DQ_Y_F16 ? 1 : 0};
   if (path < INT4DQ_PATH_AUTO || path > INT4DQ_PATH_GEMV)
     return fail(INT4DQ_EINVAL, "%s: unknown path %d", fn, path);
   if (M == 0) return ok();

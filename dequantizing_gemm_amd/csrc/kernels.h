@@ -10,10 +10,13 @@ namespace int4dq {
 
 // Output step of every matmul kernel (the engine page's fused kernel and
 // layer forward): y = act(v + bias[n]) with act = identity or ReLU; ReLU keeps
-// a value greater than zero and gives +0 otherwise.
+// a value greater than zero and gives +0 otherwise. y is binary32, or binary16
+// (the fp32 result rounded to nearest even) so that a following layer can take
+// it as its activations without a conversion pass.
 struct Epilogue {
   const float* bias;   // [N] binary32, or nullptr
   int relu;            // 0 or 1
+  int half;            // 1: y is binary16, 0: binary32
   // The bias of output column n (0 when there is none), read once per column
   // by kernels that store many outputs of one column: the compiler cannot
   // prove that the stores to y leave the bias unchanged, and would otherwise
@@ -24,6 +27,12 @@ struct Epilogue {
     return relu ? (v > 0.0f ? v : 0.0f) : v;
   }
   __device__ __forceinline__ float operator()(float v, int64_t n) const { return apply(v, column(n)); }
+  // y[i] = act(v + bias[n]) in y's precision.
+  __device__ __forceinline__ void store(void* y, int64_t i, float v, int64_t n) const {
+    const float r = apply(v, column(n));
+    if (half) static_cast<_Float16*>(y)[i] = (_Float16)r;
+    else static_cast<float*>(y)[i] = r;
+  }
 };
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
@@ -45,25 +54,25 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, cons
 
 hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                                  const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                                 float* y, Epilogue ep, hipStream_t stream);
+                                 void* y, Epilogue ep, hipStream_t stream);
 
 // nullptr if the kernel takes these arguments, else the reason it does not.
 const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
                                       const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                                float* y, Epilogue ep, hipStream_t stream);
+                                void* y, Epilogue ep, hipStream_t stream);
 
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
                                     const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
-                              const uint8_t* zeros, int64_t N, int64_t K, int64_t group, float* y, Epilogue ep,
+                              const uint8_t* zeros, int64_t N, int64_t K, int64_t group, void* y, Epilogue ep,
                               hipStream_t stream);
 
 const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
                                      int64_t K, int64_t group);
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
                                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                               float* y, Epilogue ep, hipStream_t stream);
+                               void* y, Epilogue ep, hipStream_t stream);
 
 }  // namespace int4dq

@@ -97,7 +97,7 @@ template <int RW, bool AFF>
 __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
-    int group, int gsh, float* __restrict__ y, Epilogue ep) {
+    int group, int gsh, void* __restrict__ y, Epilogue ep) {
   __shared__ float red[kGemvMaxChunks][RW];
   const int lane = threadIdx.x & 63;
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
   if ((int)threadIdx.x < RW && n0 + (int)threadIdx.x < N) {
     float sum = 0.0f;
     for (int cc = 0; cc < nchunks; ++cc) sum += red[cc][threadIdx.x];
-    y[n0 + threadIdx.x] = ep(sum, n0 + threadIdx.x);
+    ep.store(y, n0 + threadIdx.x, sum, n0 + threadIdx.x);
   }
 }
 
@@ -207,7 +207,7 @@ template <int CM, int GS, int W, bool AFF>
 __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
-    int group, int gsh, float* __restrict__ y, Epilogue ep) {
+    int group, int gsh, void* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
   constexpr int NT = 64 * W, ROWS = 4 * W;     // threads, rows per block
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   // Sum the 16 slices (lanes 4b+j, b = 0..15) of each of the 4 rows.
 #pragma unroll
   for (int off = 4; off < 64; off <<= 1) acc += __shfl_xor(acc, off);
-  if (b == 0 && n0 + 4 * wave + j < N) y[n0 + 4 * wave + j] = ep(acc, n0 + 4 * wave + j);
+  if (b == 0 && n0 + 4 * wave + j < N) ep.store(y, n0 + 4 * wave + j, acc, n0 + 4 * wave + j);
 }
 
 // ---------------------------------------------------------------------------
@@ -349,7 +349,7 @@ template <int C, bool AFF>
 __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
-    int group, float* __restrict__ y, Epilogue ep) {
+    int group, void* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
   constexpr int P = 2;                         // rows in flight per wavefront
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void matmul_gemv_rows_kernel(
     k0 += P;
   } while (k0 < R);
   wait_vmcnt_gemv<0>();
-  if (lane < R) y[r0 + lane * TW] = ep(yv, r0 + lane * TW);
+  if (lane < R) ep.store(y, r0 + lane * TW, yv, r0 + lane * TW);
 }
 
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
@@ -490,7 +490,7 @@ const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
 
 template <bool AFF>
 static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint16_t* scales,
-                          const uint8_t* zeros, int64_t N, int64_t K, int64_t group, float* y,
+                          const uint8_t* zeros, int64_t N, int64_t K, int64_t group, void* y,
                           Epilogue ep, hipStream_t stream) {
   const int G = (int)((K + group - 1) / group);
   int gsh = 0;                                                 // log2(group / 32), or -1
@@ -560,7 +560,7 @@ static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint
 }
 
 hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
-                              const uint8_t* zeros, int64_t N, int64_t K, int64_t group, float* y,
+                              const uint8_t* zeros, int64_t N, int64_t K, int64_t group, void* y,
                               Epilogue ep, hipStream_t stream) {
   const _Float16* xh = static_cast<const _Float16*>(x);
   if (zeros) launch_gemv_t<true>(xh, packed, scales, zeros, N, K, group, y, ep, stream);

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void matmul_generic_kernel(
     const XT* __restrict__ x, int64_t M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
     int64_t group, int64_t G,
-    float* __restrict__ y, Epilogue ep) {
+    void* __restrict__ y, Epilogue ep) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t out = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (out >= M * N) return;                        // whole wavefronts only
@@ -53,13 +53,13 @@ __global__ __launch_bounds__(256) void matmul_generic_kernel(
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) y[m * N + n] = ep(acc, n);
+  if (lane == 0) ep.store(y, m * N + n, acc, n);
 }
 
 template <typename XT, bool AFF>
 static void launch_generic_t(const void* x, int64_t M, const uint8_t* packed,
                              const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                             int64_t group, float* y, Epilogue ep, hipStream_t stream) {
+                             int64_t group, void* y, Epilogue ep, hipStream_t stream) {
   const int64_t G = (K + group - 1) / group;
   const int64_t outs = M * N;
   const dim3 grid((unsigned)((outs + 3) / 4)), block(256);
@@ -69,7 +69,7 @@ static void launch_generic_t(const void* x, int64_t M, const uint8_t* packed,
 
 hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                                  const uint16_t* scales, const uint8_t* zeros, int64_t N,
-                                 int64_t K, int64_t group, float* y, Epilogue ep,
+                                 int64_t K, int64_t group, void* y, Epilogue ep,
                                  hipStream_t stream) {
   if (x_dtype == 0) {
     if (zeros) launch_generic_t<float, true>(x, M, packed, scales, zeros, N, K, group, y, ep, stream);

@@ -80,7 +80,7 @@ template <int KB, int WAVES, int U, int MR, int RG, bool AFF>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
-    int kb_shift, float* __restrict__ y, Epilogue ep) {
+    int kb_shift, void* __restrict__ y, Epilogue ep) {
   typedef typename WLoad<KB>::T wvec_t;
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
   constexpr int XB = RG > 1 ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) s += red[(w * RG + r) * 256 + src];
     const int n = n0 + 16 * r + nn;
-    if (n < N) y[(int64_t)m * N + n] = ep(s, n);
+    if (n < N) ep.store(y, (int64_t)m * N + n, s, n);
   }
 }
 
@@ -286,7 +286,7 @@ constexpr size_t kSkinnyLdsMax = 64 * 1024;
 
 template <int KB, int WAVES, int U, int MR, int RG, bool AFF>
 static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      const uint8_t* zeros, int N, int K, int G, int kbs, float* y, Epilogue ep,
+                      const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
                       hipStream_t stream) {
   hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG, AFF>),
                      dim3((unsigned)((N + 16 * RG - 1) / (16 * RG))), dim3(WAVES * 64),
@@ -296,7 +296,7 @@ static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uin
 
 template <int KB, int WAVES, int U, bool AFF>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                       const uint8_t* zeros, int N, int K, int G, int kbs, float* y, Epilogue ep,
+                       const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
                        hipStream_t stream) {
   const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
   // Direct x loads: as many row groups per block as keep about one block per
@@ -330,7 +330,7 @@ static void launch_one(const _Float16* x, int M, const uint8_t* packed, const ui
 // (<= 16) that cover K with at most 4 K-blocks each, else 16 waves with up to 8.
 template <int KB, bool AFF>
 static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      const uint8_t* zeros, int N, int K, int G, int kbs, float* y, Epilogue ep,
+                      const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
                       hipStream_t stream) {
   const int nkb = K / KB;
   if (nkb <= 4 * 2) launch_one<KB, 4, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
@@ -344,7 +344,7 @@ static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uin
 template <bool AFF>
 static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
                             const uint16_t* scales, const uint8_t* zeros, int N, int K, int G,
-                            int KB, int kbs, float* y, Epilogue ep, hipStream_t stream) {
+                            int KB, int kbs, void* y, Epilogue ep, hipStream_t stream) {
   switch (KB) {
     case 128: launch_kb<128, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
     case 64: launch_kb<64, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
@@ -354,7 +354,7 @@ static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
 
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, const uint8_t* zeros, int64_t N,
-                                int64_t K, int64_t group, float* y, Epilogue ep,
+                                int64_t K, int64_t group, void* y, Epilogue ep,
                                 hipStream_t stream) {
   const int KB = skinny_kb(group);
   const int G = (int)((K + group - 1) / group);

@@ -92,7 +92,7 @@ template <int BK, int SPG, int TM, bool AFF, int WN>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
-    int gshift, float* __restrict__ y, Epilogue ep) {
+    int gshift, void* __restrict__ y, Epilogue ep) {
   constexpr int NW = 4, BM = 32 * TM * (NW / WN), BN = 64 * WN;
   static_assert(WN == 2 || WN == 4, "wave layout");
   constexpr int WMT = 32 * TM, WNT = 64, TN = 2;       // wave tile; TM x TN 32x32 MFMA tiles
@@ -431,30 +431,36 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   // Epilogue: apply the last running scale; lane l holds column l%32 and rows
   // 8*(i/4) + 4*(l/32) + (i%4) of each 32x32 tile (register i).
   // A block tile inside y (every block but the last row and column of
-  // tiles) stores without per-output bounds checks.
+  // tiles) stores without per-output bounds checks; the output precision is
+  // one branch for the whole tile.
   const bool full = m0 + BM <= M && n0 + BN <= N;
+  auto store_all = [&](auto* yt) __attribute__((always_inline)) {
+    typedef std::remove_pointer_t<decltype(yt)> T;
 #pragma unroll
-  for (int b = 0; b < TN; ++b) {
-    const int n = n0 + wn * WNT + b * 32 + c32;
-    const float bn = ep.column(n < N ? n : N - 1);
-    if (full) {
+    for (int b = 0; b < TN; ++b) {
+      const int n = n0 + wn * WNT + b * 32 + c32;
+      const float bn = ep.column(n < N ? n : N - 1);
+      if (full) {
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+        for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          y[(int64_t)m * N + n] = ep.apply(acc[a][b][i] * srun[b], bn);
-        }
-    } else {
+          for (int i = 0; i < 16; ++i) {
+            const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i] * srun[b], bn);
+          }
+      } else {
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+        for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (m < M && n < N) y[(int64_t)m * N + n] = ep.apply(acc[a][b][i] * srun[b], bn);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (m < M && n < N) yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i] * srun[b], bn);
+          }
+      }
     }
-  }
+  };
+  if (ep.half) store_all(static_cast<_Float16*>(y));
+  else store_all(static_cast<float*>(y));
 }
 
 // BK for a group size, or 0 if the kernel does not take it (group / BK must be
@@ -478,7 +484,7 @@ const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* 
 
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
                                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                               int64_t group, float* y, Epilogue ep, hipStream_t stream) {
+                               int64_t group, void* y, Epilogue ep, hipStream_t stream) {
   const int BK = tiled_bk(group);
   const int G = (int)((K + group - 1) / group);
   if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;

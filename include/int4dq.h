@@ -1,7 +1,9 @@
 /*
  * int4dq.h -- C ABI of the MI355X (gfx950) INT4 group-quantization library:
  * block-wise symmetric INT4 weight quantization with two's-complement nibble
- * packing, unpacking, and the fused dequantizing matmul.
+ * packing, unpacking, and the fused dequantizing matmul; also dequantization,
+ * the bias/ReLU epilogue, affine (zero-point) codes and a linear-layer call
+ * with binary16 output.
  *
  * The three operations are the ones stated on the drill page "Implement INT4
  * group quantization, nibble packing and a dequantizing matmul"
@@ -53,6 +55,10 @@ extern "C" {
 /* Element type of the output of int4_dequantize. */
 #define INT4DQ_OUT_F32 0       /* IEEE binary32 */
 #define INT4DQ_OUT_F16 1       /* IEEE binary16 */
+
+/* Element type of y in int4_linear (the other matmul calls write binary32). */
+#define INT4DQ_Y_F32 0         /* IEEE binary32 */
+#define INT4DQ_Y_F16 1         /* IEEE binary16: the binary32 result rounded to nearest even */
 
 /* Output activation of int4_matmul_ex / int4_matmul_path. */
 #define INT4DQ_ACT_NONE 0      /* y = v */
@@ -221,6 +227,25 @@ int int4_matmul_affine(const void *x, int x_dtype, int64_t M, const uint8_t *pac
                        const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
                        int64_t group, const float *bias, int act, float *y, int path,
                        void *stream);
+
+/*
+ * One quantized linear layer, the engine page's layer forward ("Build a
+ * Blockwise INT4 Inference Engine": y = act(x @ W_dq.T + b)), in the output
+ * precision the next layer takes:
+ *   y = act(x @ dequantize(W).T + bias), written as y_dtype.
+ *   zeros   in : NULL for symmetric codes (int4_quantize), else the [N, G] zero
+ *                points of affine codes (int4_quantize_affine).
+ *   y       out: [M, N] of y_dtype. INT4DQ_Y_F32 as int4_matmul_ex /
+ *                int4_matmul_affine; INT4DQ_Y_F16 rounds that binary32 result to
+ *                nearest even (overflowing to infinity past 65504), so a chain
+ *                of layers passes fp16 activations with no conversion pass.
+ * The kernel is chosen as int4_matmul does. Other arguments, layouts and
+ * errors as int4_matmul_affine (zeros may be NULL), plus EINVAL for an
+ * unknown y_dtype.
+ */
+int int4_linear(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                int64_t group, const float *bias, int act, void *y, int y_dtype, void *stream);
 
 /*
  * Kernel that int4_matmul would run for these arguments (an INT4DQ_PATH_*

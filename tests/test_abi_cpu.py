@@ -30,7 +30,7 @@ def test_header_declares_the_abi():
     assert _declared() == sorted(["int4_num_groups", "int4_packed_bytes", "int4_quantize", "int4_dequantize",
                                   "int4_unpack", "int4_matmul", "int4_matmul_ex", "int4_matmul_path",
                                   "int4_matmul_select", "int4_last_error", "int4_quantize_affine",
-                                  "int4_dequantize_affine", "int4_matmul_affine"])
+                                  "int4_dequantize_affine", "int4_matmul_affine", "int4_linear"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -163,6 +163,20 @@ def test_affine_entry_points_reject():
     assert "path" in L.int4_last_error().decode()
     assert L.int4_matmul_affine(FAKE, 7, 4, FAKE, FAKE, FAKE, 16, 256, 128, None, 0, FAKE, 0, None) == dq.EINVAL
     assert L.int4_matmul_affine(None, 1, 0, FAKE, FAKE, FAKE, 16, 256, 128, None, 0, None, 0, None) == dq.OK
+
+
+def test_linear_rejects():
+    dq = _lib()
+    L = dq.lib
+    args = [FAKE, 1, 4, FAKE, FAKE, None, 16, 256, 128, None, 0, FAKE]
+    assert L.int4_linear(*args, 2, None) == dq.EINVAL
+    assert "y_dtype" in L.int4_last_error().decode()
+    assert L.int4_linear(*args[:10], 3, FAKE, 0, None) == dq.EINVAL
+    assert "activation" in L.int4_last_error().decode()
+    bad_x = list(args)
+    bad_x[1] = 5
+    assert L.int4_linear(*bad_x, 0, None) == dq.EINVAL
+    assert L.int4_linear(None, 1, 0, FAKE, FAKE, None, 16, 256, 128, None, 0, None, 1, None) == dq.OK
 
 
 def test_kernel_selection_rules():
