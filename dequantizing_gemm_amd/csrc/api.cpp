@@ -68,7 +68,9 @@ int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uin
 int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t N,
                 int64_t K, int64_t group) {
   if (!int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_GEMV;
-  if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_SKINNY;
+  if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group) &&
+      int4dq::matmul_skinny_preferred(M, N))
+    return INT4DQ_PATH_SKINNY;
   if (!int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group)) return INT4DQ_PATH_TILED;
   return INT4DQ_PATH_GENERIC;
 }

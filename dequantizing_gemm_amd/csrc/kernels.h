@@ -59,6 +59,8 @@ hipError_t launch_matmul_generic(const void* x, int x_dtype, int64_t M, const ui
 // nullptr if the kernel takes these arguments, else the reason it does not.
 const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
                                       const uint8_t* packed, int64_t N, int64_t K, int64_t group);
+// Whether the automatic choice takes the skinny kernel for a supported shape.
+bool matmul_skinny_preferred(int64_t M, int64_t N);
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
                                 void* y, Epilogue ep, hipStream_t stream);

@@ -1,4 +1,4 @@
-// matmul_skinny.hip -- dequantizing matmul for few activation rows (M <= 16,
+// matmul_skinny.hip -- dequantizing matmul for few activation rows (M <= 64,
 // binary16 x; M = 1 normally takes matmul_gemv.hip) on gfx950: a
 // weight-streaming kernel bound by HBM bandwidth.
 //
@@ -9,7 +9,7 @@
 // architecture overview: the weights are never expanded to full precision in
 // memory; the takeaways put the bottleneck in memory bandwidth.)
 //
-// At M <= 16 every packed byte is used 2*M times, far below the machine's
+// At M <= 64 every packed byte is used 2*M times, far below the machine's
 // flop/byte balance. The kernel streams the packed weights once and keeps
 // each block's critical path short, because at these sizes (1-120 MB per
 // call) a launch is a single round of loads and its latency chain, not a
@@ -76,23 +76,24 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 // RG > 1 (MR == 0 only): the block owns RG groups of 16 weight rows, and each
 // activation fragment a lane loads serves all RG of them, which divides the
 // activation traffic per weight byte by RG (x is re-read by every block).
-template <int KB, int WAVES, int U, int MR, int RG, bool AFF>
+// MT > 1 (MR == 0 only): M up to 16 MT rows of x as MT tiles of 16; each
+// expanded code word feeds MT MFMAs, one per tile.
+template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
     int kb_shift, void* __restrict__ y, Epilogue ep) {
   typedef typename WLoad<KB>::T wvec_t;
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
-  constexpr int XB = RG > 1 ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
-  static_assert(MR == 0 || RG == 1, "row groups with direct x loads only");
+  constexpr int XB = (RG > 1 || MT > 1) ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
+  static_assert(MR == 0 || (RG == 1 && MT == 1), "row groups and row tiles with direct x loads only");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float* red = reinterpret_cast<float*>(lds);                  // [WAVES][RG][64][4]
+  float* red = reinterpret_cast<float*>(lds);                  // [WAVES][RG][MT][64][4]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * 16 * RG;
-  const int xrow = col < M ? col : M - 1;                    // rows >= M: discarded
   const uint8_t* prow[RG];
   const uint16_t* srow[RG];
   const uint8_t* zrow[RG];
@@ -141,9 +142,11 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
       }
   };
 
-  float4_t acc[RG];
+  float4_t acc[RG][MT];
 #pragma unroll
-  for (int r = 0; r < RG; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[r][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (MR > 0) {
     // Wave-private region: [MR][U][KB] halves, spread order within each 8.
     _Float16* xw = reinterpret_cast<_Float16*>(lds + WAVES * 64 * 4 * sizeof(float)) +
@@ -193,22 +196,29 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
           else codes_to_half_spread(word_at<KB>(wv[0][u], i), hw);
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], as_half8(hw), d, 0, 0, 0);
         }
-        acc[0] += half_bits_to_float((uint16_t)sraw[0][u]) * d;
+        acc[0][0] += half_bits_to_float((uint16_t)sraw[0][u]) * d;
       }
     }
   } else {
     // Activation fragments straight from global memory (L2 hits), natural
     // order, in batches of XB K-blocks to bound register use.
-    const _Float16* xp = x + (int64_t)xrow * K + h * (KB / 4) + wave * KB;
+    const _Float16* xp[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int r = 16 * t + col < M ? 16 * t + col : M - 1;
+      xp[t] = x + (int64_t)r * K + h * (KB / 4) + wave * KB;
+    }
     load_w();
-    half8_t xa[XB][DW];
+    half8_t xa[MT][XB][DW];
     auto load_x = [&](int b) {
 #pragma unroll
       for (int v = 0; v < XB; ++v)
         if (b + v < U && wave + (b + v) * WAVES < nkb)
 #pragma unroll
-          for (int i = 0; i < DW; ++i)
-            xa[v][i] = *reinterpret_cast<const half8_t*>(xp + (b + v) * (WAVES * KB) + 8 * i);
+          for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < DW; ++i)
+              xa[t][v][i] = *reinterpret_cast<const half8_t*>(xp[t] + (b + v) * (WAVES * KB) + 8 * i);
     };
 #pragma unroll
     for (int b = 0; b < U; b += XB) {
@@ -219,16 +229,23 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
         if (u < U && wave + u * WAVES < nkb) {
 #pragma unroll
           for (int r = 0; r < RG; ++r) {
-            float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+            float4_t d[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             const uint32_t zb = AFF ? zp_bias_natural(zraw[r][u]) : 0u;
 #pragma unroll
             for (int i = 0; i < DW; ++i) {
               half2_t hw[4];
               if constexpr (AFF) codes_to_half_natural_zp(word_at<KB>(wv[r][u], i), hw, zb);
               else codes_to_half_natural(word_at<KB>(wv[r][u], i), hw);
-              d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[v][i], as_half8(hw), d, 0, 0, 0);
+              const half8_t bw = as_half8(hw);
+#pragma unroll
+              for (int t = 0; t < MT; ++t)
+                d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], bw, d[t], 0, 0, 0);
             }
-            acc[r] += half_bits_to_float((uint16_t)sraw[r][u]) * d;
+            const float sc = half_bits_to_float((uint16_t)sraw[r][u]);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[r][t] += sc * d[t];
           }
         }
       }
@@ -238,15 +255,18 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   // Sum the waves' 16x16 partial tiles. Lane l holds rows 4*(l/16) + i of column l%16.
 #pragma unroll
   for (int r = 0; r < RG; ++r)
-    *reinterpret_cast<float4_t*>(red + ((wave * RG + r) * 64 + lane) * 4) = acc[r];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      *reinterpret_cast<float4_t*>(red + (((wave * RG + r) * MT + t) * 64 + lane) * 4) = acc[r][t];
   __syncthreads();
   for (int t = tid; t < 16 * M * RG; t += WAVES * 64) {
     const int r = t / (16 * M), rem = t - r * 16 * M;
     const int m = rem >> 4, nn = rem & 15;
-    const int src = ((m >> 2) * 16 + nn) * 4 + (m & 3);
+    const int tm = m >> 4, mm = m & 15;                       // row tile, row inside it
+    const int src = ((mm >> 2) * 16 + nn) * 4 + (mm & 3);
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s += red[(w * RG + r) * 256 + src];
+    for (int w = 0; w < WAVES; ++w) s += red[((w * RG + r) * MT + tm) * 256 + src];
     const int n = n0 + 16 * r + nn;
     if (n < N) ep.store(y, (int64_t)m * N + n, s, n);
   }
@@ -267,37 +287,78 @@ const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
                                       const uint8_t* packed, int64_t N, int64_t K,
                                       int64_t group) {
   if (x_dtype != 1) return "skinny kernel takes binary16 activations only";
-  if (M > 16) return "skinny kernel takes M <= 16";
+  if (M > 64) return "skinny kernel takes M <= 64";
   const int KB = skinny_kb(group);
   if (KB == 0) return "skinny kernel takes group 32, 64 or 128 times a power of two";
   if (K % KB != 0) return "skinny kernel needs K to be a multiple of min(group, 128)";
   if (K / KB > kSkinnyMaxKB) return "skinny kernel takes K <= 128 * min(group, 128)";
+  // (four row tiles and eight K-blocks per wave do not fit 16 wavefronts' registers)
+  if (M > 32 && K / KB > 16 * 6) return "skinny kernel takes M <= 32 when K > 96 * min(group, 128)";
   if (N >= (1ll << 30)) return "skinny kernel needs N below 2^30";
   if ((uintptr_t)x % 16 || (uintptr_t)packed % 16) return "skinny kernel needs 16-byte aligned x and packed";
   return nullptr;
 }
 
+// Whether the skinny kernel should take a shape it supports. Up to 16 rows
+// always. For 17-64 rows its time grows with N times the number of 16-row
+// tiles, while the tiled kernel's is flat there (its grid of 64 x 128 tiles is
+// small and each block walks all of K); measured on MI355X, the skinny kernel
+// is faster while N * ceil(M / 16) <= 32768: [4096,4096] M = 64 20 us against
+// 29, [11008,4096] M = 32 25 us against 33, but [11008,4096] M = 64 42 us
+// against 30 and [28672,8192] M = 17 99 us against 83.
+bool matmul_skinny_preferred(int64_t M, int64_t N) {
+  return M <= 16 || N * ((M + 15) / 16) <= 32768;
+}
+
 // Bytes of LDS a launch uses: the reduction buffer, plus the wave-private x
 // slices of MR rows when they are staged.
-static size_t skinny_lds(int waves, int U, int KB, int MR, int RG = 1) {
-  return (size_t)waves * RG * 64 * 4 * sizeof(float) + (size_t)waves * MR * U * KB * 2;
+static size_t skinny_lds(int waves, int U, int KB, int MR, int RG = 1, int MT = 1) {
+  return (size_t)waves * RG * MT * 64 * 4 * sizeof(float) + (size_t)waves * MR * U * KB * 2;
 }
 constexpr size_t kSkinnyLdsMax = 64 * 1024;
 
-template <int KB, int WAVES, int U, int MR, int RG, bool AFF>
+template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1>
 static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                       const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
                       hipStream_t stream) {
-  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG, AFF>),
+  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG, AFF, MT>),
                      dim3((unsigned)((N + 16 * RG - 1) / (16 * RG))), dim3(WAVES * 64),
-                     skinny_lds(WAVES, U, KB, MR, RG), stream, x, M, packed, scales, zeros, N, K, G,
+                     skinny_lds(WAVES, U, KB, MR, RG, MT), stream, x, M, packed, scales, zeros, N, K, G,
                      kbs, y, ep);
+}
+
+// 17 <= M <= 64: MT = 2 or 4 row tiles, direct x loads. Every block re-reads
+// its rows' share of x (M/(4 RG) bytes of x per byte of weights), so the
+// block takes as many row groups as its registers allow while the grid keeps
+// about one block per CU.
+template <int KB, int WAVES, int U, bool AFF, int MT>
+static void launch_tiles(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
+                         const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
+                         hipStream_t stream) {
+  constexpr bool rg2 = WAVES <= 8;
+  if constexpr (rg2) {
+    if (N >= 256 * 16 * 2) {
+      launch_mr<KB, WAVES, U, 0, 2, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+      return;
+    }
+  }
+  launch_mr<KB, WAVES, U, 0, 1, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
 }
 
 template <int KB, int WAVES, int U, bool AFF>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                        const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
                        hipStream_t stream) {
+  if constexpr (WAVES < 16 || U <= 6) {           // refused by matmul_skinny_unsupported otherwise
+    if (M > 32) {
+      launch_tiles<KB, WAVES, U, AFF, 4>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+      return;
+    }
+  }
+  if (M > 16) {
+    launch_tiles<KB, WAVES, U, AFF, 2>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+    return;
+  }
   const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
   // Direct x loads: as many row groups per block as keep about one block per
   // CU (x is re-read by every block, so fewer, wider blocks move less of it).
@@ -358,6 +419,7 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 hipStream_t stream) {
   const int KB = skinny_kb(group);
   const int G = (int)((K + group - 1) / group);
+  if (M > 32 && K / KB > 16 * 6) return hipErrorInvalidValue;   // refused by matmul_skinny_unsupported
   int kbs = 0;
   while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);

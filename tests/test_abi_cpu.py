@@ -182,15 +182,21 @@ def test_linear_rejects():
 def test_kernel_selection_rules():
     """Which kernel the library picks (host logic only, no launch)."""
     dq = _lib()
-    sel = lambda xd, M, K, g, x=0x1000, p=0x2000: dq.lib.int4_matmul_select(
-        ctypes.c_void_p(x), xd, M, ctypes.c_void_p(p), FAKE, 64, K, g, FAKE)
+    sel = lambda xd, M, K, g, x=0x1000, p=0x2000, N=64: dq.lib.int4_matmul_select(
+        ctypes.c_void_p(x), xd, M, ctypes.c_void_p(p), FAKE, N, K, g, FAKE)
     P = dq.PATHS
     assert sel(1, 1, 4096, 128) == P["gemv"] and sel(1, 16, 4096, 128) == P["skinny"]
     assert sel(1, 2, 4096, 128) == P["skinny"] and sel(1, 1, 11008, 128) == P["gemv"]
     assert sel(1, 1, 768, 32) == P["gemv"] and sel(1, 1, 768, 64) == P["gemv"]
     assert sel(1, 1, 4096, 16) == P["generic"]                 # group not a multiple of 32
     assert sel(1, 1, 65536, 128) == P["tiled"]                 # K beyond the gemv and skinny kernels
-    assert sel(1, 17, 4096, 128) == P["tiled"] and sel(1, 2048, 11008, 128) == P["tiled"]
+    assert sel(1, 2048, 11008, 128) == P["tiled"] and sel(1, 65, 4096, 128) == P["tiled"]
+    # 17-64 rows: skinny while N * ceil(M / 16) <= 32768, else tiled
+    assert sel(1, 17, 4096, 128) == P["skinny"] and sel(1, 64, 4096, 128, N=4096) == P["skinny"]
+    assert sel(1, 32, 4096, 128, N=11008) == P["skinny"] and sel(1, 33, 4096, 128, N=11008) == P["tiled"]
+    assert sel(1, 17, 8192, 128, N=28672) == P["tiled"] and sel(1, 16, 8192, 128, N=28672) == P["skinny"]
+    # four row tiles do not take more than 96 K-blocks
+    assert sel(1, 40, 16384, 128) == P["tiled"] and sel(1, 20, 16384, 128) == P["skinny"]
     assert sel(1, 4, 768, 64) == P["skinny"] and sel(1, 4, 768, 32) == P["skinny"]
     assert sel(0, 4, 256, 128) == P["generic"]                 # binary32 x
     assert sel(1, 3, 301, 128) == P["generic"]                 # odd K

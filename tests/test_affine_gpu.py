@@ -145,6 +145,8 @@ MM = [
     (8200, 1024, 64, 9, "skinny"),    # two row groups per block
     (16400, 2048, 128, 7, "skinny"),  # four row groups per block
     (300, 4096, 128, 16, "skinny"),
+    (300, 4096, 128, 40, "skinny"),   # four 16-row tiles
+    (8200, 1024, 64, 24, "skinny"),   # two tiles, two row groups per block
     # tiled: 64-, 128- and 256-row block tiles (TM 1, 2, 4) over every group
     # cadence (BK 32; a group every 1, 2, 4, 8 sub-steps; decided at run time)
     (200, 1024, 32, 40, "tiled"),

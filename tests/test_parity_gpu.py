@@ -279,7 +279,12 @@ def test_matmul_configs(dq, key, case, M):
 @pytest.mark.parametrize("N,K,g,M", [(200, 768, 64, 1), (200, 768, 32, 5), (48, 4096, 128, 16),
                                      (136, 1024, 256, 3), (50, 512, 128, 200), (300, 1024, 128, 130),
                                      (129, 256, 32, 257), (64, 2048, 64, 100),
-                                     (16400, 2048, 128, 7), (8200, 1024, 64, 9), (9000, 8192, 128, 16)])
+                                     (16400, 2048, 128, 7), (8200, 1024, 64, 9), (9000, 8192, 128, 16),
+                                     # 17-64 rows: two or four 16-row tiles in the skinny kernel, one or
+                                     # two row groups per block, up to the largest K each form takes
+                                     (200, 768, 32, 24), (300, 4096, 128, 64), (8200, 1024, 64, 40),
+                                     (16400, 2048, 128, 20), (300, 12288, 128, 48), (64, 16384, 128, 30),
+                                     (77, 2048, 128, 33)])
 def test_matmul_kernels_agree(dq, N, K, g, M):
     """Every kernel that takes a shape matches the oracle on it (ragged M and N tails)."""
     w = np.random.default_rng(N + K).normal(0, 0.02, size=(N, K)).astype(np.float32)
@@ -287,7 +292,8 @@ def test_matmul_kernels_agree(dq, N, K, g, M):
     pr, sr, _ = oracle.quantize_int4(w, g)
     pd, sd, xd = dev(pr), dev(sr), dev(x)
     for path in ("generic", "skinny", "tiled", "gemv"):
-        if (path == "skinny" and M > 16) or (path == "gemv" and M != 1):
+        if (path == "skinny" and (M > 64 or (M > 32 and K // min(g, 128) > 96))) or \
+                (path == "gemv" and M != 1):
             continue
         say(f"case: kernel {path} N={N} K={K} g={g} M={M}")
         y = host(dq.int4_matmul_path(xd, pd, sd, K, g, path))
@@ -350,6 +356,7 @@ def test_matmul_gemv_rows_one_hot_exact(dq):
 @pytest.mark.parametrize("N,K,g,M,path", [(300, 1024, 128, 1, "gemv"), (200, 768, 32, 1, "gemv"),
                                           (12300, 8224, 32, 1, "gemv"), (77, 4096, 96, 1, "gemv"),
                                           (200, 768, 64, 5, "skinny"), (48, 4096, 128, 16, "skinny"),
+                                          (300, 4096, 128, 64, "skinny"), (8200, 1024, 64, 24, "skinny"),
                                           (300, 1024, 128, 130, "tiled"), (129, 256, 32, 600, "tiled"),
                                           (640, 2048, 128, 520, "tiled"), (10880, 256, 64, 300, "tiled"),
                                           (4096, 256, 128, 1600, "tiled"), (40, 1000, 7, 6, "generic")])
