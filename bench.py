@@ -24,6 +24,12 @@ the step, with the unfused baseline the engine page measures it against:
 int4_dequantize to a float16 w_hat, then a library fp16 GEMM (torch's
 F.linear, hipBLASLt) on it ("unfused_baseline"; --no-unfused skips it).
 
+Also after the timed steps, "gated_cases" times each case the path is
+measured against on its own: M = 1 on the three shapes and on the
+[28672, 8192] FFN matrix (gate: 70% of HBM peak on packed weights + scales),
+M = 2048 on the three shapes (gate: 50% of the dense fp16 MFMA peak), and
+M = 4096 on the FFN matrix (reported). --no-gates skips it.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
 
 --copy-probe adds, after the timed region, three plain device-to-device
@@ -214,6 +220,101 @@ def unfused_comparison(mats, pool, reps=20):
     return out
 
 
+def _graph_time_us(fn, reps):
+    """Best of three replays of a HIP graph of `reps` calls, microseconds per call."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e3 / reps)
+    return best
+
+
+# The measurement gates of the hot path: M = 1 at >= 70% of HBM peak on the
+# packed weights + scales, M = 2048 at >= 50% of the dense fp16 MFMA peak
+# (256 CUs x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s).
+GATE_HBM_FRAC, GATE_MFMA_FRAC, MFMA_PEAK_GATE_TFLOPS = 0.70, 0.50, 2516.6
+
+
+def gated_cases(mats, pool, dev):
+    """Each gated case of the path timed on its own (graph replays, best of
+    three): the three 7B-class shapes at M = 1 (weights rotating through the
+    >= 1 GiB pool) and M = 2048, and the [28672, 8192] FFN matrix at M = 1
+    (its own >= 1 GiB pool of quantized N(0, 0.02) weights) and M = 4096
+    (reported, not gated)."""
+    import torch
+    import dequantizing_gemm_amd as dq
+
+    L = dq.lib
+    out = []
+
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
+
+    def decode_case(name, N, K, copies, x, y):
+        it = {"k": 0}
+
+        def call():
+            p, s_ = copies[it["k"] % len(copies)]
+            it["k"] += 1
+            assert L.int4_matmul(x.data_ptr(), 1, 1, p.data_ptr(), s_.data_ptr(), N, K, GROUP,
+                                 y.data_ptr(), cur()) == 0
+        us = _graph_time_us(call, len(copies))
+        gbs = packed_weight_bytes(N, K) / us / 1e3
+        gate = GATE_HBM_FRAC * HBM_PEAK_GBS
+        out.append({"case": f"{name} [{N},{K}] M=1", "time_us": round(us, 3), "achieved": round(gbs, 1),
+                    "unit": "GB/s", "gate": gate, "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "pass": gbs >= gate})
+
+    def prefill_case(name, N, K, M_, p, s_, x, y, gated=True):
+        def call():
+            assert L.int4_matmul(x.data_ptr(), 1, M_, p.data_ptr(), s_.data_ptr(), N, K, GROUP,
+                                 y.data_ptr(), cur()) == 0
+        us = _graph_time_us(call, 10)
+        tf = 2 * M_ * N * K / us / 1e6
+        gate = GATE_MFMA_FRAC * MFMA_PEAK_GATE_TFLOPS
+        rec = {"case": f"{name} [{N},{K}] M={M_}", "time_us": round(us, 3), "achieved": round(tf, 1),
+               "unit": "TFLOP/s", "frac_of_peak": round(tf / MFMA_PEAK_GATE_TFLOPS, 4)}
+        if gated:
+            rec.update(gate=gate, **{"pass": tf >= gate})
+        out.append(rec)
+
+    for i, m in enumerate(mats):
+        decode_case(m["name"], m["N"], m["K"], [pool[r][i] for r in range(len(pool))], m["x1"], m["y1"])
+    for m in mats:
+        prefill_case(m["name"], m["N"], m["K"], M_PREFILL, m["packed"], m["scales"], m["xp"], m["yp"])
+
+    N, K = 28672, 8192
+    gen = torch.Generator(device=dev).manual_seed(0)
+    w = torch.randn((N, K), generator=gen, device=dev) * 0.02
+    p0, s0, _ = dq.quantize_int4(w, GROUP)
+    del w
+    copies = [(p0, s0)] + [(p0.clone(), s0.clone())
+                           for _ in range(max(1, -(-POOL_BYTES // packed_weight_bytes(N, K)) - 1))]
+    x1 = torch.randn((1, K), generator=gen, device=dev).half()
+    y1 = torch.empty((1, N), device=dev)
+    decode_case("ffn", N, K, copies, x1, y1)
+    del copies
+    x4 = torch.randn((4096, K), generator=gen, device=dev).half()
+    y4 = torch.empty((4096, N), device=dev)
+    prefill_case("ffn", N, K, 4096, p0, s0, x4, y4, gated=False)
+    del x4, y4, p0, s0
+    torch.cuda.empty_cache()
+    return out
+
+
 def packed_weight_bytes(N, K, g=GROUP):
     return N * ((K + 1) // 2) + 2 * N * ((K + g - 1) // g)
 
@@ -261,6 +362,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-gates", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -417,6 +519,9 @@ def main():
     if not args.no_unfused:
         print("bench: fused vs dequantize-then-GEMM", file=sys.stderr, flush=True)
         line["unfused_baseline"] = unfused_comparison(mats, pool)
+    if not args.no_gates:
+        print("bench: gated cases", file=sys.stderr, flush=True)
+        line["gated_cases"] = gated_cases(mats, pool, dev)
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
