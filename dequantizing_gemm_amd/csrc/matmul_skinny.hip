@@ -301,13 +301,13 @@ const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
 
 // Whether the skinny kernel should take a shape it supports. Up to 16 rows
 // always. For 17-64 rows its time grows with N times the number of 16-row
-// tiles, while the tiled kernel's is flat there (its grid of 64 x 128 tiles is
-// small and each block walks all of K); measured on MI355X, the skinny kernel
-// is faster while N * ceil(M / 16) <= 32768: [4096,4096] M = 64 20 us against
-// 29, [11008,4096] M = 32 25 us against 33, but [11008,4096] M = 64 42 us
-// against 30 and [28672,8192] M = 17 99 us against 83.
+// tiles, while the tiled kernel's (32 x 128 tiles there) is about flat;
+// measured on MI355X, the skinny kernel is the faster one while
+// N * ceil(M / 16) <= 12288: [4096,4096] M = 32 11.6 us, M = 48 17.0 us
+// (tiled about 20), but M = 64 20.1 against 20.5, [4096,11008] M = 64 59.8
+// against 48.9, [11008,4096] M = 64 42.1 against 21.8.
 bool matmul_skinny_preferred(int64_t M, int64_t N) {
-  return M <= 16 || N * ((M + 15) / 16) <= 32768;
+  return M <= 16 || N * ((M + 15) / 16) <= 12288;
 }
 
 // Bytes of LDS a launch uses: the reduction buffer, plus the wave-private x

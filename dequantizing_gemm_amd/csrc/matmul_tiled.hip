@@ -13,10 +13,11 @@
 // side by side along N, one per SIMD, each owning 128 x 64 outputs as 4 x 2
 // tiles of v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 VGPRs). The
 // global -> LDS bytes per sub-step are 16 KB of x and 8 KB of packed weights
-// (a 256 x 128 tile moves 32 KB + 4 KB for the same flops). For a few hundred
-// rows of x the block is 128 x 128 or 64 x 128 instead (2 x 2 wavefronts of
-// 2 x 2 or 1 x 2 tiles) so that the grid still covers the CUs. Wave tiles
-// larger than 64 x 64 halve the LDS bytes read per MFMA.
+// (a 256 x 128 tile moves 32 KB + 4 KB for the same flops). For fewer rows of
+// x the block is 128 x 128, 64 x 128 or 32 x 128 with wave tiles one MFMA
+// tile wide (4, 2 or 1 tiles of 32 rows), so that the grid still covers the
+// CUs and every code is expanded once per block. Wave tiles larger than
+// 64 x 64 halve the LDS bytes read per MFMA.
 // K advances in sub-steps of BK = min(group, 64) codes:
 //  * x tiles [BM x BK] fp16 go global -> LDS by DMA (global_load_lds, 16 B
 //    per lane, no VGPRs) into a 4-stage ring, three sub-steps ahead.
@@ -84,18 +85,19 @@ constexpr int kThreads = 256;
 }  // namespace
 
 // BK: codes per sub-step (32 or 64). SPG: sub-steps per group (1, 2, 4 or 8),
-// or 0: any power of two 2^gshift, decided at run time. TM: 32-row MFMA tiles
-// per wavefront in M (4, 2 or 1). WN: wavefronts side by side along N (4:
-// block tile 32 TM x 256; 2: 2 x 2 wavefronts, block tile 64 TM x 128). The
-// launcher uses (TM, WN) = (4, 4), (2, 2) and (1, 2).
-template <int BK, int SPG, int TM, bool AFF, int WN>
+// or 0: any power of two 2^gshift, decided at run time. TM, TN: 32 x 32 MFMA
+// tiles per wavefront in M and N. WN: wavefronts side by side along N (4, or
+// 2 for 2 x 2 wavefronts). Block tile (32 TM * 4 / WN) x (32 TN * WN). The
+// launcher uses WN = 4 with (TM, TN) = (4, 2), (4, 1), (2, 1) and (1, 1).
+template <int BK, int SPG, int TM, bool AFF, int WN, int TN>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
     int gshift, void* __restrict__ y, Epilogue ep) {
-  constexpr int NW = 4, BM = 32 * TM * (NW / WN), BN = 64 * WN;
+  constexpr int WMT = 32 * TM, WNT = 32 * TN;         // wave tile; TM x TN 32x32 MFMA tiles
+  constexpr int NW = 4, BM = WMT * (NW / WN), BN = WNT * WN;
   static_assert(WN == 2 || WN == 4, "wave layout");
-  constexpr int WMT = 32 * TM, WNT = 64, TN = 2;       // wave tile; TM x TN 32x32 MFMA tiles
+  static_assert(TN == 1 || TN == 2, "wave tile columns");
   constexpr int KS = BK / 16;                  // MFMA k-steps per sub-step
   constexpr int PIECES = BK / 8;               // 16-byte pieces per x row per stage
   constexpr int RPB = 16 / PIECES;             // x rows per 256-byte bank period
@@ -488,28 +490,38 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   const int BK = tiled_bk(group);
   const int G = (int)((K + group - 1) / group);
   if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
-  // Block tile: the largest of 128 x 256, 128 x 128 and 64 x 128 (rows of x
-  // x weight rows) that still gives the grid 160 blocks or more. Measured on
-  // the 7B-class shapes: 128 x 256 is 7-8% faster than 256 x 128 (x is read
-  // from L2 half as often), and a grid of about 170 large tiles beats one of
-  // 340 smaller ones (M = 512 on [11008, 4096]: 60 us against 78), but 128
-  // blocks on 256 CUs do not.
+  // Block tile (rows of x x weight rows), always four wavefronts side by side
+  // along N: the first of 128 x 256, 128 x 128, 64 x 128 and 32 x 128 whose
+  // height fits M (rounded up to 32) and whose grid has 160 blocks or more,
+  // else 32 x 128. Measured on the 7B-class shapes: 128 x 256 is 7-8% faster
+  // than 256 x 128 (x is read from L2 half as often); a grid of about 170
+  // large tiles beats one of 340 smaller ones (M = 512 on [11008, 4096]: 60 us
+  // against 78), but 128 blocks on 256 CUs do not. For small M the narrow
+  // wave tiles (one 32-column MFMA tile each) expand every code once per
+  // block where 2 x 2 wavefronts expanded it twice: M = 128 on [4096, 11008]
+  // 70.4 -> 50.0 us with 32 x 128 tiles, [4096, 4096] 29.2 -> 21.5 us.
   auto grid_of = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  const int TM = grid_of(128, 256) >= 160 ? 4 : grid_of(128, 128) >= 160 ? 2 : 1;
-  const int64_t blocks = TM == 4 ? grid_of(128, 256) : grid_of(32 * TM * 2, 128);
+  const int64_t Mr = (M + 31) / 32 * 32;
+  int cfg = (Mr >= 128 && grid_of(128, 256) >= 160) ? 0
+          : (Mr >= 128 && grid_of(128, 128) >= 160) ? 1
+          : (Mr >= 64 && grid_of(64, 128) >= 160) ? 2 : 3;
+  // (a 32-row tile of 32-code sub-steps is 2 KB of x: less than one DMA
+  // instruction per wavefront, so group 32 takes 64-row tiles at least)
+  if (BK == 32 && cfg == 3) cfg = 2;
+  const int64_t blocks = cfg == 0 ? grid_of(128, 256) : grid_of(128 >> (cfg - 1), 128);
   if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
   int gs = 0;                                  // group = BK << gs
   while ((int64_t(BK) << gs) < group) ++gs;
-#define INT4DQ_TILED_PICK(TMV, A, W)                                                                     \
-  (BK == 32 ? matmul_tiled_kernel<32, 1, TMV, A, W>                                                      \
-   : gs == 0 ? matmul_tiled_kernel<64, 1, TMV, A, W> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV, A, W>   \
-   : gs == 2 ? matmul_tiled_kernel<64, 4, TMV, A, W> : gs == 3 ? matmul_tiled_kernel<64, 8, TMV, A, W>    \
-             : matmul_tiled_kernel<64, 0, TMV, A, W>)
-  const auto kernel =
-      zeros ? (TM == 4 ? INT4DQ_TILED_PICK(4, true, 4) : TM == 2 ? INT4DQ_TILED_PICK(2, true, 2)
-                                                                 : INT4DQ_TILED_PICK(1, true, 2))
-            : (TM == 4 ? INT4DQ_TILED_PICK(4, false, 4) : TM == 2 ? INT4DQ_TILED_PICK(2, false, 2)
-                                                                  : INT4DQ_TILED_PICK(1, false, 2));
+#define INT4DQ_TILED_PICK(TMV, A, TNV)                                                                     \
+  (BK == 32 ? matmul_tiled_kernel<32, 1, (TMV > 1 ? TMV : 2), A, 4, TNV>                                 \
+   : gs == 0 ? matmul_tiled_kernel<64, 1, TMV, A, 4, TNV> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV, A, 4, TNV> \
+   : gs == 2 ? matmul_tiled_kernel<64, 4, TMV, A, 4, TNV> : gs == 3 ? matmul_tiled_kernel<64, 8, TMV, A, 4, TNV> \
+             : matmul_tiled_kernel<64, 0, TMV, A, 4, TNV>)
+#define INT4DQ_TILED_CFG(A)                                                                            \
+  (cfg == 0 ? INT4DQ_TILED_PICK(4, A, 2) : cfg == 1 ? INT4DQ_TILED_PICK(4, A, 1)                      \
+   : cfg == 2 ? INT4DQ_TILED_PICK(2, A, 1) : INT4DQ_TILED_PICK(1, A, 1))
+  const auto kernel = zeros ? INT4DQ_TILED_CFG(true) : INT4DQ_TILED_CFG(false);
+#undef INT4DQ_TILED_CFG
 #undef INT4DQ_TILED_PICK
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const _Float16*>(x), (int)M, packed, scales, zeros, (int)N, (int)K, G,

@@ -191,9 +191,10 @@ def test_kernel_selection_rules():
     assert sel(1, 1, 4096, 16) == P["generic"]                 # group not a multiple of 32
     assert sel(1, 1, 65536, 128) == P["tiled"]                 # K beyond the gemv and skinny kernels
     assert sel(1, 2048, 11008, 128) == P["tiled"] and sel(1, 65, 4096, 128) == P["tiled"]
-    # 17-64 rows: skinny while N * ceil(M / 16) <= 32768, else tiled
-    assert sel(1, 17, 4096, 128) == P["skinny"] and sel(1, 64, 4096, 128, N=4096) == P["skinny"]
-    assert sel(1, 32, 4096, 128, N=11008) == P["skinny"] and sel(1, 33, 4096, 128, N=11008) == P["tiled"]
+    # 17-64 rows: skinny while N * ceil(M / 16) <= 12288, else tiled
+    assert sel(1, 17, 4096, 128) == P["skinny"] and sel(1, 48, 4096, 128, N=4096) == P["skinny"]
+    assert sel(1, 49, 4096, 128, N=4096) == P["tiled"] and sel(1, 32, 4096, 128, N=6144) == P["skinny"]
+    assert sel(1, 32, 4096, 128, N=11008) == P["tiled"]
     assert sel(1, 17, 8192, 128, N=28672) == P["tiled"] and sel(1, 16, 8192, 128, N=28672) == P["skinny"]
     # four row tiles do not take more than 96 K-blocks
     assert sel(1, 40, 16384, 128) == P["tiled"] and sel(1, 20, 16384, 128) == P["skinny"]

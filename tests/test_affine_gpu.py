@@ -147,14 +147,15 @@ MM = [
     (300, 4096, 128, 16, "skinny"),
     (300, 4096, 128, 40, "skinny"),   # four 16-row tiles
     (8200, 1024, 64, 24, "skinny"),   # two tiles, two row groups per block
-    # tiled: 64-, 128- and 256-row block tiles (TM 1, 2, 4) over every group
-    # cadence (BK 32; a group every 1, 2, 4, 8 sub-steps; decided at run time)
+    # tiled: 32 x 128, 64 x 128, 128 x 128 and 128 x 256 block tiles over every
+    # group cadence (BK 32; a group every 1, 2, 4, 8 sub-steps; decided at run time)
     (200, 1024, 32, 40, "tiled"),
     (4096, 1024, 32, 2048, "tiled"),
     (256, 1024, 64, 300, "tiled"),
     (4096, 1024, 64, 2048, "tiled"),
     (384, 2048, 128, 70, "tiled"),
     (8192, 1024, 128, 512, "tiled"),
+    (4096, 1024, 128, 512, "tiled"),
     (260, 2048, 256, 130, "tiled"),
     (4096, 1024, 512, 2048, "tiled"),
     (200, 4096, 1024, 100, "tiled"),

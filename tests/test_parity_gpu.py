@@ -284,7 +284,9 @@ def test_matmul_configs(dq, key, case, M):
                                      # two row groups per block, up to the largest K each form takes
                                      (200, 768, 32, 24), (300, 4096, 128, 64), (8200, 1024, 64, 40),
                                      (16400, 2048, 128, 20), (300, 12288, 128, 48), (64, 16384, 128, 30),
-                                     (77, 2048, 128, 33)])
+                                     (77, 2048, 128, 33),
+                                     # tiled block tiles 64 x 128 and 128 x 128 (four wavefronts along N)
+                                     (2048, 1024, 64, 700), (3000, 512, 128, 1100)])
 def test_matmul_kernels_agree(dq, N, K, g, M):
     """Every kernel that takes a shape matches the oracle on it (ragged M and N tails)."""
     w = np.random.default_rng(N + K).normal(0, 0.02, size=(N, K)).astype(np.float32)
@@ -359,7 +361,8 @@ def test_matmul_gemv_rows_one_hot_exact(dq):
                                           (300, 4096, 128, 64, "skinny"), (8200, 1024, 64, 24, "skinny"),
                                           (300, 1024, 128, 130, "tiled"), (129, 256, 32, 600, "tiled"),
                                           (640, 2048, 128, 520, "tiled"), (10880, 256, 64, 300, "tiled"),
-                                          (4096, 256, 128, 1600, "tiled"), (40, 1000, 7, 6, "generic")])
+                                          (4096, 256, 128, 1600, "tiled"), (4096, 512, 128, 512, "tiled"),
+                                          (40, 1000, 7, 6, "generic")])
 def test_matmul_epilogue(dq, N, K, g, M, path):
     """The engine page's epilogue act(x @ w_hat.T + bias) through every kernel
     (all three M = 1 variants, the 64/128/256-row tiles, the generic kernel):
