@@ -67,7 +67,7 @@ extern "C" {
 /* Kernel selection for int4_matmul_path (int4_matmul always uses AUTO). */
 #define INT4DQ_PATH_AUTO    0  /* choose by M, dtype and alignment */
 #define INT4DQ_PATH_GENERIC 1  /* VALU kernel, any shape, any group, fp32 or fp16 x */
-#define INT4DQ_PATH_SKINNY  2  /* M <= 16, fp16 x: weight-streaming MFMA kernel */
+#define INT4DQ_PATH_SKINNY  2  /* M <= 64, fp16 x: weight-streaming MFMA kernel */
 #define INT4DQ_PATH_TILED   3  /* any M, fp16 x: LDS-tiled MFMA kernel */
 #define INT4DQ_PATH_GEMV    4  /* M = 1, fp16 x, group and K multiples of 32: row-streaming kernel */
 
