@@ -195,22 +195,27 @@ __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
 // since the group is a multiple of 32 -- which the lane multiplies by its
 // scale. The dot products cost 8 MFMAs instead of 16 v_dot2 per 32 codes.
 //
-// Block = W wavefronts of 4 rows each. The activation row (permuted to the
-// spread order, zero past K) and the block's scales are staged once in LDS;
+// Block = W groups of 4 rows, each taken by KSP wavefronts that split the
+// rows' column blocks (KSP = 2 for long rows). The activation row (permuted
+// to the spread order, zero past K) and the block's scales are staged once in LDS;
 // every weight load of a lane (one per column block) is issued before the
 // first wait, and column c waits only for its own load. Used for group sizes
 // 32 << p and K <= 12288; other shapes take the VALU kernel above.
 // CM: column blocks (256 bytes) per row, >= ceil(K / 512). GS: min(gsh, 3)
 // (group = 32 << gsh), which bounds the groups per row and so the scale
 // entries each thread stages.
-template <int CM, int GS, int W, bool AFF>
-__global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
+// KSP: wavefronts per group of 4 rows, each taking CM / KSP of the column
+// blocks; their partial sums are added through LDS in a fixed order.
+template <int CM, int GS, int W, bool AFF, int KSP = 1>
+__global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
     const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
     int group, int gsh, void* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
-  constexpr int NT = 64 * W, ROWS = 4 * W;     // threads, rows per block
+  static_assert(CM % KSP == 0, "column split");
+  constexpr int CMP = CM / KSP;                // column blocks per wavefront
+  constexpr int NT = 64 * W * KSP, ROWS = 4 * W;   // threads, rows per block
   constexpr int XPT = (CM * 64 + NT - 1) / NT; // 16-byte x units per thread (x row <= CM KB)
   constexpr int GMAX = (CM * 16 + (1 << GS) - 1) >> GS;           // groups per row, at most
   constexpr int SPT = (ROWS * GMAX + NT - 1) / NT;                 // scale entries per thread
@@ -219,9 +224,11 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t xsp[XPT * NT * 4];   // x, spread order
   __shared__ uint16_t ssh[SPT * NT];                                  // scales of the block's rows
   __shared__ uint8_t zsh[AFF ? SPT * NT : 1];                         // their zero points
+  __shared__ float part_sum[KSP > 1 ? KSP * ROWS : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wid / KSP, part = wid % KSP;  // group of 4 rows, share of the columns
   const int b = lane >> 2, j = lane & 3;
   const int RB = K >> 1;
   const int n0 = blockIdx.x * ROWS;
@@ -256,15 +263,15 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   // Phase 2: the lane's 16 bytes of each column block of its row.
   const int n = n0 + 4 * wave + j < N ? n0 + 4 * wave + j : N - 1;
   const uint8_t* prow = packed + (int64_t)n * RB;
-  u32x4_t w[CM];
+  u32x4_t w[CMP];
 #pragma unroll
-  for (int c = 0; c < CM; ++c) {
-    int o = c * 256 + b * 16;
+  for (int c = 0; c < CMP; ++c) {
+    int o = (part * CMP + c) * 256 + b * 16;
     o = o < RB ? o : RB - 16;                  // past the row end: valid, masked below
     w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(prow + (uint32_t)o));
   }
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt_gemv<CM>();                       // phase 1 landed
+  wait_vmcnt_gemv<CMP>();                      // phase 1 landed
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < XPT; ++t) {
@@ -296,14 +303,15 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   const uint8_t* zrow = zsh + (AFF ? (4 * wave + j) * G + (b >> gsh) : 0);
   const uint32_t* xl = xsp + 16 * b;
   float acc = 0.0f;
-  static_for<0, CM>([&](auto C_) {
+  static_for<0, CMP>([&](auto C_) {
     constexpr int c = decltype(C_)::value;
-    const float sc = half_bits_to_float(srow[(16 * c) >> gsh]);
-    const uint32_t zp = AFF ? (uint32_t)zrow[(16 * c) >> gsh] : 0u;
+    const int cg = part * CMP + c;             // column block in the row
+    const float sc = half_bits_to_float(srow[(16 * cg) >> gsh]);
+    const uint32_t zp = AFF ? (uint32_t)zrow[(16 * cg) >> gsh] : 0u;
     u32x4_t xa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4_t*>(xl + 256 * c + 4 * i);
-    wait_vmcnt_gemv<CM - 1 - c>();
+    for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4_t*>(xl + 256 * cg + 4 * i);
+    wait_vmcnt_gemv<CMP - 1 - c>();
     float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -322,6 +330,14 @@ __global__ __launch_bounds__(64 * W) void matmul_gemv_mfma_kernel(
   // Sum the 16 slices (lanes 4b+j, b = 0..15) of each of the 4 rows.
 #pragma unroll
   for (int off = 4; off < 64; off <<= 1) acc += __shfl_xor(acc, off);
+  if constexpr (KSP > 1) {
+    if (b == 0) part_sum[part * ROWS + 4 * wave + j] = acc;
+    __syncthreads();
+    if (part != 0) return;
+    acc = part_sum[4 * wave + j];
+#pragma unroll
+    for (int p = 1; p < KSP; ++p) acc += part_sum[p * ROWS + 4 * wave + j];
+  }
   if (b == 0 && n0 + 4 * wave + j < N) ep.store(y, n0 + 4 * wave + j, acc, n0 + 4 * wave + j);
 }
 
@@ -525,15 +541,21 @@ static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint
   }
   const int cols = (int)((K / 2 + 255) / 256);                // 256-byte column blocks per row
   if (cols <= 24 && gsh >= 0 && g_gemv_mfma) {
-    constexpr int W = g_gemv_waves;                              // wavefronts (4 rows each) per block
-    const dim3 g16((unsigned)((N + 4 * W - 1) / (4 * W))), b256(64 * W);
+    // Rows of 16 or more column blocks (K >= 7680) split each row's columns
+    // over two wavefronts (blocks of 2 x 2 wavefronts, 8 rows): their chains
+    // of expansions and MFMAs after the loads land are half as long. Measured
+    // (1 GiB rotation pool): [4096,8192] 6.41 -> 5.65 us, [4096,11008] 7.91 ->
+    // 6.98 us; rows of 12 column blocks or fewer were slower split ([4096,6144]
+    // 4.65 -> 4.94 us), so they keep 4 wavefronts of whole rows per block.
 #define INT4DQ_GEMV_MFMA(CMV)                                                                    \
   do {                                                                                          \
-    const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<CMV, 0, W, AFF>                        \
-                    : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, W, AFF>                        \
-                    : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, W, AFF>                        \
-                               : matmul_gemv_mfma_kernel<CMV, 3, W, AFF>;                       \
-    hipLaunchKernelGGL(kern, g16, b256, 0, stream, xh0, packed, scales, zeros, (int)N, (int)K,  \
+    constexpr int KS = CMV >= 16 ? 2 : 1, W = CMV >= 16 ? 2 : g_gemv_waves;                     \
+    const dim3 grid((unsigned)((N + 4 * W - 1) / (4 * W))), block(64 * W * KS);                \
+    const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<CMV, 0, W, AFF, KS>                    \
+                    : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, W, AFF, KS>                    \
+                    : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, W, AFF, KS>                    \
+                               : matmul_gemv_mfma_kernel<CMV, 3, W, AFF, KS>;                   \
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, packed, scales, zeros, (int)N, (int)K, \
                        G, (int)group, gsh, y, ep);                                              \
   } while (0)
     if (cols <= 2) INT4DQ_GEMV_MFMA(2);

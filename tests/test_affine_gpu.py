@@ -134,6 +134,7 @@ def test_dequantize_affine_bit_exact(dq, N, K, g, shift):
 MM = [
     (300, 4096, 128, 1, "gemv"),      # 4-row MFMA gemv
     (513, 2080, 32, 1, "gemv"),       # MFMA gemv, ragged column blocks
+    (301, 8192, 64, 1, "gemv"),       # MFMA gemv, columns split over two wavefronts
     (77, 4096, 96, 1, "gemv"),        # VALU gemv (group not 32 * 2^p)
     (40, 32768, 128, 1, "gemv"),      # VALU gemv, long rows
     (12300, 8224, 32, 1, "gemv"),     # whole-row gemv (>= 48 MB)

@@ -302,7 +302,8 @@ def test_matmul_kernels_agree(dq, N, K, g, M):
         check_matmul(y, x, pr, sr, K, g, what=path)
 
 
-@pytest.mark.parametrize("N,K,g", [(300, 11008, 128), (77, 4096, 96), (513, 2080, 32), (40, 32768, 128),
+@pytest.mark.parametrize("N,K,g", [(300, 11008, 128), (301, 8192, 64), (4099, 7680, 256), (77, 4096, 96),
+                                   (513, 2080, 32), (40, 32768, 128),
                                    (10, 32, 32), (4099, 4096, 128), (8195, 4096, 64), (2051, 2048, 128),
                                    (12300, 8224, 32), (24577, 4096, 96), (6700, 16384, 256)])
 def test_matmul_gemv_shapes(dq, N, K, g):
@@ -357,6 +358,7 @@ def test_matmul_gemv_rows_one_hot_exact(dq):
 
 @pytest.mark.parametrize("N,K,g,M,path", [(300, 1024, 128, 1, "gemv"), (200, 768, 32, 1, "gemv"),
                                           (12300, 8224, 32, 1, "gemv"), (77, 4096, 96, 1, "gemv"),
+                                          (301, 11008, 128, 1, "gemv"),
                                           (200, 768, 64, 5, "skinny"), (48, 4096, 128, 16, "skinny"),
                                           (300, 4096, 128, 64, "skinny"), (8200, 1024, 64, 24, "skinny"),
                                           (300, 1024, 128, 130, "tiled"), (129, 256, 32, 600, "tiled"),
