@@ -12,7 +12,10 @@
 // (this file is compiled with -fhip-fp32-correctly-rounded-divide-sqrt and
 // without fast-math, so `a / b` is the IEEE operation, not a reciprocal
 // multiply), binary32 -> binary16 is v_cvt_f16_f32 in round-to-nearest-even
-// with fp16 denormals kept, and rintf is v_rndne_f32 (ties to even).
+// with fp16 denormals kept, and rintf is v_rndne_f32 (ties to even). The
+// per-element division is only carried out where it can change the code
+// (quotient_for_rint): elsewhere a reciprocal multiply rounds to the same
+// integer.
 //
 // Work decomposition (vector kernel): one wavefront per 512-element segment
 // of a row; lane l owns elements [8l, 8l+8) of the segment, read as two
@@ -27,51 +30,98 @@
 
 namespace int4dq {
 
-__device__ __forceinline__ uint32_t code_of(float w, float sf) {
-  if (sf == 0.0f) return 0u;                       // a group of zeros -> codes 0
-  float r = __builtin_rintf(w / sf);               // IEEE division, ties-to-even
+// The quotient w / scale as far as rounding it to an integer is concerned.
+// t = w * rcp(scale) is within 2^-22 |t| of the correctly rounded quotient
+// (v_rcp_f32 is within 1 ulp, the product rounds once), and |t| < 32 here
+// (|w| <= 7.01 scale, or 15.02 scale for affine codes; subnormal binary16
+// scales stay below 22), so within 2^-17: rint gives the same integer unless
+// a half-integer lies that close. Those elements (|t - rint(t)| within 2^-14
+// of 0.5; a true tie always is) take the IEEE division; a wavefront whose
+// lanes have none skips it. Exact: the codes are the ones the division gives.
+__device__ __forceinline__ bool near_half_integer(float t) {
+  const float d = __builtin_fabsf(t - __builtin_rintf(t));   // exact for |t| < 2^22
+  return __builtin_fabsf(d - 0.5f) < 0x1p-14f;
+}
+
+__device__ __forceinline__ float quotient_for_rint(float w, float sf, float rsf) {
+  float t = w * rsf;
+  if (__builtin_expect(near_half_integer(t), 0)) t = w / sf;   // IEEE division
+  return t;
+}
+
+// rcp(sf) once per group, and 0 for a zero scale: then t = 0, which is no
+// half-integer, so a zero group gets codes 0 without a branch.
+__device__ __forceinline__ float scale_rcp(float sf) {
+  return sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf);
+}
+
+__device__ __forceinline__ uint32_t code_of(float w, float sf, float rsf) {
+  float r = __builtin_rintf(quotient_for_rint(w, sf, rsf));   // ties-to-even
   r = __builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f);
   return (uint32_t)(int)r & 0xFu;
 }
 
-// LANES = group / 8, a power of two in [1, 64].
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const float o = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_fmaxf(v, o);
+}
+
+// Maximum of v over aligned runs of LANES lanes, in every lane of the run:
+// inside a 16-lane row a DPP butterfly (lanes i^1, i^2, then i <-> 7-i and
+// i <-> 15-i, which after the first two steps pair whole quads and halves),
+// across rows lane shuffles.
+template <int LANES>
+__device__ __forceinline__ float run_max(float v) {
+  if constexpr (LANES >= 2) v = dpp_max<0xB1>(v);      // quad_perm [1,0,3,2]
+  if constexpr (LANES >= 4) v = dpp_max<0x4E>(v);      // quad_perm [2,3,0,1]
+  if constexpr (LANES >= 8) v = dpp_max<0x141>(v);     // row_half_mirror
+  if constexpr (LANES >= 16) v = dpp_max<0x140>(v);    // row_mirror
+#pragma unroll
+  for (int o = 16; o < LANES; o <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// LANES = group / 8, a power of two in [1, 64]. Grid: x covers the 512-code
+// segments of a row, four per block (one per wavefront); y walks the rows.
 template <int LANES>
 __global__ __launch_bounds__(256) void quantize_vec_kernel(
-    const float* __restrict__ w, int64_t K, int64_t G, int64_t segs_per_row,
-    int64_t total_segs, uint8_t* __restrict__ packed, uint16_t* __restrict__ scales) {
+    const float* __restrict__ w, int64_t N, int64_t K, int64_t G, int64_t segs_per_row,
+    uint8_t* __restrict__ packed, uint16_t* __restrict__ scales) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t seg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (seg >= total_segs) return;                   // whole wavefronts only
-  const int64_t n = seg / segs_per_row;
-  const int64_t k = (seg - n * segs_per_row) * 512 + (int64_t)lane * 8;
-  const bool valid = k < K;                        // K % 8 == 0: all 8 or none
-  float v[8];
-  if (valid) {
-    const float4_t* p = reinterpret_cast<const float4_t*>(w + n * K + k);
-    const float4_t a = __builtin_nontemporal_load(p);
-    const float4_t b = __builtin_nontemporal_load(p + 1);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
+  if (seg >= segs_per_row) return;                 // whole wavefronts only
+  for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
+    const int64_t k = seg * 512 + (int64_t)lane * 8;
+    const bool valid = k < K;                        // K % 8 == 0: all 8 or none
+    float v[8];
+    if (valid) {
+      const float4_t* p = reinterpret_cast<const float4_t*>(w + n * K + k);
+      const float4_t a = __builtin_nontemporal_load(p);
+      const float4_t b = __builtin_nontemporal_load(p + 1);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  float amax = 0.0f;
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-#pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o));
+    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    amax = run_max<LANES>(amax);
 
-  const float s32 = amax / 7.0f;
-  const _Float16 s16 = (_Float16)s32;
-  const float sf = (float)s16;
-  uint32_t word = 0;
+    const float s32 = amax / 7.0f;
+    const _Float16 s16 = (_Float16)s32;
+    const float sf = (float)s16;
+    const float rsf = scale_rcp(sf);
+    uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= code_of(v[i], sf) << (4 * i);
-  if (valid) {
-    *reinterpret_cast<uint32_t*>(packed + n * (K >> 1) + (k >> 1)) = word;
-    if ((lane & (LANES - 1)) == 0)
-      scales[n * G + k / (LANES * 8)] = __builtin_bit_cast(uint16_t, s16);
+    for (int i = 0; i < 8; ++i) word |= code_of(v[i], sf, rsf) << (4 * i);
+    if (valid) {
+      *reinterpret_cast<uint32_t*>(packed + n * (K >> 1) + (k >> 1)) = word;
+      if ((lane & (LANES - 1)) == 0)
+        scales[n * G + k / (LANES * 8)] = __builtin_bit_cast(uint16_t, s16);
+    }
   }
 }
 
@@ -102,10 +152,10 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
   const int64_t n = t / B, j = t - n * B;
   const int64_t k = 2 * j;
   const float sf0 = half_bits_to_float(scales[n * G + k / group]);
-  uint32_t byte = code_of(w[n * K + k], sf0);
+  uint32_t byte = code_of(w[n * K + k], sf0, scale_rcp(sf0));
   if (k + 1 < K) {
     const float sf1 = half_bits_to_float(scales[n * G + (k + 1) / group]);
-    byte |= code_of(w[n * K + k + 1], sf1) << 4;
+    byte |= code_of(w[n * K + k + 1], sf1, scale_rcp(sf1)) << 4;
   }
   packed[t] = (uint8_t)byte;
 }
@@ -130,59 +180,82 @@ __device__ __forceinline__ uint32_t affine_zp(float lo, float sf) {
   return (uint32_t)z;
 }
 
-__device__ __forceinline__ uint32_t affine_code(float w, float sf, uint32_t zp) {
-  if (sf == 0.0f) return 0u;
-  const double t = (double)(w / sf) + (double)zp;  // exact
-  double r = __builtin_rint(t);
-  r = __builtin_fmin(__builtin_fmax(r, 0.0), 15.0);
+// rint(w / sf + zp) with the exact sum. Away from a half-integer the integer
+// zp does not change the rounding, so rint(t + zp) = rint(t) + zp with t as in
+// quotient_for_rint. Near one (a tie above all: rint(0.5 + 1) = 2 but
+// rint(0.5) + 1 = 1), the IEEE quotient plus zp in binary64, where the sum is
+// exact, is rounded half to even.
+__device__ __forceinline__ uint32_t affine_code(float w, float sf, float rsf, uint32_t zp) {
+  const float t = w * rsf;                         // 0 for a zero scale (rsf = 0, zp = 0)
+  float r;
+  if (__builtin_expect(near_half_integer(t), 0))
+    r = (float)__builtin_rint((double)(w / sf) + (double)zp);   // IEEE division, exact sum
+  else
+    r = __builtin_rintf(t) + (float)zp;                         // integers < 2^24: exact
+  r = __builtin_fminf(__builtin_fmaxf(r, 0.0f), 15.0f);
   return (uint32_t)r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_min(float v) {
+  const float o = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_fminf(v, o);
+}
+
+template <int LANES>
+__device__ __forceinline__ float run_min(float v) {
+  if constexpr (LANES >= 2) v = dpp_min<0xB1>(v);
+  if constexpr (LANES >= 4) v = dpp_min<0x4E>(v);
+  if constexpr (LANES >= 8) v = dpp_min<0x141>(v);
+  if constexpr (LANES >= 16) v = dpp_min<0x140>(v);
+#pragma unroll
+  for (int o = 16; o < LANES; o <<= 1) v = __builtin_fminf(v, __shfl_xor(v, o));
+  return v;
 }
 
 template <int LANES>
 __global__ __launch_bounds__(256) void quantize_affine_vec_kernel(
-    const float* __restrict__ w, int64_t K, int64_t G, int64_t segs_per_row,
-    int64_t total_segs, uint8_t* __restrict__ packed, uint16_t* __restrict__ scales,
-    uint8_t* __restrict__ zeros) {
+    const float* __restrict__ w, int64_t N, int64_t K, int64_t G, int64_t segs_per_row,
+    uint8_t* __restrict__ packed, uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t seg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (seg >= total_segs) return;                   // whole wavefronts only
-  const int64_t n = seg / segs_per_row;
-  const int64_t k = (seg - n * segs_per_row) * 512 + (int64_t)lane * 8;
-  const bool valid = k < K;
-  float v[8];
-  if (valid) {
-    const float4_t* p = reinterpret_cast<const float4_t*>(w + n * K + k);
-    const float4_t a = __builtin_nontemporal_load(p);
-    const float4_t b = __builtin_nontemporal_load(p + 1);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
+  if (seg >= segs_per_row) return;                 // whole wavefronts only
+  for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
+    const int64_t k = seg * 512 + (int64_t)lane * 8;
+    const bool valid = k < K;
+    float v[8];
+    if (valid) {
+      const float4_t* p = reinterpret_cast<const float4_t*>(w + n * K + k);
+      const float4_t a = __builtin_nontemporal_load(p);
+      const float4_t b = __builtin_nontemporal_load(p + 1);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  float lo = 0.0f, hi = 0.0f;                      // the range includes zero
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float lo = 0.0f, hi = 0.0f;                      // the range includes zero
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    lo = __builtin_fminf(lo, v[i]);
-    hi = __builtin_fmaxf(hi, v[i]);
-  }
+    for (int i = 0; i < 8; ++i) {
+      lo = __builtin_fminf(lo, v[i]);
+      hi = __builtin_fmaxf(hi, v[i]);
+    }
+    lo = run_min<LANES>(lo);
+    hi = run_max<LANES>(hi);
+    const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
+    const float sf = (float)s16;
+    const float rsf = scale_rcp(sf);
+    const uint32_t zp = affine_zp(lo, sf);
+    uint32_t word = 0;
 #pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) {
-    lo = __builtin_fminf(lo, __shfl_xor(lo, o));
-    hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
-  }
-  const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
-  const float sf = (float)s16;
-  const uint32_t zp = affine_zp(lo, sf);
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) word |= affine_code(v[i], sf, zp) << (4 * i);
-  if (valid) {
-    *reinterpret_cast<uint32_t*>(packed + n * (K >> 1) + (k >> 1)) = word;
-    if ((lane & (LANES - 1)) == 0) {
-      const int64_t gi = n * G + k / (LANES * 8);
-      scales[gi] = __builtin_bit_cast(uint16_t, s16);
-      zeros[gi] = (uint8_t)zp;
+    for (int i = 0; i < 8; ++i) word |= affine_code(v[i], sf, rsf, zp) << (4 * i);
+    if (valid) {
+      *reinterpret_cast<uint32_t*>(packed + n * (K >> 1) + (k >> 1)) = word;
+      if ((lane & (LANES - 1)) == 0) {
+        const int64_t gi = n * G + k / (LANES * 8);
+        scales[gi] = __builtin_bit_cast(uint16_t, s16);
+        zeros[gi] = (uint8_t)zp;
+      }
     }
   }
 }
@@ -215,10 +288,12 @@ __global__ __launch_bounds__(256) void quantize_affine_pack_kernel(
   const int64_t n = t / B, j = t - n * B;
   const int64_t k = 2 * j;
   const int64_t g0 = n * G + k / group;
-  uint32_t byte = affine_code(w[n * K + k], half_bits_to_float(scales[g0]), zeros[g0]);
+  const float sf0 = half_bits_to_float(scales[g0]);
+  uint32_t byte = affine_code(w[n * K + k], sf0, scale_rcp(sf0), zeros[g0]);
   if (k + 1 < K) {
     const int64_t g1 = n * G + (k + 1) / group;
-    byte |= affine_code(w[n * K + k + 1], half_bits_to_float(scales[g1]), zeros[g1]) << 4;
+    const float sf1 = half_bits_to_float(scales[g1]);
+    byte |= affine_code(w[n * K + k + 1], sf1, scale_rcp(sf1), zeros[g1]) << 4;
   }
   packed[t] = (uint8_t)byte;
 }
@@ -235,13 +310,12 @@ hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, 
   const int64_t G = (K + group - 1) / group;
   if (quantize_vec_supported(w, K, group, packed, scales)) {
     const int64_t segs_per_row = (K + 511) / 512;
-    const int64_t total = N * segs_per_row;
-    const dim3 grid((unsigned)((total + 3) / 4)), block(256);
+    const dim3 grid((unsigned)((segs_per_row + 3) / 4), (unsigned)(N < 65535 ? N : 65535)), block(256);
     switch (group) {
 #define INT4DQ_Q(Gs)                                                                        \
   case Gs:                                                                                  \
-    hipLaunchKernelGGL(quantize_vec_kernel<Gs / 8>, grid, block, 0, stream, w, K, G,      \
-                       segs_per_row, total, packed, scales);                               \
+    hipLaunchKernelGGL(quantize_vec_kernel<Gs / 8>, grid, block, 0, stream, w, N, K, G,   \
+                       segs_per_row, packed, scales);                                      \
     break;
       INT4DQ_Q(8) INT4DQ_Q(16) INT4DQ_Q(32) INT4DQ_Q(64) INT4DQ_Q(128) INT4DQ_Q(256) INT4DQ_Q(512)
 #undef INT4DQ_Q
@@ -266,13 +340,12 @@ hipError_t launch_quantize_affine(const float* w, int64_t N, int64_t K, int64_t 
   const int64_t G = (K + group - 1) / group;
   if (quantize_vec_supported(w, K, group, packed, scales)) {
     const int64_t segs_per_row = (K + 511) / 512;
-    const int64_t total = N * segs_per_row;
-    const dim3 grid((unsigned)((total + 3) / 4)), block(256);
+    const dim3 grid((unsigned)((segs_per_row + 3) / 4), (unsigned)(N < 65535 ? N : 65535)), block(256);
     switch (group) {
 #define INT4DQ_QA(Gs)                                                                       \
   case Gs:                                                                                  \
-    hipLaunchKernelGGL(quantize_affine_vec_kernel<Gs / 8>, grid, block, 0, stream, w, K, G, \
-                       segs_per_row, total, packed, scales, zeros);                        \
+    hipLaunchKernelGGL(quantize_affine_vec_kernel<Gs / 8>, grid, block, 0, stream, w, N, K, \
+                       G, segs_per_row, packed, scales, zeros);                            \
     break;
       INT4DQ_QA(8) INT4DQ_QA(16) INT4DQ_QA(32) INT4DQ_QA(64) INT4DQ_QA(128) INT4DQ_QA(256) INT4DQ_QA(512)
 #undef INT4DQ_QA
