@@ -234,3 +234,27 @@ def test_affine_auto_path_and_zero_m(dq):
         check(host(dq.int4_matmul(dev(x), p, s, K, g, zeros=z)), x, pr, sr, zr, K, g, what=f"auto M={M}")
     y = dq.int4_matmul(dev(acts(0, K, 0)).reshape(0, K), p, s, K, g, zeros=z)
     assert tuple(y.shape) == (0, N)
+
+
+def test_quantize_affine_near_ties(dq):
+    """Affine quotients on and within a few ulps of half-integers, with odd and
+    even zero points (odd ones flip which way an exact tie rounds): codes and
+    zero points bit for bit with the oracle."""
+    say("case: quantize_affine near-tie quotients")
+    rng = np.random.default_rng(78)
+    rows = []
+    for (lo, hi) in ((-1.0, 14.0), (-2.0, 13.0), (-7.3, 7.7), (-0.021, 0.138), (-5.5, 9.5)):
+        sf = float(np.float16(np.float32(np.float32(hi) - np.float32(lo)) / np.float32(15)))
+        for h in np.arange(-6.5, 6.5, 1.0):
+            for d in (0.0, 2.0 ** -24, -2.0 ** -24, 2.0 ** -21, -2.0 ** -21, 2.0 ** -18):
+                row = [lo, hi]
+                for j in range(6):
+                    t = h + d * (j + 1) * rng.choice([-1, 1])
+                    row.append(float(np.clip(np.float32(t * sf), lo, hi)))
+                rows.append(row)
+    w = np.array(rows, np.float32)
+    p, s, z, K = dq.quantize_int4_affine(dev(w), 8)
+    pr, sr, zr, _ = oracle.quantize_int4_affine(w, 8)
+    assert np.array_equal(host(s).view(np.uint16), sr.view(np.uint16))
+    assert np.array_equal(host(z), zr)
+    assert np.array_equal(host(p), pr)

@@ -458,3 +458,36 @@ def test_rows_independent(dq):
         one = host(dq.int4_matmul(dev(x[m:m + 1]), pd, sd, 4096, 128))
         _, bound = oracle.int4_matmul(x[m:m + 1], pr, sr, 4096, 128, with_bound=True)
         assert np.all(np.abs(one[0] - big[m]) <= 2 * TOL * bound[0])
+
+
+def _near_tie_rows(rng, lo_h, hi_h, scales):
+    """Rows of 8 weights whose quotients w / scale sit on and a few ulps
+    around half-integers (the cases where a reciprocal multiply could round
+    the other way); element 0 fixes the group's scale."""
+    rows = []
+    for s_target in scales:
+        for h in np.arange(lo_h, hi_h + 0.5, 1.0):
+            for d in (0.0, 2.0 ** -24, -2.0 ** -24, 2.0 ** -22, -2.0 ** -22, 2.0 ** -19, -2.0 ** -19):
+                row = [s_target[0]]
+                for j in range(7):
+                    t = h + d * (j + 1) * rng.choice([-1, 1])
+                    row.append(np.float32(t * s_target[1]))
+                rows.append(row)
+    return np.array(rows, np.float32)
+
+
+def test_quantize_near_ties_gpu(dq):
+    """Quotients on and within a few ulps of every half-integer code boundary
+    (-7.5 .. 6.5) for several non-power-of-two scales: the codes must equal the
+    oracle's (IEEE division, ties to even) bit for bit."""
+    say("case: quantize near-tie quotients")
+    rng = np.random.default_rng(77)
+    sc = []
+    for target in (0.7, 1.3, 0.0123, 3.7e-3, 5.1):
+        sf = float(np.float16(np.float32(np.float32(7 * target) / np.float32(7))))
+        sc.append((np.float32(7 * target), sf))
+    w = _near_tie_rows(rng, -7.5, 6.5, sc)
+    p, s, K = dq.quantize_int4(dev(w), 8)
+    pr, sr, _ = oracle.quantize_int4(w, 8)
+    assert np.array_equal(host(s).view(np.uint16), sr.view(np.uint16))
+    assert np.array_equal(host(p), pr)
