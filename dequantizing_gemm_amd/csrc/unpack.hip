@@ -7,7 +7,7 @@
 // is dropped.
 //
 // Even K: the packed array and the output are the same byte stream read at
-// 1:2, so the kernel is flat. Each thread turns one 16-byte load into two
+// 1:2, so the kernel is flat. Each thread turns two 8-byte loads into two
 // 16-byte stores: per 32-bit word, low and high nibbles are split with two
 // masks, sign-extended bytewise (v | ((v & 8) * 0x1E) sets bits 4..7 exactly
 // when bit 3 is set, with no carry between bytes), and interleaved with two
@@ -30,27 +30,32 @@ __device__ __forceinline__ u32x2_t unpack_word(uint32_t w) {
   return r;
 }
 
+// A wavefront takes 1 KB of packed bytes: lane l reads the 8 bytes at 8 l and
+// at 512 + 8 l, so each of its two 16-byte stores lands in one contiguous
+// kilobyte of output per wavefront instruction (a lane owning 16 consecutive
+// bytes would store two half-filled 32-byte strides instead).
 __global__ __launch_bounds__(256) void unpack_flat_kernel(const uint8_t* __restrict__ packed,
                                                           int64_t nbytes, int8_t* __restrict__ out) {
-  const int64_t chunk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b0 = chunk * 16;
-  if (b0 >= nbytes) return;
-  if (b0 + 16 <= nbytes) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(packed + b0));
-    const u32x2_t a = unpack_word(v.x), b = unpack_word(v.y), c = unpack_word(v.z),
-                  d = unpack_word(v.w);
-    u32x4_t o0, o1;
-    o0.x = a.x; o0.y = a.y; o0.z = b.x; o0.w = b.y;
-    o1.x = c.x; o1.y = c.y; o1.z = d.x; o1.w = d.y;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + 2 * b0);
-    __builtin_nontemporal_store(o0, dst);
-    __builtin_nontemporal_store(o1, dst + 1);
-  } else {
-    for (int64_t b = b0; b < nbytes; ++b) {
-      const uint32_t v = packed[b];
-      out[2 * b] = (int8_t)sx4(v & 0xFu);
-      out[2 * b + 1] = (int8_t)sx4(v >> 4);
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 1024;
+  if (base >= nbytes) return;
+  if (base + 1024 <= nbytes) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t b0 = base + 512 * h + 8 * lane;
+      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(packed + b0));
+      const u32x2_t a = unpack_word(v.x), b = unpack_word(v.y);
+      u32x4_t o;
+      o.x = a.x; o.y = a.y; o.z = b.x; o.w = b.y;
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + 2 * b0));
     }
+  } else {
+    for (int h = 0; h < 2; ++h)
+      for (int64_t b = base + 512 * h + 8 * lane; b < base + 512 * h + 8 * lane + 8 && b < nbytes; ++b) {
+        const uint32_t v = packed[b];
+        out[2 * b] = (int8_t)sx4(v & 0xFu);
+        out[2 * b + 1] = (int8_t)sx4(v >> 4);
+      }
   }
 }
 
@@ -70,8 +75,8 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* ou
                          hipStream_t stream) {
   if (K % 2 == 0 && ((uintptr_t)packed % 16) == 0 && ((uintptr_t)out % 16) == 0) {
     const int64_t nbytes = N * (K / 2);
-    const int64_t chunks = (nbytes + 15) / 16;
-    hipLaunchKernelGGL(unpack_flat_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+    const int64_t kb = (nbytes + 1023) / 1024;                 // one wavefront per KB
+    hipLaunchKernelGGL(unpack_flat_kernel, dim3((unsigned)((kb + 3) / 4)), dim3(256), 0,
                        stream, packed, nbytes, out);
   } else {
     const int64_t total = N * ((K + 1) / 2);
