@@ -82,6 +82,30 @@ __device__ __forceinline__ float run_max(float v) {
   return v;
 }
 
+// run_max for values that are +0 or positive and never NaN (absolute values
+// reduced with fmax from 0, which drops NaN operands): their binary32
+// patterns order like the values as unsigned integers, and 0 is the identity
+// of the unsigned max, so each butterfly step is one DPP max instruction.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return v > o ? v : o;
+}
+template <int LANES>
+__device__ __forceinline__ float run_max_abs(float a) {
+  uint32_t v = __builtin_bit_cast(uint32_t, a);
+  if constexpr (LANES >= 2) v = dpp_umax<0xB1>(v);
+  if constexpr (LANES >= 4) v = dpp_umax<0x4E>(v);
+  if constexpr (LANES >= 8) v = dpp_umax<0x141>(v);
+  if constexpr (LANES >= 16) v = dpp_umax<0x140>(v);
+#pragma unroll
+  for (int o = 16; o < LANES; o <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_xor((int)v, o);
+    v = v > u ? v : u;
+  }
+  return __builtin_bit_cast(float, v);
+}
+
 // LANES = group / 8, a power of two in [1, 64]. Grid: x covers the 512-code
 // segments of a row, four per block (one per wavefront); y walks the rows.
 template <int LANES>
@@ -108,15 +132,33 @@ __global__ __launch_bounds__(256) void quantize_vec_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    amax = run_max<LANES>(amax);
+    amax = run_max_abs<LANES>(amax);
 
     const float s32 = amax / 7.0f;
     const _Float16 s16 = (_Float16)s32;
     const float sf = (float)s16;
     const float rsf = scale_rcp(sf);
+    // code_of for the lane's 8 elements, with one branch around the divisions
+    // (each element is clamped on its own path, so no NaN quieting is needed
+    // where the two paths meet)
+    float c[8];
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = v[i] * rsf;
+      const float q = __builtin_rintf(t);
+      near |= __builtin_fabsf(__builtin_fabsf(t - q) - 0.5f) < 0x1p-14f;   // near_half_integer(t)
+      c[i] = __builtin_fminf(__builtin_fmaxf(q, -8.0f), 7.0f);
+    }
+    if (__builtin_expect(near, 0)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (near_half_integer(v[i] * rsf))
+          c[i] = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i] / sf), -8.0f), 7.0f);   // IEEE division
+    }
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= code_of(v[i], sf, rsf) << (4 * i);
+    for (int i = 0; i < 8; ++i) word |= ((uint32_t)(int)c[i] & 0xFu) << (4 * i);
     if (valid) {
       *reinterpret_cast<uint32_t*>(packed + n * (K >> 1) + (k >> 1)) = word;
       if ((lane & (LANES - 1)) == 0)
