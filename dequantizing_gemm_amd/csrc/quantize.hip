@@ -61,38 +61,22 @@ __device__ __forceinline__ uint32_t code_of(float w, float sf, float rsf) {
   return (uint32_t)(int)r & 0xFu;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  const float o = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-  return __builtin_fmaxf(v, o);
-}
-
-// Maximum of v over aligned runs of LANES lanes, in every lane of the run:
-// inside a 16-lane row a DPP butterfly (lanes i^1, i^2, then i <-> 7-i and
-// i <-> 15-i, which after the first two steps pair whole quads and halves),
-// across rows lane shuffles.
-template <int LANES>
-__device__ __forceinline__ float run_max(float v) {
-  if constexpr (LANES >= 2) v = dpp_max<0xB1>(v);      // quad_perm [1,0,3,2]
-  if constexpr (LANES >= 4) v = dpp_max<0x4E>(v);      // quad_perm [2,3,0,1]
-  if constexpr (LANES >= 8) v = dpp_max<0x141>(v);     // row_half_mirror
-  if constexpr (LANES >= 16) v = dpp_max<0x140>(v);    // row_mirror
-#pragma unroll
-  for (int o = 16; o < LANES; o <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// run_max for values that are +0 or positive and never NaN (absolute values
-// reduced with fmax from 0, which drops NaN operands): their binary32
-// patterns order like the values as unsigned integers, and 0 is the identity
-// of the unsigned max, so each butterfly step is one DPP max instruction.
+// Group extremes across lanes, as an unsigned maximum of binary32 patterns.
+// The lane values reduced here never are NaN (fmax / fmin from 0 drop NaN
+// operands) and have one sign: non-negative values (an absmax, or the upper
+// end of a range from 0) order like their patterns; non-positive values (the
+// lower end of a range from 0) order reversed, so their minimum has the
+// largest pattern. (For a lower end the result may be -0 where a float min
+// gives +0; the scale hi - lo and the zero point rint(-lo / s) are the same
+// either way.) 0 is the identity of the unsigned max, so each butterfly step
+// is one DPP max instruction.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
   const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
   return v > o ? v : o;
 }
 template <int LANES>
-__device__ __forceinline__ float run_max_abs(float a) {
+__device__ __forceinline__ float run_umax_bits(float a) {
   uint32_t v = __builtin_bit_cast(uint32_t, a);
   if constexpr (LANES >= 2) v = dpp_umax<0xB1>(v);
   if constexpr (LANES >= 4) v = dpp_umax<0x4E>(v);
@@ -132,7 +116,7 @@ __global__ __launch_bounds__(256) void quantize_vec_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    amax = run_max_abs<LANES>(amax);
+    amax = run_umax_bits<LANES>(amax);
 
     const float s32 = amax / 7.0f;
     const _Float16 s16 = (_Float16)s32;
@@ -238,23 +222,6 @@ __device__ __forceinline__ uint32_t affine_code(float w, float sf, float rsf, ui
   return (uint32_t)r;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_min(float v) {
-  const float o = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-  return __builtin_fminf(v, o);
-}
-
-template <int LANES>
-__device__ __forceinline__ float run_min(float v) {
-  if constexpr (LANES >= 2) v = dpp_min<0xB1>(v);
-  if constexpr (LANES >= 4) v = dpp_min<0x4E>(v);
-  if constexpr (LANES >= 8) v = dpp_min<0x141>(v);
-  if constexpr (LANES >= 16) v = dpp_min<0x140>(v);
-#pragma unroll
-  for (int o = 16; o < LANES; o <<= 1) v = __builtin_fminf(v, __shfl_xor(v, o));
-  return v;
-}
-
 template <int LANES>
 __global__ __launch_bounds__(256) void quantize_affine_vec_kernel(
     const float* __restrict__ w, int64_t N, int64_t K, int64_t G, int64_t segs_per_row,
@@ -282,15 +249,31 @@ __global__ __launch_bounds__(256) void quantize_affine_vec_kernel(
       lo = __builtin_fminf(lo, v[i]);
       hi = __builtin_fmaxf(hi, v[i]);
     }
-    lo = run_min<LANES>(lo);
-    hi = run_max<LANES>(hi);
+    lo = run_umax_bits<LANES>(lo);
+    hi = run_umax_bits<LANES>(hi);
     const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
     const float sf = (float)s16;
     const float rsf = scale_rcp(sf);
     const uint32_t zp = affine_zp(lo, sf);
+    // affine_code for the lane's 8 elements, with one branch around the
+    // divisions (each element is clamped on its own path)
+    float c[8];
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = v[i] * rsf;
+      const float q = __builtin_rintf(t);
+      near |= __builtin_fabsf(__builtin_fabsf(t - q) - 0.5f) < 0x1p-14f;   // near_half_integer(t)
+      c[i] = __builtin_fminf(__builtin_fmaxf(q + (float)zp, 0.0f), 15.0f);
+    }
+    if (__builtin_expect(near, 0)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (near_half_integer(v[i] * rsf)) c[i] = (float)affine_code(v[i], sf, rsf, zp);
+    }
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= affine_code(v[i], sf, rsf, zp) << (4 * i);
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)c[i] << (4 * i);
     if (valid) {
       *reinterpret_cast<uint32_t*>(packed + n * (K >> 1) + (k >> 1)) = word;
       if ((lane & (LANES - 1)) == 0) {
