@@ -226,7 +226,7 @@ int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uin
     case INT4DQ_PATH_GEMV: {
       const char* why = int4dq::matmul_gemv_unsupported(x_dtype, M, x, packed, N, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "%s: %s", fn, why);
-      return hip_status(int4dq::launch_matmul_gemv(x, packed, scales, zeros, N, K, group, y, ep, s),
+      return hip_status(int4dq::launch_matmul_gemv(x, M, packed, scales, zeros, N, K, group, y, ep, s),
                         "int4_matmul gemv launch");
     }
     case INT4DQ_PATH_TILED: {

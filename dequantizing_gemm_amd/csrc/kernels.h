@@ -67,7 +67,7 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
 
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
                                     const uint8_t* packed, int64_t N, int64_t K, int64_t group);
-hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
+hipError_t launch_matmul_gemv(const void* x, int64_t M, const uint8_t* packed, const uint16_t* scales,
                               const uint8_t* zeros, int64_t N, int64_t K, int64_t group, void* y, Epilogue ep,
                               hipStream_t stream);
 

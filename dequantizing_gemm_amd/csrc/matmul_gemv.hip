@@ -1,5 +1,6 @@
-// matmul_gemv.hip -- dequantizing matrix-vector product (one activation row,
-// binary16 x) on gfx950: a weight-streaming kernel bound by HBM bandwidth.
+// matmul_gemv.hip -- dequantizing matrix-vector product (one to four
+// activation rows, binary16 x) on gfx950: weight-streaming kernels bound by
+// HBM bandwidth.
 //
 // Definition (drill page "Implement INT4 group quantization, nibble packing
 // and a dequantizing matmul", statement, int4_matmul): y = x @ dequantize(W).T,
@@ -17,6 +18,9 @@
 //    4x4x4 MFMAs used on their diagonal (matmul_gemv_rows_kernel, below);
 //  * K <= 12288 with group = 32 << p: 4 rows x 256 bytes per load, which is
 //    directly the B operand of v_mfma_f32_4x4x4f16 (matmul_gemv_mfma_kernel);
+//    this variant alone also takes 2 to 4 activation rows, as the four rows
+//    of the MFMA's A operand (the loads, code expansions and MFMAs are those
+//    of one row);
 //  * everything else (K <= 32768, group a multiple of 32): the VALU kernel
 //    that follows, where a wavefront load covers 1 KB of one weight row
 //    (lane l: bytes c*1024 + 16 l):
@@ -206,9 +210,14 @@ __global__ __launch_bounds__(64 * kGemvMaxChunks) void matmul_gemv_kernel(
 // entries each thread stages.
 // KSP: wavefronts per group of 4 rows, each taking CM / KSP of the column
 // blocks; their partial sums are added through LDS in a fixed order.
-template <int CM, int GS, int W, bool AFF, int KSP = 1>
+// MR: rows of x staged (1, or 4 for M = 2 .. 4). Lane 4b+i supplies row i of
+// block b's A, so with MR = 4 the A rows are x rows 0 .. 3 (rows >= M are
+// zeros) and D[i][j] -- register i of lane 4b+j -- is x row i times weight
+// row j: the same loads, expansions and MFMAs give up to four outputs per
+// weight row.
+template <int CM, int GS, int W, bool AFF, int KSP = 1, int MR = 1>
 __global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
-    const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
+    const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
     int group, int gsh, void* __restrict__ y, Epilogue ep) {
   typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -216,7 +225,8 @@ __global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
   static_assert(CM % KSP == 0, "column split");
   constexpr int CMP = CM / KSP;                // column blocks per wavefront
   constexpr int NT = 64 * W * KSP, ROWS = 4 * W;   // threads, rows per block
-  constexpr int XPT = (CM * 64 + NT - 1) / NT; // 16-byte x units per thread (x row <= CM KB)
+  constexpr int XU = CM * 64;                  // 16-byte x units per staged row (x row <= CM KB)
+  constexpr int XPT = (MR * XU + NT - 1) / NT; // x units per thread
   constexpr int GMAX = (CM * 16 + (1 << GS) - 1) >> GS;           // groups per row, at most
   constexpr int SPT = (ROWS * GMAX + NT - 1) / NT;                 // scale entries per thread
   // Sized so that every thread's staging store is in bounds (no branch: a
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t xsp[XPT * NT * 4];   // x, spread order
   __shared__ uint16_t ssh[SPT * NT];                                  // scales of the block's rows
   __shared__ uint8_t zsh[AFF ? SPT * NT : 1];                         // their zero points
-  __shared__ float part_sum[KSP > 1 ? KSP * ROWS : 1];
+  __shared__ float part_sum[KSP > 1 ? KSP * ROWS * MR : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -235,12 +245,15 @@ __global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
   const int xunits = K >> 3;                   // 8 activations per unit
 
   // Phase 1: activations and scales (older than every weight load).
+  // unit u of the staging: row u / XU, unit u % XU of that row (past the row
+  // end or past row M-1: unit 0 of x, stored as zeros below)
   u32x4_t xv[XPT];
 #pragma unroll
   for (int t = 0; t < XPT; ++t) {
-    int u = t * NT + tid;
-    u = u < xunits ? u : xunits - 1;
-    xv[t] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(x) + 16u * (uint32_t)u);
+    const int u = t * NT + tid;
+    const int m = u / XU, uu = u - m * XU;
+    const int src = m < M && uu < xunits ? m * xunits + uu : 0;
+    xv[t] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(x) + 16u * (uint32_t)src);
   }
   // the block's rows' scales are contiguous from row n0 (rows past N: clamped)
   const uint16_t* sblk = scales + (int64_t)n0 * G;
@@ -276,9 +289,10 @@ __global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < XPT; ++t) {
     const int u = t * NT + tid;
-    // units past the end of x are stored as zeros: lanes past a row's end
-    // then contribute exactly 0 without a mask
-    const uint32_t z = u < xunits ? 0xFFFFFFFFu : 0u;
+    const int m = u / XU, uu = u - m * XU;
+    // units past the end of x (or of its M rows) are stored as zeros: lanes
+    // past a row's end then contribute exactly 0 without a mask
+    const uint32_t z = m < M && uu < xunits ? 0xFFFFFFFFu : 0u;
     u32x4_t sp;
     sp.x = __builtin_amdgcn_perm(xv[t].z, xv[t].x, 0x05040100u) & z;
     sp.y = __builtin_amdgcn_perm(xv[t].z, xv[t].x, 0x07060302u) & z;
@@ -301,8 +315,10 @@ __global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
   // past the row end read x units past K, which are zero.
   const uint16_t* srow = ssh + (4 * wave + j) * G + (b >> gsh);
   const uint8_t* zrow = zsh + (AFF ? (4 * wave + j) * G + (b >> gsh) : 0);
-  const uint32_t* xl = xsp + 16 * b;
-  float acc = 0.0f;
+  const uint32_t* xl = xsp + 16 * b + (MR > 1 ? j * XU * 4 : 0);   // x row j of A (row 0 if MR = 1)
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
   static_for<0, CMP>([&](auto C_) {
     constexpr int c = decltype(C_)::value;
     const int cg = part * CMP + c;             // column block in the row
@@ -325,20 +341,39 @@ __global__ __launch_bounds__(64 * W * KSP) void matmul_gemv_mfma_kernel(
       d = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d, 0, 0, 0);
       d = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d, 0, 0, 0);
     }
-    acc += sc * d.x;                           // row 0 of the block: the activation row
+    // register m of D: x row m (row 0 of the block's A when MR = 1)
+    acc[0] += sc * d.x;
+    if constexpr (MR > 1) {
+      acc[1] += sc * d.y;
+      acc[2] += sc * d.z;
+      acc[3] += sc * d.w;
+    }
   });
   // Sum the 16 slices (lanes 4b+j, b = 0..15) of each of the 4 rows.
 #pragma unroll
-  for (int off = 4; off < 64; off <<= 1) acc += __shfl_xor(acc, off);
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
   if constexpr (KSP > 1) {
-    if (b == 0) part_sum[part * ROWS + 4 * wave + j] = acc;
+    if (b == 0) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) part_sum[(part * ROWS + 4 * wave + j) * MR + m] = acc[m];
+    }
     __syncthreads();
     if (part != 0) return;
-    acc = part_sum[4 * wave + j];
 #pragma unroll
-    for (int p = 1; p < KSP; ++p) acc += part_sum[p * ROWS + 4 * wave + j];
+    for (int m = 0; m < MR; ++m) {
+      acc[m] = part_sum[(4 * wave + j) * MR + m];
+#pragma unroll
+      for (int p = 1; p < KSP; ++p) acc[m] += part_sum[(p * ROWS + 4 * wave + j) * MR + m];
+    }
   }
-  if (b == 0 && n0 + 4 * wave + j < N) ep.store(y, n0 + 4 * wave + j, acc, n0 + 4 * wave + j);
+  const int nrow = n0 + 4 * wave + j;
+  if (b == 0 && nrow < N) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      if (m < M) ep.store(y, (int64_t)m * N + nrow, acc[m], nrow);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -495,7 +530,9 @@ const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
                                     const uint8_t* packed, int64_t N, int64_t K,
                                     int64_t group) {
   if (x_dtype != 1) return "gemv kernel takes binary16 activations only";
-  if (M != 1) return "gemv kernel takes M = 1";
+  if (M < 1 || M > 4) return "gemv kernel takes 1 <= M <= 4";
+  if (M > 1 && (K > 12288 || group % 32 != 0 || ((group / 32) & (group / 32 - 1)) != 0))
+    return "gemv kernel takes M = 2 .. 4 only with K <= 12288 and group = 32 * 2^p";
   if (group % 32 != 0) return "gemv kernel needs group to be a multiple of 32";
   if (K % 32 != 0) return "gemv kernel needs K to be a multiple of 32";
   if (K / 2 > 1024 * kGemvMaxChunks) return "gemv kernel takes K <= 32768";
@@ -505,7 +542,7 @@ const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
 }
 
 template <bool AFF>
-static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint16_t* scales,
+static void launch_gemv_t(const _Float16* xh0, int64_t M, const uint8_t* packed, const uint16_t* scales,
                           const uint8_t* zeros, int64_t N, int64_t K, int64_t group, void* y,
                           Epilogue ep, hipStream_t stream) {
   const int G = (int)((K + group - 1) / group);
@@ -513,6 +550,34 @@ static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint
   while ((32ll << gsh) < group) ++gsh;
   if ((32ll << gsh) != group) gsh = -1;
   const int chunks = (int)((K / 2 + 1023) / 1024);            // 1 KB chunks per row
+  const int cols = (int)((K / 2 + 255) / 256);                // 256-byte column blocks per row
+  if (M > 1) {
+    // M = 2 .. 4 (K <= 12288, group 32 << gsh): the matrix-core variant with
+    // four x rows in A. Blocks of 4 groups of 4 rows (x, up to 96 KB of it in
+    // LDS, is staged once for 16 rows), column blocks split over two
+    // wavefronts for rows of 16 or more.
+#define INT4DQ_GEMV_MFMA4(CMV)                                                                   \
+  do {                                                                                          \
+    constexpr int KS = CMV >= 16 ? 2 : 1, W = 4;                                                \
+    const dim3 grid((unsigned)((N + 4 * W - 1) / (4 * W))), block(64 * W * KS);                \
+    const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<CMV, 0, W, AFF, KS, 4>                 \
+                    : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, W, AFF, KS, 4>                 \
+                    : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, W, AFF, KS, 4>                 \
+                               : matmul_gemv_mfma_kernel<CMV, 3, W, AFF, KS, 4>;                \
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, (int)M, packed, scales, zeros, (int)N, \
+                       (int)K, G, (int)group, gsh, y, ep);                                      \
+  } while (0)
+    if (cols <= 2) INT4DQ_GEMV_MFMA4(2);
+    else if (cols <= 4) INT4DQ_GEMV_MFMA4(4);
+    else if (cols <= 6) INT4DQ_GEMV_MFMA4(6);
+    else if (cols <= 8) INT4DQ_GEMV_MFMA4(8);
+    else if (cols <= 12) INT4DQ_GEMV_MFMA4(12);
+    else if (cols <= 16) INT4DQ_GEMV_MFMA4(16);
+    else if (cols <= 22) INT4DQ_GEMV_MFMA4(22);
+    else INT4DQ_GEMV_MFMA4(24);
+#undef INT4DQ_GEMV_MFMA4
+    return;
+  }
   // (the AFF form with 8 chunks would exceed 256 VGPRs and spill: it takes the
   // variants below)
   if (N * (K / 2) >= (48ll << 20) && chunks <= (AFF ? 7 : 8)) {
@@ -539,7 +604,6 @@ static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint
 #undef INT4DQ_GEMV_ROWS
     return;
   }
-  const int cols = (int)((K / 2 + 255) / 256);                // 256-byte column blocks per row
   if (cols <= 24 && gsh >= 0 && g_gemv_mfma) {
     // Rows of 16 or more column blocks (K >= 7680) split each row's columns
     // over two wavefronts (blocks of 2 x 2 wavefronts, 8 rows): their chains
@@ -555,8 +619,8 @@ static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint
                     : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, W, AFF, KS>                    \
                     : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, W, AFF, KS>                    \
                                : matmul_gemv_mfma_kernel<CMV, 3, W, AFF, KS>;                   \
-    hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, packed, scales, zeros, (int)N, (int)K, \
-                       G, (int)group, gsh, y, ep);                                              \
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, 1, packed, scales, zeros, (int)N,     \
+                       (int)K, G, (int)group, gsh, y, ep);                                      \
   } while (0)
     if (cols <= 2) INT4DQ_GEMV_MFMA(2);
     else if (cols <= 4) INT4DQ_GEMV_MFMA(4);
@@ -581,12 +645,12 @@ static void launch_gemv_t(const _Float16* xh0, const uint8_t* packed, const uint
                      (int)group, gsh, y, ep);
 }
 
-hipError_t launch_matmul_gemv(const void* x, const uint8_t* packed, const uint16_t* scales,
+hipError_t launch_matmul_gemv(const void* x, int64_t M, const uint8_t* packed, const uint16_t* scales,
                               const uint8_t* zeros, int64_t N, int64_t K, int64_t group, void* y,
                               Epilogue ep, hipStream_t stream) {
   const _Float16* xh = static_cast<const _Float16*>(x);
-  if (zeros) launch_gemv_t<true>(xh, packed, scales, zeros, N, K, group, y, ep, stream);
-  else launch_gemv_t<false>(xh, packed, scales, zeros, N, K, group, y, ep, stream);
+  if (zeros) launch_gemv_t<true>(xh, M, packed, scales, zeros, N, K, group, y, ep, stream);
+  else launch_gemv_t<false>(xh, M, packed, scales, zeros, N, K, group, y, ep, stream);
   return hipGetLastError();
 }
 

@@ -69,7 +69,8 @@ extern "C" {
 #define INT4DQ_PATH_GENERIC 1  /* VALU kernel, any shape, any group, fp32 or fp16 x */
 #define INT4DQ_PATH_SKINNY  2  /* M <= 64, fp16 x: weight-streaming MFMA kernel */
 #define INT4DQ_PATH_TILED   3  /* any M, fp16 x: LDS-tiled MFMA kernel */
-#define INT4DQ_PATH_GEMV    4  /* M = 1, fp16 x, group and K multiples of 32: row-streaming kernel */
+#define INT4DQ_PATH_GEMV    4  /* fp16 x, group and K multiples of 32, M = 1; or M <= 4 with K <= 12288
+                                   and group = 32 * 2^p: weight-streaming kernels */
 
 /*
  * Number of scale groups per row, G = ceil(K / group) (drill page,

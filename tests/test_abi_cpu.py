@@ -186,7 +186,10 @@ def test_kernel_selection_rules():
         ctypes.c_void_p(x), xd, M, ctypes.c_void_p(p), FAKE, N, K, g, FAKE)
     P = dq.PATHS
     assert sel(1, 1, 4096, 128) == P["gemv"] and sel(1, 16, 4096, 128) == P["skinny"]
-    assert sel(1, 2, 4096, 128) == P["skinny"] and sel(1, 1, 11008, 128) == P["gemv"]
+    assert sel(1, 2, 4096, 128) == P["gemv"] and sel(1, 1, 11008, 128) == P["gemv"]
+    # 2-4 rows: the matrix-core gemv while K <= 12288 and group = 32 * 2^p
+    assert sel(1, 4, 12288, 128) == P["gemv"] and sel(1, 4, 12416, 128) == P["skinny"]
+    assert sel(1, 5, 4096, 128) == P["skinny"] and sel(1, 3, 4096, 96) == P["generic"]
     assert sel(1, 1, 768, 32) == P["gemv"] and sel(1, 1, 768, 64) == P["gemv"]
     assert sel(1, 1, 4096, 16) == P["generic"]                 # group not a multiple of 32
     assert sel(1, 1, 65536, 128) == P["tiled"]                 # K beyond the gemv and skinny kernels
@@ -198,7 +201,7 @@ def test_kernel_selection_rules():
     assert sel(1, 17, 8192, 128, N=28672) == P["tiled"] and sel(1, 16, 8192, 128, N=28672) == P["skinny"]
     # four row tiles do not take more than 96 K-blocks
     assert sel(1, 40, 16384, 128) == P["tiled"] and sel(1, 20, 16384, 128) == P["skinny"]
-    assert sel(1, 4, 768, 64) == P["skinny"] and sel(1, 4, 768, 32) == P["skinny"]
+    assert sel(1, 4, 768, 64) == P["gemv"] and sel(1, 4, 768, 32) == P["gemv"]
     assert sel(0, 4, 256, 128) == P["generic"]                 # binary32 x
     assert sel(1, 3, 301, 128) == P["generic"]                 # odd K
     assert sel(1, 4, 768, 96) == P["generic"]                  # group not 32/64/128k

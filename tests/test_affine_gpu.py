@@ -140,6 +140,9 @@ MM = [
     (12300, 8224, 32, 1, "gemv"),     # whole-row gemv (>= 48 MB)
     (24577, 4096, 96, 1, "gemv"),     # whole-row gemv, group 96
     (6700, 16384, 256, 1, "gemv"),    # 8 chunks per row: the VALU gemv for affine codes
+    (300, 4096, 128, 3, "gemv"),      # MFMA gemv, four x rows in A (rows past M zero)
+    (301, 8192, 64, 4, "gemv"),       # ... with the column split
+    (513, 2080, 32, 2, "gemv"),       # ... ragged column blocks
     (200, 768, 32, 2, "skinny"),      # staged x, spread order
     (200, 1024, 128, 4, "skinny"),
     (200, 768, 64, 5, "skinny"),      # direct x loads

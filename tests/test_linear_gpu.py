@@ -80,7 +80,7 @@ def test_layer_matches_oracle(L, affine, out_dtype):
     assert np.array_equal(layer.scales.cpu().numpy().view(np.uint16), s.view(np.uint16))
     if affine:
         assert np.array_equal(host(layer.zeros), z)
-    for M in (1, 5, 16, 40, 300):
+    for M in (1, 3, 5, 16, 40, 300):
         x = np.random.default_rng(M).normal(size=(M, K)).astype(np.float16)
         y = layer(dev(x))
         assert y.dtype == out_dtype and tuple(y.shape) == (M, N)

@@ -22,6 +22,15 @@ TOL = 2e-3
 ORACLE_MACS = 3e8          # per matmul check; beyond this the outputs are sampled
 
 
+def gemv_takes(M, K, g):
+    """Whether the gemv path takes M rows (M = 1 always; 2 .. 4 with K <= 12288
+    and group 32 * 2^p)."""
+    if M == 1:
+        return True
+    q, r = divmod(g, 32)
+    return 2 <= M <= 4 and K <= 12288 and r == 0 and q & (q - 1) == 0
+
+
 @pytest.fixture(scope="module")
 def dq():
     import dequantizing_gemm_amd as dq
@@ -295,7 +304,7 @@ def test_matmul_kernels_agree(dq, N, K, g, M):
     pd, sd, xd = dev(pr), dev(sr), dev(x)
     for path in ("generic", "skinny", "tiled", "gemv"):
         if (path == "skinny" and (M > 64 or (M > 32 and K // min(g, 128) > 96))) or \
-                (path == "gemv" and M != 1):
+                (path == "gemv" and not gemv_takes(M, K, g)):
             continue
         say(f"case: kernel {path} N={N} K={K} g={g} M={M}")
         y = host(dq.int4_matmul_path(xd, pd, sd, K, g, path))
@@ -320,6 +329,47 @@ def test_matmul_gemv_shapes(dq, N, K, g):
     assert dq.matmul_select(xd, pd, sd, K, g) == "gemv"
     y = host(dq.int4_matmul_path(xd, pd, sd, K, g, "gemv"))
     check_matmul(y, x, pr, sr, K, g, what=f"gemv {N}x{K}")
+
+
+@pytest.mark.parametrize("N,K,g,M", [(300, 11008, 128, 4), (4099, 4096, 128, 2), (513, 2080, 32, 3),
+                                     (77, 7680, 256, 4), (10, 32, 32, 3), (8200, 12288, 64, 4),
+                                     (2051, 2048, 128, 3), (28672, 8192, 128, 4), (40, 768, 32, 2)])
+def test_matmul_gemv_multi_row(dq, N, K, g, M):
+    """M = 2 .. 4 through the matrix-core gemv (four x rows in A, rows past M
+    zero): column splits for rows of 16 or more column blocks (K = 7680 ..
+    12288), a partial last column block (K = 2080), the smallest K (one
+    lane), the largest (24 column blocks), N tails, the c5 matrix."""
+    say(f"case: gemv M={M} N={N} K={K} g={g}")
+    w = np.random.default_rng(N + K + M).normal(0, 0.02, size=(N, K)).astype(np.float32)
+    x = np.random.default_rng(K + M).normal(size=(M, K)).astype(np.float16)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    pd, sd, xd = dev(pr), dev(sr), dev(x)
+    assert dq.matmul_select(xd, pd, sd, K, g) == "gemv"
+    y = host(dq.int4_matmul_path(xd, pd, sd, K, g, "gemv"))
+    if N * K > 64 << 20:                       # the oracle on sampled columns
+        cols = np.random.default_rng(1).choice(N, 256, replace=False)
+        check_matmul(y[:, cols], x, pr[cols], sr[cols], K, g, what=f"gemv M={M} {N}x{K}")
+    else:
+        check_matmul(y, x, pr, sr, K, g, what=f"gemv M={M} {N}x{K}")
+
+
+def test_matmul_gemv_multi_row_one_hot_exact(dq):
+    """Four one-hot rows of x through the M = 2 .. 4 gemv: row m of y is
+    column k_m of (q * scale)^T bit-exactly (one exact product per output)."""
+    for (N, K, g) in [(48, 4096, 128), (300, 11008, 128), (32, 768, 32)]:
+        say(f"case: gemv multi-row one-hot N={N} K={K} g={g}")
+        w = np.random.default_rng(K + 1).normal(size=(N, K)).astype(np.float32)
+        pr, sr, _ = oracle.quantize_int4(w, g)
+        what = (oracle.unpack_int4(pr, K).astype(np.float64) *
+                np.repeat(sr.astype(np.float64), g, 1)[:, :K]).T
+        ks = [0, 33, K // 2 + 7, K - 1]
+        for M in (2, 3, 4):
+            e = np.zeros((M, K), dtype=np.float16)
+            for m in range(M):
+                e[m, ks[m]] = 1.0
+            y = host(dq.int4_matmul_path(dev(e), dev(pr), dev(sr), K, g, "gemv"))
+            for m in range(M):
+                assert np.array_equal(y[m].astype(np.float64), what[ks[m]]), f"M={M} m={m}"
 
 
 def test_matmul_gemv_one_hot_exact(dq):
@@ -358,7 +408,8 @@ def test_matmul_gemv_rows_one_hot_exact(dq):
 
 @pytest.mark.parametrize("N,K,g,M,path", [(300, 1024, 128, 1, "gemv"), (200, 768, 32, 1, "gemv"),
                                           (12300, 8224, 32, 1, "gemv"), (77, 4096, 96, 1, "gemv"),
-                                          (301, 11008, 128, 1, "gemv"),
+                                          (301, 11008, 128, 1, "gemv"), (300, 1024, 128, 3, "gemv"),
+                                          (301, 11008, 128, 4, "gemv"),
                                           (200, 768, 64, 5, "skinny"), (48, 4096, 128, 16, "skinny"),
                                           (300, 4096, 128, 64, "skinny"), (8200, 1024, 64, 24, "skinny"),
                                           (300, 1024, 128, 130, "tiled"), (129, 256, 32, 600, "tiled"),
@@ -426,9 +477,9 @@ def test_matmul_zero_and_empty(dq):
     w = np.random.default_rng(1).normal(size=(64, 512)).astype(np.float32)
     pr, sr, _ = oracle.quantize_int4(w, 128)
     pd, sd = dev(pr), dev(sr)
-    for M in (1, 16, 300):
+    for M in (1, 3, 16, 300):
         for path in ("skinny", "tiled", "generic", "gemv"):
-            if (path == "skinny" and M > 16) or (path == "gemv" and M != 1):
+            if (path == "skinny" and M > 16) or (path == "gemv" and not gemv_takes(M, 512, 128)):
                 continue
             y = host(dq.int4_matmul_path(torch.zeros(M, 512, dtype=torch.float16, device=DEV), pd, sd, 512, 128, path))
             assert np.all(y == 0)
