@@ -519,6 +519,15 @@ def main():
     if not args.no_unfused:
         print("bench: fused vs dequantize-then-GEMM", file=sys.stderr, flush=True)
         line["unfused_baseline"] = unfused_comparison(mats, pool)
+        # Context for the prefill fraction: the library's plain fp16 GEMM on
+        # the same three shapes at M = 2048 (fp16 weights, fp16 output), timed
+        # in the same run; the fused kernel's rate as a fraction of it.
+        flops = sum(2.0 * M_PREFILL * m["N"] * m["K"] for m in mats)
+        lib_tf = flops / line["unfused_baseline"]["m2048"]["gemm_us"] / 1e6
+        line["library_fp16_gemm_m2048"] = {
+            "tflops": round(lib_tf, 1), "frac_of_peak": round(lib_tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "fused_frac_of_library": round(roofs[3]["achieved"] / lib_tf, 4),
+            "note": "F.linear (hipBLASLt) on the same three shapes, fp16 weights and output"}
     if not args.no_gates:
         print("bench: gated cases", file=sys.stderr, flush=True)
         line["gated_cases"] = gated_cases(mats, pool, dev)
