@@ -2,16 +2,16 @@
 // x) on gfx950: an MFMA kernel bound by matrix-core throughput.
 //
 // Definition (drill page "Implement INT4 group quantization, nibble packing
-// and a dequantizing matmul", statement, int4_matmul): y = x @ dequantize(W).T,
-// one group at a time -- x times the group's integer codes first, then the
-// group's scale on each output column. Full-precision weights never reach
+// and a dequantizing matmul", statement, int4_matmul): y = x @ dequantize(W).T
+// with dequantize(W) = q * scale per group. Full-precision weights never reach
 // memory ("Build a Blockwise INT4 Inference Engine", architecture overview:
-// the fusion boundary); here they exist only as exact fp16 integer codes in
-// registers, one MFMA k-step at a time.
+// the fusion boundary); here they exist only in registers, one MFMA k-step at
+// a time, as binary16 products q * scale of the exact integer codes and their
+// group's scale (one rounding each, at most 2^-11 relative).
 //
 // Block tile 128 (rows of x) x 256 (weight rows), 256 threads = 4 wavefronts
 // side by side along N, one per SIMD, each owning 128 x 64 outputs as 4 x 2
-// tiles of v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 VGPRs). The
+// tiles of v_mfma_f32_32x32x16_f16 (fp32 accumulation in 128 AGPRs). The
 // global -> LDS bytes per sub-step are 16 KB of x and 8 KB of packed weights
 // (a 256 x 128 tile moves 32 KB + 4 KB for the same flops). For fewer rows of
 // x the block is 128 x 128, 64 x 128 or 32 x 128 with wave tiles one MFMA
@@ -25,8 +25,9 @@
 //    (256 codes) of each of the block's weight rows: eight lanes cover a full
 //    128-byte line, and a 2-slot ring loads super-tile j+1 while j is used.
 //  * Each wavefront reads its own packed words (one 16-byte read per 32-column
-//    tile per sub-step) and expands them to exact fp16 codes in registers
-//    (codes_to_half_natural) right before the MFMAs that use them.
+//    tile per sub-step), expands them to exact fp16 codes in registers
+//    (codes_to_half_natural) and multiplies each pair by its group's scale
+//    (one packed fp16 multiply) right before the MFMAs that use them.
 //  * The k order inside a sub-step is a fixed permutation shared by A and B
 //    (lane half h, k-step s: codes (BK/2) h + 8 s .. +7), so each lane's
 //    packed bytes for a sub-step are contiguous and the dot product is
@@ -39,14 +40,11 @@
 //    the end of sub-step t-1, so the MFMA pipe does not wait for LDS after the
 //    barrier; the barrier of sub-step t therefore makes the data of t+1
 //    visible (it waits for the loads issued two sub-steps earlier).
-//  * Integer-first scaling with one accumulator set: the accumulator holds
-//    (sum of finished groups' scaled partials) / (scale of the current group);
-//    at each group boundary it is multiplied by s_prev / s_new for its column
-//    (done at the end of the group's last sub-step, overlapping the last
-//    MFMAs), the group's integer products are accumulated by the MFMAs, and
-//    the final value is multiplied by the last scale. A zero scale (a group of
-//    zero codes) leaves the running scale unchanged. Mathematically this is
-//    sum_g s_g * (x . q_g); the ratio multiply adds one fp32 rounding per group.
+//  * The scale enters with the codes, so the accumulators are never read or
+//    rescaled inside the loop (they stay in AGPRs); a group boundary only
+//    switches the scale word of each column. A scale too large for the
+//    binary16 product (above 8188) sends the block through two more passes
+//    with the exponent shifted, described at the passes below.
 //  * Each sub-step waits for exactly the loads issued two sub-steps earlier
 //    (counts known at compile time; the loop is unrolled over two super-tiles
 //    so every stage and slot index is a constant), then one LDS-only barrier.
@@ -54,7 +52,8 @@
 //  * Affine codes ("Build a Blockwise INT4 Inference Engine", step 2; the AFF
 //    form): each group's zero point is loaded with its scale, and its bias
 //    word (codes_to_half_natural_zp) is switched at the group boundary
-//    together with the running scale, so the codes expand to u - zp exactly.
+//    together with the scale, so the codes expand to u - zp exactly before
+//    the multiply.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -89,7 +88,7 @@ constexpr int kThreads = 256;
 // tiles per wavefront in M and N. WN: wavefronts side by side along N (4, or
 // 2 for 2 x 2 wavefronts). Block tile (32 TM * 4 / WN) x (32 TN * WN). The
 // launcher uses WN = 4 with (TM, TN) = (4, 2), (4, 1), (2, 1) and (1, 1).
-template <int BK, int SPG, int TM, bool AFF, int WN, int TN>
+template <int BK, int SPG, int TM, bool AFF, int WN, int TN, int NXS_ = 4, int WS_ = 2>
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
@@ -104,8 +103,8 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   // x ring stages and prefetch distance; packed super-tile slots. (Deeper
   // rings for the small tiles -- 8 stages, 4 slots -- measured no faster: with
   // 64-row tiles a block is bound by its own instruction stream, not latency.)
-  constexpr int NXS = 4, D = NXS - 1;
-  constexpr int WS = 2;
+  constexpr int NXS = NXS_, D = NXS - 1;
+  constexpr int WS = WS_;
   constexpr int A_BYTES = BM * BK * 2;         // one x stage
   constexpr int XDMA = BM * PIECES / (64 * NW);// x DMA instructions per wave per sub-step
   constexpr int RPI = 64 / PIECES;             // x rows per DMA instruction
@@ -132,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   // still be in flight.
   constexpr auto newer_loads = [group_loads](int j) {
     int n = 0;
-    for (int i = 1; i <= D - 2; ++i) n += group_loads(j - i);
+    for (int i = 0; i <= D - 2; ++i) n += group_loads(j - i);
     return n;
   };
 
@@ -248,193 +247,287 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     return (wn * WNT + b * 32 + c32) * 128 + 16 * ((byte >> 4) ^ wsw) + (byte & 15);
   };
 
+  // Each code is multiplied by its group's binary16 scale as it is expanded:
+  // w_hat = q * scale rounded once to binary16 (exact whenever the product
+  // fits 11 significant bits; a relative error of at most 2^-11 otherwise,
+  // subnormal products included), so the MFMAs accumulate x . w_hat directly
+  // and no accumulator is touched at a group boundary. A zero scale makes its
+  // group contribute nothing, whatever its codes.
+  // That needs |q * scale| <= 65504: every scale at most 8188 (4094 for affine
+  // codes, whose integer weights reach 15). A block that meets a larger (or
+  // non-finite) scale in its columns discards its first pass and makes two
+  // more over K: one with only the large-scale groups, their scales
+  // multiplied by 2^-16 (an exponent shift: exact, and normal since the scale
+  // is at least 4096), whose sums are then multiplied by 2^16, and one adding
+  // the other groups at their own scales. Every product keeps its single
+  // binary16 rounding; only the sum order changes.
+  // Pass modes: 0 every group as is; 1 the groups with small scales only; 2
+  // the groups with large scales only, scaled by 2^-16.
+  constexpr uint32_t kSafe = AFF ? 0x6BFFu : 0x6FFFu;   // largest scale bits without overflow
+
   float16_t acc[TM][TN];
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-  float srun[TN];
-  uint32_t zb[TN];                             // bias word of the current group (AFF)
-#pragma unroll
-  for (int b = 0; b < TN; ++b) srun[b] = 0.0f, zb[b] = 0u;
+  uint32_t big = 0;                            // a scale above kSafe was seen (mode 0)
 
-  half8_t af[TM];                              // A fragments of the next k-step
-  uint32_t wp[TN][KS];                         // packed words of the current sub-step
-  auto read_a = [&](int stage, int s, half8_t* dst) {
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-      dst[a] = *reinterpret_cast<const half8_t*>(lds + stage * A_BYTES + aoff[s] + a * 32 * BK * 2);
-  };
-  auto read_w = [&](int slot, int u, uint32_t (*dst)[KS]) {
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const uint8_t* p = lds + W_LDS + slot * W_BYTES + woff(u, b);
-      if constexpr (BK == 64) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-        dst[b][0] = v.x; dst[b][1] = v.y; dst[b][2] = v.z; dst[b][3] = v.w;
-      } else {
-        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-        dst[b][0] = v.x; dst[b][1] = v.y;
-      }
-    }
-  };
-  auto expand_b = [&](const uint32_t (*w)[KS], int s, half8_t* bf) {
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      half2_t hw[4];
-      if constexpr (AFF) codes_to_half_natural_zp(w[b][s], hw, zb[b]);
-      else codes_to_half_natural(w[b][s], hw);
-      bf[b] = as_half8(hw);
-    }
+  // Scale word (the group's factor twice, binary16) of a column whose scale
+  // has bits sb, in pass mode `mode`.
+  auto scale_word = [&](uint32_t sb, int mode) {
+    const bool large = (sb & 0x7FFFu) > kSafe;
+    const bool keep = mode == 0 || (mode == 1) != large;
+    const uint32_t f = sb - (mode == 2 ? 0x4000u : 0u);   // 2^-16: exponent - 16
+    return keep ? f | (f << 16) : 0u;
   };
 
-  // Prologue: the load groups of the virtual sub-steps -D .. -1, built like
-  // the steady state's (x(t+D), s(t+D), super-tile t/SUB + WS - 1 where t is
-  // a multiple of SUB), the first one also carrying the super-tiles that the
-  // steady state would have loaded before it. Then wait for that first group
-  // and read sub-step 0's k-step-0 fragments and packed words.
-  constexpr int catch_up = WS - (D + SUB - 1) / SUB;   // super-tiles 0 .. catch_up-1
-  unroll<0, D>([&](auto I_) {
-    constexpr int t = decltype(I_)::value - D;
-    issue_x(t + D, (t + D) % NXS);
-    if constexpr (t == -D) {
-      issue_s(0, 0);
-#pragma unroll
-      for (int st = 0; st < catch_up; ++st) issue_w(st, st % WS);
-    } else {
-      if constexpr (s_used(t + D)) issue_s(t + D, (t + D) % NXS);
-      if constexpr (t % SUB == 0) issue_w(t / SUB + WS - 1, (t / SUB + WS - 1) % WS);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  });
-  constexpr auto prologue_newer = [group_loads]() {
-    int n = 0;
-    for (int i = 1; i <= D - 1; ++i) n += group_loads(-i);
-    return n;
-  };
-  wait_vmcnt<prologue_newer()>();
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  read_a(0, 0, af);
-  read_w(0, 0, wp);
-  // Sub-step 0 opens the first group: the running scale starts at s(0) (a
-  // zero scale leaves it 0, and the accumulator is still 0).
-#pragma unroll
-  for (int b = 0; b < TN; ++b) {
-    srun[b] = half_bits_to_float((uint16_t)sr[0][b]);
-    if constexpr (AFF) zb[b] = zp_bias_natural(zr[0][b]);
-  }
-
-  // Sub-step t = t0 + J, t0 a multiple of U: x stage J % NXS, W slot
-  // (J / SUB) % WS, scale slot J % NXS, all compile-time.
-  // (always inlined: an outlined sub-step would take the DMA destinations and
-  // the register arrays by reference, i.e. through scratch memory)
-  auto substep = [&](auto J_, int t) __attribute__((always_inline)) {
-    constexpr int J = decltype(J_)::value;
-    constexpr int ws = (J / SUB) % WS, xs = J % NXS;
-    constexpr int J1 = (J + 1) % U;
-    constexpr int xs1 = J1 % NXS, ws1 = (J1 / SUB) % WS, u1 = J1 % SUB;
-    wait_vmcnt<newer_loads(J)>();
-    lds_barrier();                             // data of t+1 visible; stages of t-1 free
-    // Keep every use of the awaited data below the wait: a use hoisted above
-    // it makes the compiler add a wait of its own, and with LDS DMA in flight
-    // that wait is for every load.
-    __builtin_amdgcn_sched_barrier(0);
-    issue_x(t + D, (J + D) % NXS);             // into the stage of t-1
-    if constexpr (s_used(J + D)) issue_s(t + D, (J + D) % NXS);
-    if constexpr (J % SUB == 0) issue_w(t / SUB + WS - 1, (ws + WS - 1) % WS);
-    half8_t bcur[TN];
-    expand_b(wp, 0, bcur);
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t wnext[TN][KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      half8_t cur[TM];
-#pragma unroll
-      for (int a = 0; a < TM; ++a) cur[a] = af[a];
-      if (s + 1 < KS) {
-        read_a(xs, s + 1, af);
-      } else {                                 // sub-step t+1: k-step 0 and its packed words
-        read_a(xs1, 0, af);
-        read_w(ws1, u1, wnext);
-      }
-      half8_t bnext[TN];
-      if (s + 1 < KS) expand_b(wp, s + 1, bnext);
+  // The usual pass (mode 0), operands staged through the LDS rings.
+  auto run = [&]() __attribute__((always_inline)) {
+    uint32_t s2[TN];                           // the group's scale factor twice, binary16
+    uint32_t zb[TN];                           // bias word of the current group (AFF)
+    half8_t af[TM];                            // A fragments of the next k-step
+    uint32_t wp[TN][KS];                       // packed words of the current sub-step
+    auto read_a = [&](int stage, int s, half8_t* dst) {
 #pragma unroll
       for (int a = 0; a < TM; ++a)
+        dst[a] = *reinterpret_cast<const half8_t*>(lds + stage * A_BYTES + aoff[s] + a * 32 * BK * 2);
+    };
+    auto read_w = [&](int slot, int u, uint32_t (*dst)[KS]) {
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[a], bcur[b], acc[a][b], 0, 0, 0);
-      if (s + 1 < KS) {
-        // one MFMA, three VALU (next k-step's codes), one LDS read
-#pragma unroll
-        for (int i = 0; i < TM * TN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-          if (i < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      } else {
-        // If t+1 opens a group, rescale now: the accumulators are not used
-        // again before sub-step t+1. Never past the last sub-step.
-        bool gnext;
-        if constexpr (SPG == 0) gnext = ((t + 1) & ((1 << gshift) - 1)) == 0;
-        else gnext = (J + 1) % SPG == 0;
-        gnext = gnext && t + 1 < T;
-        float ratio[TN];
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const float sn = half_bits_to_float((uint16_t)sr[xs1][b]);
-          const bool live = gnext && sn != 0.0f;   // zero scale: keep the running one
-          // srun / sn to within an ulp (a uniform relative error of the finished
-          // groups' part, far inside the tolerance); srun = 0 gives 0.
-          ratio[b] = live ? srun[b] * __builtin_amdgcn_rcpf(sn) : 1.0f;
-          srun[b] = live ? sn : srun[b];
-          // The zero-point slot of t+1 holds t+1's group wherever a group can
-          // open there (every sub-step when SPG is decided at run time), so
-          // the bias is switched without a condition.
-          if constexpr (AFF && (SPG == 0 || (J + 1) % SPG == 0)) zb[b] = zp_bias_natural(zr[xs1][b]);
-        }
-        if constexpr (SPG == 0 || (J + 1) % SPG == 0) {
-#pragma unroll
-          for (int a = 0; a < TM; ++a)
-#pragma unroll
-            for (int b = 0; b < TN; ++b) acc[a][b] *= ratio[b];
-        }
-#pragma unroll
-        for (int i = 0; i < TM * TN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      for (int b = 0; b < TN; ++b) {
+        const uint8_t* p = lds + W_LDS + slot * W_BYTES + woff(u, b);
+        if constexpr (BK == 64) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+          dst[b][0] = v.x; dst[b][1] = v.y; dst[b][2] = v.z; dst[b][3] = v.w;
+        } else {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+          dst[b][0] = v.x; dst[b][1] = v.y;
         }
       }
+    };
+    auto expand_b = [&](const uint32_t (*w)[KS], int s, half8_t* bf) {
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        half2_t hw[4];
+        if constexpr (AFF) codes_to_half_natural_zp(w[b][s], hw, zb[b]);
+        else codes_to_half_natural(w[b][s], hw);
+        const half2_t sc = __builtin_bit_cast(half2_t, s2[b]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hw[i] *= sc;
+        bf[b] = as_half8(hw);
+      }
+    };
+    // State of the group that opens at the sub-step whose scale (and zero
+    // point) slot is `slot`.
+    auto open_group = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const uint32_t sb = sr[slot][b] & 0xFFFFu;
+        big |= (sb & 0x7FFFu) > kSafe ? 1u : 0u;
+        s2[b] = scale_word(sb, 0);
+        if constexpr (AFF) zb[b] = zp_bias_natural(zr[slot][b]);
+      }
+    };
+
+    // Prologue: the load groups of the virtual sub-steps -D .. -1, built like
+    // the steady state's (x(t+D), s(t+D), super-tile t/SUB + WS - 1 where t is
+    // a multiple of SUB), the first one also carrying the super-tiles that the
+    // steady state would have loaded before it. Then wait for that first group
+    // and read sub-step 0's k-step-0 fragments and packed words.
+    constexpr int catch_up = WS - (D + SUB - 1) / SUB;   // super-tiles 0 .. catch_up-1
+    unroll<0, D>([&](auto I_) {
+      constexpr int t = decltype(I_)::value - D;
+      issue_x(t + D, (t + D) % NXS);
+      if constexpr (t == -D) {
+        issue_s(0, 0);
+#pragma unroll
+        for (int st = 0; st < catch_up; ++st) issue_w(st, st % WS);
+      } else {
+        if constexpr (s_used(t + D)) issue_s(t + D, (t + D) % NXS);
+        if constexpr (t % SUB == 0) issue_w(t / SUB + WS - 1, (t / SUB + WS - 1) % WS);
+      }
       __builtin_amdgcn_sched_barrier(0);
+    });
+    constexpr auto prologue_newer = [group_loads]() {
+      int n = 0;
+      for (int i = 1; i <= D - 1; ++i) n += group_loads(-i);
+      return n;
+    };
+    wait_vmcnt<prologue_newer()>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(0, 0, af);
+    read_w(0, 0, wp);
+    open_group(0);                             // sub-step 0 opens the first group
+
+    // Sub-step t = t0 + J, t0 a multiple of U: x stage J % NXS, W slot
+    // (J / SUB) % WS, scale slot J % NXS, all compile-time.
+    // (always inlined: an outlined sub-step would take the DMA destinations and
+    // the register arrays by reference, i.e. through scratch memory)
+    auto substep = [&](auto J_, int t) __attribute__((always_inline)) {
+      constexpr int J = decltype(J_)::value;
+      constexpr int ws = (J / SUB) % WS, xs = J % NXS;
+      constexpr int J1 = (J + 1) % U;
+      constexpr int xs1 = J1 % NXS, ws1 = (J1 / SUB) % WS, u1 = J1 % SUB;
+      __builtin_amdgcn_sched_barrier(0);
+      issue_x(t + D, (J + D) % NXS);           // into the stage of t-1
+      if constexpr (s_used(J + D)) issue_s(t + D, (J + D) % NXS);
+      if constexpr (J % SUB == 0) issue_w(t / SUB + WS - 1, (ws + WS - 1) % WS);
+      half8_t bcur[TN];
+      expand_b(wp, 0, bcur);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t wnext[TN][KS];
 #pragma unroll
-      for (int b = 0; b < TN; ++b) bcur[b] = bnext[b];
-    }
+      for (int s = 0; s < KS; ++s) {
+        half8_t cur[TM];
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
+        for (int a = 0; a < TM; ++a) cur[a] = af[a];
+        if (s + 1 < KS) {
+          read_a(xs, s + 1, af);
+        } else {                               // sub-step t+1: k-step 0 and its packed words
+          wait_vmcnt<newer_loads(J)>();
+          lds_barrier();                       // data of t+1 visible; stage of t free
+          __builtin_amdgcn_sched_barrier(0);
+          read_a(xs1, 0, af);
+          read_w(ws1, u1, wnext);
+        }
+        half8_t bnext[TN];
+        if (s + 1 < KS) expand_b(wp, s + 1, bnext);
 #pragma unroll
-      for (int i = 0; i < KS; ++i) wp[b][i] = wnext[b][i];
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[a], bcur[b], acc[a][b], 0, 0, 0);
+        if (s + 1 < KS) {
+          // one MFMA, four VALU (the next k-step's codes and scale), one LDS read
+#pragma unroll
+          for (int i = 0; i < TM * TN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            if (i < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        } else {
+          // The scale (and zero-point) slot of t+1 holds t+1's group wherever
+          // a group can open there (every sub-step when the group size is
+          // decided at run time), so the group state is switched there without
+          // a condition.
+          if constexpr (SPG == 0 || (J + 1) % SPG == 0) open_group(xs1);
+#pragma unroll
+          for (int i = 0; i < TM * TN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < TN; ++b) bcur[b] = bnext[b];
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int i = 0; i < KS; ++i) wp[b][i] = wnext[b][i];
+    };
+
+    // Main loop over whole bodies, then the last partial body with each
+    // sub-step guarded (sub-steps skipped there are all at the end, so the
+    // load counts of the ones that run are unchanged).
+    int t0 = 0;
+    for (; t0 + U <= T; t0 += U)
+      unroll<0, U>([&](auto J) { substep(J, t0 + decltype(J)::value); });
+    unroll<0, U>([&](auto J) {
+      if (t0 + decltype(J)::value < T) substep(J, t0 + decltype(J)::value);
+    });
+    wait_vmcnt<0>();                           // no LDS DMA in flight at exit
   };
 
-  // Main loop over whole bodies, then the last partial body with each
-  // sub-step guarded (sub-steps skipped there are all at the end, so the
-  // load counts of the ones that run are unchanged).
-  int t0 = 0;
-  for (; t0 + U <= T; t0 += U)
-    unroll<0, U>([&](auto J) { substep(J, t0 + decltype(J)::value); });
-  unroll<0, U>([&](auto J) {
-    if (t0 + decltype(J)::value < T) substep(J, t0 + decltype(J)::value);
-  });
-  wait_vmcnt<0>();                             // no LDS DMA in flight at exit
+  // The rare passes (modes 2 and 1): each wavefront reads its A fragments and
+  // packed words straight from global memory, with the same k order and
+  // fragment layout as the usual pass. Slow, and kept apart from the LDS
+  // rings so that it adds no LDS traffic the usual pass has to be ordered
+  // against.
+  auto run_direct = [&](int mode) {
+    const int kb = RB;                         // bytes per packed row
+    int rows[TM], cols[TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int m = m0 + wm * WMT + a * 32 + c32;
+      rows[a] = m < M ? m : M - 1;
+    }
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      const int n = n0 + wn * WNT + b * 32 + c32;
+      cols[b] = n < N ? n : N - 1;
+    }
+    for (int t = 0; t < T; ++t) {
+      const int gi = t >> spg_log;
+      uint32_t s2[TN], zb[TN];
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        s2[b] = scale_word(scales[(int64_t)cols[b] * G + gi], mode);
+        zb[b] = 0u;
+        if constexpr (AFF) zb[b] = zp_bias_natural(zeros[(int64_t)cols[b] * G + gi]);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int k = t * BK + (BK / 2) * h + 8 * s;   // first of the lane's 8 codes
+        half8_t af[TM], bf[TN];
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+          af[a] = *reinterpret_cast<const half8_t*>(x + (int64_t)rows[a] * K + k);
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const uint32_t d = *reinterpret_cast<const uint32_t*>(packed + (int64_t)cols[b] * kb + (k >> 1));
+          half2_t hw[4];
+          if constexpr (AFF) codes_to_half_natural_zp(d, hw, zb[b]);
+          else codes_to_half_natural(d, hw);
+          const half2_t sc = __builtin_bit_cast(half2_t, s2[b]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hw[i] *= sc;
+          bf[b] = as_half8(hw);
+        }
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+      }
+    }
+  };
 
-  // Epilogue: apply the last running scale; lane l holds column l%32 and rows
-  // 8*(i/4) + 4*(l/32) + (i%4) of each 32x32 tile (register i).
-  // A block tile inside y (every block but the last row and column of
-  // tiles) stores without per-output bounds checks; the output precision is
-  // one branch for the whole tile.
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  };
+  zero_acc();
+  run();
+  // Block-wide OR of the waves' flags, through the ring array itself (every
+  // DMA and LDS read of the pass has completed). (__syncthreads_or would add a
+  // second LDS object, after which the compiler can no longer tell the DMA
+  // targets from the operand reads and waits for every load in flight.)
+  {
+    const bool wave_big = __builtin_amdgcn_ballot_w64(big != 0u) != 0;
+    lds_barrier();
+    if (lane == 0) reinterpret_cast<volatile uint32_t*>(lds)[wave] = wave_big ? 1u : 0u;
+    lds_barrier();
+  }
+  const uint32_t* flags = reinterpret_cast<const uint32_t*>(lds);
+  if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0u) {
+    // a large scale somewhere in the block's columns: mode 2, times 2^16,
+    // then mode 1 on top
+    zero_acc();
+    run_direct(2);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) acc[a][b] *= 65536.0f;
+    run_direct(1);
+  }
+
+  // Store: lane l holds column l%32 and rows 8*(i/4) + 4*(l/32) + (i%4) of each
+  // 32x32 tile (register i). A block tile inside y (every block but the last
+  // row and column of tiles) stores without per-output bounds checks; the
+  // output precision is one branch for the whole tile.
   const bool full = m0 + BM <= M && n0 + BN <= N;
   auto store_all = [&](auto* yt) __attribute__((always_inline)) {
     typedef std::remove_pointer_t<decltype(yt)> T;
@@ -448,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i] * srun[b], bn);
+            yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i], bn);
           }
       } else {
 #pragma unroll
@@ -456,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (m < M && n < N) yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i] * srun[b], bn);
+            if (m < M && n < N) yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i], bn);
           }
       }
     }
