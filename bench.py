@@ -24,13 +24,18 @@ the step, with the unfused baseline the engine page measures it against:
 int4_dequantize to a float16 w_hat, then a library fp16 GEMM (torch's
 F.linear, hipBLASLt) on it ("unfused_baseline"; --no-unfused skips it).
 
-Also after the timed steps, "gated_cases" times each case the path is
-measured against on its own: M = 1 on the three shapes and on the
-[28672, 8192] FFN matrix (gate: 70% of HBM peak on packed weights + scales),
-M = 2048 on the three shapes (gate: 50% of the dense fp16 MFMA peak), and
-M = 4096 on the FFN matrix (reported). --no-gates skips it.
+Also after the timed steps, "cases" times every (configuration, matrix, M)
+of the workloads on its own (the small-transformer linears at M = 1, 4, 16
+with groups 64 and 32; the 7B-class linears at M = 1, 16, 512, 2048; the
+[28672, 8192] FFN matrix at M = 1, 8, 256, 4096, and its full-W quantize):
+median of five graph replays, each against its roofline min(HBM, MFMA) from
+its algorithmic bytes and flops, M = 1 also against a measured streaming-read
+ceiling of the same weight pool; the gated cases (M = 1 at >= 70% of HBM
+peak on packed weights + scales for the 7B-class and FFN matrices, M = 2048
+at >= 50% of the fp16 MFMA peak) report pass or fail. --no-report skips it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-probe]
+       [--no-unfused] [--no-report]
 
 --copy-probe adds, after the timed region, three plain device-to-device
 copies of 512 MiB: under rocprofv3 --pmc they give the FETCH_SIZE and
@@ -125,7 +130,7 @@ def measured_traffic():
 def unfused_comparison(mats, pool, reps=20):
     """Fused int4_matmul against dequantize-to-fp16 + library GEMM, per shape,
     at M = 1 (weights from the HBM rotation pool) and M = 2048. Each variant is
-    captured in a HIP graph of `reps` calls and replayed; the best of three
+    captured in a HIP graph of `reps` calls and replayed; the median of five
     replays counts. Returns microseconds per call and the HBM bytes each
     variant moves for the weights."""
     import torch
@@ -146,15 +151,15 @@ def unfused_comparison(mats, pool, reps=20):
                 fn()
         g.replay()
         torch.cuda.synchronize()
-        best = float("inf")
-        for _ in range(3):
+        ts = []
+        for _ in range(5):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             g.replay()
             b.record()
             torch.cuda.synchronize()
-            best = min(best, a.elapsed_time(b) * 1e3 / reps)
-        return best
+            ts.append(a.elapsed_time(b) * 1e3 / reps)
+        return sorted(ts)[2]
 
     out = {}
     for M_, key in ((M_DECODE, "m1"), (M_PREFILL, "m2048")):
@@ -220,8 +225,9 @@ def unfused_comparison(mats, pool, reps=20):
     return out
 
 
-def _graph_time_us(fn, reps):
-    """Best of three replays of a HIP graph of `reps` calls, microseconds per call."""
+def _graph_times_us(fn, reps, trials=5):
+    """Per-call times (microseconds) of `trials` replays of a HIP graph of
+    `reps` calls of fn, after one warm replay."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -231,31 +237,102 @@ def _graph_time_us(fn, reps):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    best = float("inf")
-    for _ in range(3):
+    out = []
+    for _ in range(trials):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         g.replay()
         b.record()
         torch.cuda.synchronize()
-        best = min(best, a.elapsed_time(b) * 1e3 / reps)
-    return best
+        out.append(a.elapsed_time(b) * 1e3 / reps)
+    return out
+
+
+def _graph_time_us(fn, reps):
+    """Median of five graph replays, microseconds per call."""
+    import statistics
+    return statistics.median(_graph_times_us(fn, reps))
 
 
 # The measurement gates of the hot path: M = 1 at >= 70% of HBM peak on the
-# packed weights + scales, M = 2048 at >= 50% of the dense fp16 MFMA peak
-# (256 CUs x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s).
-GATE_HBM_FRAC, GATE_MFMA_FRAC, MFMA_PEAK_GATE_TFLOPS = 0.70, 0.50, 2516.6
+# packed weights + scales, M = 2048 at >= 50% of the dense fp16 MFMA peak.
+GATE_HBM_FRAC, GATE_MFMA_FRAC = 0.70, 0.50
+
+# Every (configuration, matrix, M) of the workloads, as the report lists them.
+C3_SHAPES = [("c_attn", 2304, 768), ("attn_c_proj", 768, 768), ("c_fc", 3072, 768),
+             ("mlp_c_proj", 768, 3072)]
 
 
-def gated_cases(mats, pool, dev):
-    """Each gated case of the path timed on its own (graph replays, best of
-    three): the three 7B-class shapes at M = 1 (weights rotating through the
-    >= 1 GiB pool) and M = 2048, and the [28672, 8192] FFN matrix at M = 1
-    (its own >= 1 GiB pool of quantized N(0, 0.02) weights) and M = 4096
-    (reported, not gated)."""
+def report_cases():
+    cases = []
+    for g in (64, 32):
+        for name, N, K in C3_SHAPES:
+            for M in (1, 4, 16):
+                cases.append(("c3", f"{name}_g{g}", N, K, g, M))
+    for name, N, K in SHAPES:
+        for M in (1, 16, 512, 2048):
+            cases.append(("c4", name, N, K, GROUP, M))
+    for M in (1, 8, 256, 4096):
+        cases.append(("c5", "ffn", 28672, 8192, GROUP, M))
+    return cases
+
+
+def algorithmic(N, K, g, M):
+    """(bytes, flops) one int4_matmul call must move and compute: packed
+    weights, scales, x (fp16) and y (fp32); 2 M N K."""
+    return packed_weight_bytes(N, K, g) + 2 * M * K + 4 * M * N, 2 * M * N * K
+
+
+_probe = None
+
+
+def _probe_lib():
+    """The streaming-read probe (dequantizing_gemm_amd/probe), loaded by path."""
+    global _probe
+    if _probe is None:
+        import ctypes
+        path = os.path.join(ROOT, "dequantizing_gemm_amd", "probe", "libint4dq_probe.so")
+        lib = ctypes.CDLL(path)
+        lib.int4dq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                 ctypes.c_int, ctypes.c_void_p]
+        lib.int4dq_probe_stream_read.restype = ctypes.c_int
+        _probe = lib
+    return _probe
+
+
+def stream_read_ceiling(copies):
+    """Measured streaming-read rate (GB/s) over a rotation pool, timed like the
+    matmul (graph replays, median of five): a plain read of each copy's packed
+    bytes (the probe kernel: 1 KB per wavefront load, four loads in flight per
+    lane, 8 blocks of 4 wavefronts per CU), the bytes int4_matmul streams at
+    M = 1 less the 1.5% of scales."""
+    import torch
+    lib = _probe_lib()
+    sink = torch.zeros(1, dtype=torch.int32, device=copies[0][0].device)
+    it = {"k": 0}
+
+    def call():
+        p = copies[it["k"] % len(copies)][0]
+        it["k"] += 1
+        assert lib.int4dq_probe_stream_read(p.data_ptr(), p.numel(), sink.data_ptr(), 2048,
+                                            torch.cuda.current_stream().cuda_stream) == 0
+    us = _graph_time_us(call, len(copies))
+    return copies[0][0].numel() / us / 1e3
+
+
+def case_report(dev):
+    """Every case of the report timed on its own: HIP graphs of the call,
+    median of five replays (min and max beside it); for M <= 16 the weights
+    rotate through a >= 1 GiB pool of copies so every launch streams them from
+    HBM. Each case gets its roofline min(HBM, MFMA) from its algorithmic bytes
+    and flops; M = 1 cases also get the streaming-read ceiling of the same pool
+    and their fraction of it; the gated cases (M = 1 on the 7B-class and FFN
+    matrices, M = 2048 on the 7B-class matrices) report pass or fail."""
+    import statistics
+    import numpy as np
     import torch
     import dequantizing_gemm_amd as dq
+    import workloads
 
     L = dq.lib
     out = []
@@ -263,55 +340,75 @@ def gated_cases(mats, pool, dev):
     def cur():
         return torch.cuda.current_stream().cuda_stream
 
-    def decode_case(name, N, K, copies, x, y):
-        it = {"k": 0}
+    by_matrix = {}
+    for c in report_cases():
+        by_matrix.setdefault(c[:5], []).append(c[5])
+    for (cfg, name, N, K, g), Ms in by_matrix.items():
+        print(f"bench: report {cfg} {name} [{N},{K}] g={g}", file=sys.stderr, flush=True)
+        if cfg == "c5":
+            gen = torch.Generator(device=dev).manual_seed(0)
+            w = torch.randn((N, K), generator=gen, device=dev) * 0.02
+        else:
+            case = workloads.Case(name, N, K, g, 0.02, cfg == "c4")
+            w = torch.from_numpy(workloads.weights(case)).to(dev)
+        p0, s0, _ = dq.quantize_int4(w, g)
+        if cfg == "c5":
+            # full-W quantize: fp32 read, packed codes and scales written
+            qb = N * K * 4 + packed_weight_bytes(N, K, g)
+            pq, sq = torch.empty_like(p0), torch.empty_like(s0)
 
-        def call():
-            p, s_ = copies[it["k"] % len(copies)]
-            it["k"] += 1
-            assert L.int4_matmul(x.data_ptr(), 1, 1, p.data_ptr(), s_.data_ptr(), N, K, GROUP,
-                                 y.data_ptr(), cur()) == 0
-        us = _graph_time_us(call, len(copies))
-        gbs = packed_weight_bytes(N, K) / us / 1e3
-        gate = GATE_HBM_FRAC * HBM_PEAK_GBS
-        out.append({"case": f"{name} [{N},{K}] M=1", "time_us": round(us, 3), "achieved": round(gbs, 1),
-                    "unit": "GB/s", "gate": gate, "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                    "pass": gbs >= gate})
+            def qcall():
+                assert L.int4_quantize(w.data_ptr(), N, K, g, pq.data_ptr(), sq.data_ptr(), cur()) == 0
+            ts = _graph_times_us(qcall, 5)
+            us = statistics.median(ts)
+            out.append({"case": f"c5 int4_quantize [{N},{K}] g={g} (full W)", "time_us": round(us, 3),
+                        "min_us": round(min(ts), 3), "max_us": round(max(ts), 3),
+                        "achieved": round(qb / us / 1e3, 1), "unit": "GB/s", "bound": "hbm",
+                        "frac_of_peak": round(qb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": qb})
+            del pq, sq
+        del w
+        wb = packed_weight_bytes(N, K, g)
+        copies = [(p0, s0)]
+        if min(Ms) <= 16:
+            copies += [(p0.clone(), s0.clone()) for _ in range(max(1, -(-POOL_BYTES // wb) - 1))]
+        ceiling = stream_read_ceiling(copies) if 1 in Ms else None
+        for M in Ms:
+            x = torch.from_numpy(workloads.activations(M, K)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            pool = copies if M <= 16 else copies[:1]
+            it = {"k": 0}
 
-    def prefill_case(name, N, K, M_, p, s_, x, y, gated=True):
-        def call():
-            assert L.int4_matmul(x.data_ptr(), 1, M_, p.data_ptr(), s_.data_ptr(), N, K, GROUP,
-                                 y.data_ptr(), cur()) == 0
-        us = _graph_time_us(call, 10)
-        tf = 2 * M_ * N * K / us / 1e6
-        gate = GATE_MFMA_FRAC * MFMA_PEAK_GATE_TFLOPS
-        rec = {"case": f"{name} [{N},{K}] M={M_}", "time_us": round(us, 3), "achieved": round(tf, 1),
-               "unit": "TFLOP/s", "frac_of_peak": round(tf / MFMA_PEAK_GATE_TFLOPS, 4)}
-        if gated:
-            rec.update(gate=gate, **{"pass": tf >= gate})
-        out.append(rec)
-
-    for i, m in enumerate(mats):
-        decode_case(m["name"], m["N"], m["K"], [pool[r][i] for r in range(len(pool))], m["x1"], m["y1"])
-    for m in mats:
-        prefill_case(m["name"], m["N"], m["K"], M_PREFILL, m["packed"], m["scales"], m["xp"], m["yp"])
-
-    N, K = 28672, 8192
-    gen = torch.Generator(device=dev).manual_seed(0)
-    w = torch.randn((N, K), generator=gen, device=dev) * 0.02
-    p0, s0, _ = dq.quantize_int4(w, GROUP)
-    del w
-    copies = [(p0, s0)] + [(p0.clone(), s0.clone())
-                           for _ in range(max(1, -(-POOL_BYTES // packed_weight_bytes(N, K)) - 1))]
-    x1 = torch.randn((1, K), generator=gen, device=dev).half()
-    y1 = torch.empty((1, N), device=dev)
-    decode_case("ffn", N, K, copies, x1, y1)
-    del copies
-    x4 = torch.randn((4096, K), generator=gen, device=dev).half()
-    y4 = torch.empty((4096, N), device=dev)
-    prefill_case("ffn", N, K, 4096, p0, s0, x4, y4, gated=False)
-    del x4, y4, p0, s0
-    torch.cuda.empty_cache()
+            def call():
+                p, s_ = pool[it["k"] % len(pool)]
+                it["k"] += 1
+                assert L.int4_matmul(x.data_ptr(), 1, M, p.data_ptr(), s_.data_ptr(), N, K, g,
+                                     y.data_ptr(), cur()) == 0
+            ts = _graph_times_us(call, len(pool) if M <= 16 else 10)
+            us = statistics.median(ts)
+            nbytes, flops = algorithmic(N, K, g, M)
+            t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e3), flops / (FP16_MFMA_PEAK_TFLOPS * 1e6)
+            bound = "hbm" if t_hbm >= t_mfma else "mfma"
+            rec = {"case": f"{cfg} {name} [{N},{K}] g={g} M={M}",
+                   "kernel": dq.matmul_select(x, p0, s0, K, g),
+                   "time_us": round(us, 3), "min_us": round(min(ts), 3), "max_us": round(max(ts), 3),
+                   "bound": bound, "roofline_us": round(max(t_hbm, t_mfma), 3),
+                   "frac_of_roofline": round(max(t_hbm, t_mfma) / us, 4),
+                   "gbs": round(nbytes / us / 1e3, 1), "tflops": round(flops / us / 1e6, 2)}
+            if M == 1:
+                rec["weight_gbs"] = round(wb / us / 1e3, 1)
+                rec["weight_frac_of_peak"] = round(wb / us / 1e3 / HBM_PEAK_GBS, 4)
+                rec["stream_read_ceiling_gbs"] = round(ceiling, 1)
+                rec["frac_of_measured_ceiling"] = round(wb / us / 1e3 / ceiling, 4)
+                if cfg in ("c4", "c5"):
+                    rec["gate"] = f">= {GATE_HBM_FRAC} of HBM peak on packed weights + scales"
+                    rec["pass"] = rec["weight_frac_of_peak"] >= GATE_HBM_FRAC
+            if M == 2048 and cfg == "c4":
+                rec["gate"] = f">= {GATE_MFMA_FRAC} of the fp16 MFMA peak"
+                rec["pass"] = flops / us / 1e6 / FP16_MFMA_PEAK_TFLOPS >= GATE_MFMA_FRAC
+            out.append(rec)
+            del x, y
+        del copies, p0, s0
+        torch.cuda.empty_cache()
     return out
 
 
@@ -362,7 +459,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
-    ap.add_argument("--no-gates", action="store_true")
+    ap.add_argument("--no-report", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -528,9 +625,11 @@ def main():
             "tflops": round(lib_tf, 1), "frac_of_peak": round(lib_tf / FP16_MFMA_PEAK_TFLOPS, 4),
             "fused_frac_of_library": round(roofs[3]["achieved"] / lib_tf, 4),
             "note": "F.linear (hipBLASLt) on the same three shapes, fp16 weights and output"}
-    if not args.no_gates:
-        print("bench: gated cases", file=sys.stderr, flush=True)
-        line["gated_cases"] = gated_cases(mats, pool, dev)
+    if not args.no_report:
+        print("bench: per-case report", file=sys.stderr, flush=True)
+        line["cases"] = case_report(dev)
+        gated = [c for c in line["cases"] if "pass" in c]
+        line["gates_passed"] = f"{sum(c['pass'] for c in gated)} of {len(gated)}"
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

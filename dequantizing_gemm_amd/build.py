@@ -39,11 +39,12 @@ HIPFLAGS = [
 SOURCES = ["api.cpp", "quantize.hip", "unpack.hip", "dequantize.hip", "matmul_generic.hip",
            "matmul_skinny.hip", "matmul_tiled.hip", "matmul_gemv.hip"]
 
-# The tiled and gemv kernels read or rescale their MFMA accumulators with VALU
-# ops; selecting the VGPR form of the MFMA instructions keeps the accumulators
-# in VGPRs instead of AGPRs (no accvgpr read/write around them).
-EXTRA = {"matmul_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-         "matmul_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# The gemv kernels read their MFMA accumulators with VALU ops; selecting the
+# VGPR form of the MFMA instructions keeps the accumulators in VGPRs instead of
+# AGPRs (no accvgpr read/write around them). The tiled kernel never touches its
+# accumulators inside the loop and keeps them in AGPRs, which leaves the VGPRs
+# to the operands.
+EXTRA = {"matmul_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 # Every kernel's resource-usage remark is read back: a kernel that uses scratch
@@ -63,10 +64,10 @@ def _scratch_users(stderr: str) -> list[str]:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *HIPFLAGS, *EXTRA.get(src, []), *RESOURCE_REMARKS, *lang, "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *HIPFLAGS, *EXTRA.get(src, []), *RESOURCE_REMARKS, *lang, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -84,20 +85,35 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every HIP source for gfx950 and link the shared library. Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+# The measurement probe (a plain streaming read, the ceiling the benchmark
+# compares bandwidth-bound kernels with) is its own small library: it is not
+# part of the path and the binding never loads it.
+PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libint4dq_probe.so")
+
+
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every HIP source for gfx950 and link the shared library (and the
+    measurement probe). Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES) + 1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        probe = ex.submit(_compile, PROBE_SRC)
+        objs = list(ex.map(_compile, SOURCES))
+        probe_obj = probe.result()
+    _link(objs, LIB)
+    _link([probe_obj], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
