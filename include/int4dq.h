@@ -132,17 +132,22 @@ int int4_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, in
 
 /*
  * int4_matmul (drill page, statement):
- *   y = x @ dequantize(W).T, computed one group at a time: x times the group's
- *   integer weights first, then that group's scale on each output column.
+ *   y = x @ dequantize(W).T, the statement's sum over groups of the group's
+ *   scale times x dotted with the group's integer weights, without writing
+ *   full-precision weights to memory.
  *   x       in : [M, K], element type x_dtype (INT4DQ_X_F32 or INT4DQ_X_F16).
  *   packed  in : [N, ceil(K/2)] bytes, scales in: [N, G] binary16, as written
  *                by int4_quantize with the same K and group.
  *   y       out: [M, N] binary32.
- *   Arithmetic: products and sums in binary32 (MFMA fp16 x fp16 -> fp32 for
- *   fp16 x; the integer codes are exact in fp16). Each output is within
+ *   Arithmetic: sums in binary32. The kernels for a few rows of x form each
+ *   group's integer dot product (fp16 x times the exact integer codes) and
+ *   multiply it by the group's scale; the kernel for many rows multiplies each
+ *   code by its scale in binary16 first (q * scale rounded once, at most 2^-11
+ *   relative) and accumulates x times that. Either way each output is within
  *   2e-3 * sum_k |x[m,k] * q[n,k] * scale| of the exactly rounded result.
- *   M = 0 is a valid no-op. The pad nibble of an odd K is never used and
- *   x[:, K] is never read.
+ *   A group whose scale is zero (+0 or -0) contributes nothing, whatever its
+ *   codes. M = 0 is a valid no-op. The pad nibble of an odd K is never used
+ *   and x[:, K] is never read.
  *   Errors: EINVAL if M < 0, N, K or group < 1, a pointer is NULL (when M > 0),
  *   x_dtype is unknown, or sizes overflow.
  */
