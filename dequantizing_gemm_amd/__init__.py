@@ -34,7 +34,8 @@ import os
 import torch
 
 __all__ = ["quantize_int4", "quantize_int4_affine", "unpack_int4", "dequantize_int4", "int4_matmul",
-           "int4_matmul_path", "int4_linear", "matmul_select",
+           "int4_matmul_path", "int4_linear", "linear_workspace_bytes", "linear_workspace",
+           "matmul_select",
            "num_groups", "packed_bytes", "lib", "LIB_PATH", "Int4Error", "PATHS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4dq.so")
@@ -64,6 +65,9 @@ SIGNATURES = {
     "int4_matmul_affine": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp,
                                   _int, _vp]),
     "int4_linear": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _int, _vp]),
+    "int4_linear_ws": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _int,
+                              _vp, _i64, _vp]),
+    "int4_linear_workspace_bytes": (_i64, [_int, _i64, _i64, _i64, _i64]),
     "int4_last_error": (ctypes.c_char_p, []),
 }
 
@@ -266,14 +270,33 @@ def int4_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: 
     return int4_matmul_path(x, packed, scales, K, group, "auto", out, bias, relu, zeros)
 
 
+def linear_workspace_bytes(M: int, N: int, K: int, group: int = 128, x_dtype=torch.float16) -> int:
+    """Bytes of workspace int4_linear(..., workspace=) uses for these sizes (0:
+    the call does not split K)."""
+    xd = X_F16 if x_dtype == torch.float16 else X_F32
+    r = lib.int4_linear_workspace_bytes(xd, M, N, K, group)
+    if r < 0:
+        raise ValueError(f"invalid sizes M={M} N={N} K={K} group={group}")
+    return int(r)
+
+
+def linear_workspace(M: int, N: int, K: int, group: int = 128, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace tensor for int4_linear(..., workspace=), or an
+    empty one when the shape does not use it."""
+    return torch.zeros(max(linear_workspace_bytes(M, N, K, group), 0), dtype=torch.uint8, device=device)
+
+
 def int4_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: int,
                 group: int = 128, *, zeros: torch.Tensor | None = None,
                 bias: torch.Tensor | None = None, relu: bool = False,
                 out_dtype: torch.dtype = torch.float32,
-                out: torch.Tensor | None = None) -> torch.Tensor:
+                out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
     """One layer: y [M, N] = act(x @ dequantize(W).T + bias) written as
     ``out_dtype`` (float32, or float16 rounded to nearest even), symmetric or
-    (with ``zeros``) affine codes; the kernel is chosen as int4_matmul does."""
+    (with ``zeros``) affine codes; the kernel is chosen as int4_matmul does.
+    ``workspace`` (a uint8 device tensor from linear_workspace) lets the
+    many-row kernel split K across blocks when its grid is small."""
     M, N, xd = _matmul_args(x, packed, scales, K, group)
     if out_dtype not in (torch.float32, torch.float16):
         raise ValueError(f"out_dtype must be float32 or float16 (got {out_dtype})")
@@ -290,10 +313,20 @@ def int4_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, K: 
             raise ValueError(f"bias must be [N] = [{N}] on {x.device}")
         bptr = bias.data_ptr()
     zp = _zeros_ptr(zeros, N, K, group, x.device)
+    act = ACT_RELU if relu else ACT_NONE
+    yd = Y_F16 if out_dtype == torch.float16 else Y_F32
     with torch.cuda.device(x.device):
-        rc = lib.int4_linear(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), zp, N, K,
-                             group, bptr, ACT_RELU if relu else ACT_NONE, out.data_ptr(),
-                             Y_F16 if out_dtype == torch.float16 else Y_F32, _stream(x))
+        if workspace is None:
+            rc = lib.int4_linear(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), zp, N, K,
+                                 group, bptr, act, out.data_ptr(), yd, _stream(x))
+        else:
+            _gpu(workspace, "workspace", torch.uint8, ndim=1)
+            if workspace.device != x.device:
+                raise ValueError(f"workspace must be on {x.device}")
+            wptr = workspace.data_ptr() if workspace.numel() else None
+            rc = lib.int4_linear_ws(x.data_ptr(), xd, M, packed.data_ptr(), scales.data_ptr(), zp, N, K,
+                                    group, bptr, act, out.data_ptr(), yd, wptr, workspace.numel(),
+                                    _stream(x))
     _raise(rc, "int4_linear")
     return out
 

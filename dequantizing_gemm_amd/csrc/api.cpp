@@ -63,7 +63,8 @@ int check_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
 // codes; y of y_dtype).
 int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                const float* bias, int act, void* y, int y_dtype, int path, void* stream);
+                const float* bias, int act, void* y, int y_dtype, int path, void* stream,
+                void* workspace = nullptr, int64_t workspace_bytes = 0);
 
 int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, int64_t N,
                 int64_t K, int64_t group) {
@@ -174,6 +175,27 @@ int int4_linear(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                      y_dtype, INT4DQ_PATH_AUTO, stream);
 }
 
+int64_t int4_linear_workspace_bytes(int x_dtype, int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (M < 0 || N < 1 || K < 1 || group < 1 || (x_dtype != INT4DQ_X_F32 && x_dtype != INT4DQ_X_F16)) return -1;
+  if (M == 0) return 0;
+  // The kernel choice of an aligned call (the split applies to the tiled kernel only).
+  static const uint8_t aligned_probe[16] __attribute__((aligned(16))) = {0};
+  if (choose_path(aligned_probe, x_dtype, M, aligned_probe, N, K, group) != INT4DQ_PATH_TILED) return 0;
+  return int4dq::matmul_tiled_workspace(M, N, K, group);
+}
+
+int int4_linear_ws(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                   const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
+                   const float* bias, int act, void* y, int y_dtype, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+    return fail(INT4DQ_EINVAL, "int4_linear_ws: workspace_bytes must be >= 0, with a non-NULL workspace when > 0");
+  if ((uintptr_t)workspace % 256)
+    return fail(INT4DQ_EINVAL, "int4_linear_ws: workspace must be 256-byte aligned");
+  return matmul_impl("int4_linear_ws", x, x_dtype, M, packed, scales, zeros, N, K, group, bias, act, y,
+                     y_dtype, INT4DQ_PATH_AUTO, stream, workspace, workspace_bytes);
+}
+
 int int4_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                 const uint16_t* scales, int64_t N, int64_t K, int64_t group, float* y,
                 void* stream) {
@@ -203,7 +225,8 @@ namespace {
 
 int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uint8_t* packed,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                const float* bias, int act, void* y, int y_dtype, int path, void* stream) {
+                const float* bias, int act, void* y, int y_dtype, int path, void* stream,
+                void* workspace, int64_t workspace_bytes) {
   int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
   if (rc != INT4DQ_OK) return rc;
   if (act != INT4DQ_ACT_NONE && act != INT4DQ_ACT_RELU)
@@ -232,7 +255,8 @@ int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uin
     case INT4DQ_PATH_TILED: {
       const char* why = int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "%s: %s", fn, why);
-      return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, zeros, N, K, group, y, ep, s),
+      return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, zeros, N, K, group, y, ep,
+                                                    workspace, workspace_bytes, s),
                         "int4_matmul tiled launch");
     }
     default:

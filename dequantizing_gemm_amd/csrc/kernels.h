@@ -35,6 +35,14 @@ struct Epilogue {
   }
 };
 
+// Split of K for the tiled kernel: S shares of `steps` sub-steps each, whose
+// partial tiles go to part ([S, M, N] binary32). S = 1: no split, part unused.
+struct TiledSplit {
+  float* part;
+  int S;
+  int steps;
+};
+
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
                            uint16_t* scales, hipStream_t stream);
 
@@ -73,8 +81,14 @@ hipError_t launch_matmul_gemv(const void* x, int64_t M, const uint8_t* packed, c
 
 const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
                                      int64_t K, int64_t group);
+// workspace: nullptr, or workspace_bytes of device memory for a split of K
+// (any contents). The split is taken only when the workspace holds
+// matmul_tiled_workspace(M, N, K, group) bytes; that is 0 when the shape is
+// not split.
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
                                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                               void* y, Epilogue ep, hipStream_t stream);
+                               void* y, Epilogue ep, void* workspace, int64_t workspace_bytes,
+                               hipStream_t stream);
+int64_t matmul_tiled_workspace(int64_t M, int64_t N, int64_t K, int64_t group);
 
 }  // namespace int4dq

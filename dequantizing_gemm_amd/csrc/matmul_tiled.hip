@@ -57,6 +57,7 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace int4dq {
@@ -92,7 +93,7 @@ template <int BK, int SPG, int TM, bool AFF, int WN, int TN, int NXS_ = 4, int W
 __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
-    int gshift, void* __restrict__ y, Epilogue ep) {
+    int gshift, void* __restrict__ y, Epilogue ep, TiledSplit sp) {
   constexpr int WMT = 32 * TM, WNT = 32 * TN;         // wave tile; TM x TN 32x32 MFMA tiles
   constexpr int NW = 4, BM = WMT * (NW / WN), BN = WNT * WN;
   static_assert(WN == 2 || WN == 4, "wave layout");
@@ -149,12 +150,19 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 
   // Tile assignment: consecutive block ids walk down the M tiles first. The
   // hardware deals block ids round-robin to the 8 XCDs, so with a multiple of
-  // 8 M tiles each XCD keeps its x row-tiles in its own L2.
+  // 8 M tiles each XCD keeps its x row-tiles in its own L2. With a split of K
+  // (sp.S > 1) block id / tiles is the block's share of K: sub-steps
+  // [split * sp.steps, +sp.steps), which start on a packed super-tile and on a
+  // group boundary.
   const int mtiles = (M + BM - 1) / BM;
-  const int bm = blockIdx.x % mtiles, bn = blockIdx.x / mtiles;
+  const int tiles = mtiles * ((N + BN - 1) / BN);
+  const int tile = blockIdx.x % tiles, split = blockIdx.x / tiles;
+  const int bm = tile % mtiles, bn = tile / mtiles;
   const int m0 = bm * BM, n0 = bn * BN;
+  const int t_begin = split * sp.steps;        // first sub-step of the block's share of K
+  const int T = min(K / BK - t_begin, sp.steps);   // sub-steps of the share
   const int RB = K >> 1;                       // bytes per packed row
-  const int T = K / BK;                        // sub-steps
+  const int RBl = RB - t_begin * (BK / 2);     // bytes of a row from the share's start
 
   auto swz = [](int r, int c) { return c ^ ((r / RPB) & (PIECES - 1)); };
 
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   // piece lane % PIECES. Byte offsets from the tile's first row fit 32 bits
   // (BM rows, K < 2^23). Rows past M read row M-1 (discarded).
   const int xr0 = wave * XDMA * RPI + lane / PIECES;
-  const char* xtile = reinterpret_cast<const char*>(x + (int64_t)m0 * K);
+  const char* xtile = reinterpret_cast<const char*>(x + (int64_t)m0 * K + (int64_t)t_begin * BK);
   uint32_t xoff[XDMA];
 #pragma unroll
   for (int i = 0; i < XDMA; ++i) {
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   for (int i = 0; i < WDMA; ++i) {
     const int R = 8 * (wave * WDMA + i) + lane / 8;
     const int n = n0 + R < N ? n0 + R : N - 1;
-    wsrc[i] = packed + (int64_t)n * RB;
+    wsrc[i] = packed + (int64_t)n * RB + (int64_t)t_begin * (BK / 2);
     wpiece[i] = 16 * ((lane % 8) ^ ((R >> 1) & 7));
   }
   // --- scales of the lane's two output columns
@@ -192,6 +200,11 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     zsrc[b] = AFF ? zeros + (int64_t)(n < N ? n : N - 1) * G : nullptr;
   }
   const int spg_log = SPG == 0 ? gshift : SPG == 8 ? 3 : SPG == 4 ? 2 : SPG == 2 ? 1 : 0;
+#pragma unroll
+  for (int b = 0; b < TN; ++b) {
+    ssrc[b] += t_begin >> spg_log;
+    if constexpr (AFF) zsrc[b] += t_begin >> spg_log;
+  }
 
   // Loads (an index past the end is clamped to a valid address; such data is
   // never used).
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < WDMA; ++i) {
       int o = 128 * st + wpiece[i];
-      o = o < RB - 16 ? o : RB - 16;           // past the row end: valid, unused
+      o = o < RBl - 16 ? o : RBl - 16;         // past the row end: valid, unused
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wsrc[i] + (uint32_t)o),
                                        reinterpret_cast<void*>(lds + W_LDS + slot * W_BYTES + (wave * WDMA + i) * 1024),
                                        16, 0, 0);
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
       const int n = n0 + wn * WNT + b * 32 + c32;
       cols[b] = n < N ? n : N - 1;
     }
-    for (int t = 0; t < T; ++t) {
+    for (int t = t_begin; t < t_begin + T; ++t) {
       const int gi = t >> spg_log;
       uint32_t s2[TN], zb[TN];
 #pragma unroll
@@ -524,6 +537,22 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
     run_direct(1);
   }
 
+  // Split of K: the share's partial tile goes to the workspace; a second
+  // kernel adds the shares in order and applies the output step.
+  if (sp.S > 1) {
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int n = n0 + wn * WNT + b * 32 + c32;
+          const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (m < M && n < N) sp.part[((int64_t)split * M + m) * N + n] = acc[a][b][i];
+        }
+    return;
+  }
+
   // Store: lane l holds column l%32 and rows 8*(i/4) + 4*(l/32) + (i%4) of each
   // 32x32 tile (register i). A block tile inside y (every block but the last
   // row and column of tiles) stores without per-output bounds checks; the
@@ -577,34 +606,114 @@ const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* 
   return nullptr;
 }
 
-hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
-                               const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                               int64_t group, void* y, Epilogue ep, hipStream_t stream) {
-  const int BK = tiled_bk(group);
-  const int G = (int)((K + group - 1) / group);
-  if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
-  // Block tile (rows of x x weight rows), always four wavefronts side by side
-  // along N: the first of 128 x 256, 128 x 128, 64 x 128 and 32 x 128 whose
-  // height fits M (rounded up to 32) and whose grid has 160 blocks or more,
-  // else 32 x 128. Measured on the 7B-class shapes: 128 x 256 is 7-8% faster
-  // than 256 x 128 (x is read from L2 half as often); a grid of about 170
-  // large tiles beats one of 340 smaller ones (M = 512 on [11008, 4096]: 60 us
-  // against 78), but 128 blocks on 256 CUs do not. For small M the narrow
-  // wave tiles (one 32-column MFMA tile each) expand every code once per
-  // block where 2 x 2 wavefronts expanded it twice: M = 128 on [4096, 11008]
-  // 70.4 -> 50.0 us with 32 x 128 tiles, [4096, 4096] 29.2 -> 21.5 us.
+// Second step of a split of K: y[m, n] = act(sum over shares q = 0 .. S-1,
+// in that order, of part[q, m, n] + bias[n]) in y's precision. Four outputs
+// per thread (N a multiple of 4), one per thread otherwise.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int S,
+                                                           int64_t MN, int N, void* __restrict__ y,
+                                                           Epilogue ep) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= MN) return;
+  if ((N & 3) == 0) {                          // four outputs of one row
+    float4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < S; ++q) v += *reinterpret_cast<const float4_t*>(part + q * MN + i0);
+    const int64_t n = i0 % N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ep.store(y, i0 + j, v[j], n + j);
+  } else {
+    for (int64_t i = i0; i < i0 + 4 && i < MN; ++i) {
+      float v = 0.0f;
+      for (int q = 0; q < S; ++q) v += part[q * MN + i];
+      ep.store(y, i, v, i % N);
+    }
+  }
+}
+
+// Tile configuration, group cadence and split of K for one call.
+struct TiledPlan {
+  int cfg;          // 0: 128 x 256, 1: 128 x 128, 2: 64 x 128, 3: 32 x 128 block tiles
+  int BK, gs;       // codes per sub-step; group = BK << gs
+  int64_t tiles;    // output tiles
+  int S, steps;     // shares of K and sub-steps per share (S = 1: no split)
+  int64_t ws_bytes; // workspace the split needs (0 without one)
+};
+
+// Block tile (rows of x x weight rows), always four wavefronts side by side
+// along N: the first of 128 x 256, 128 x 128, 64 x 128 and 32 x 128 whose
+// height fits M (rounded up to 32) and whose grid has 160 blocks or more,
+// else 32 x 128. Measured on the 7B-class shapes: 128 x 256 is 7-8% faster
+// than 256 x 128 (x is read from L2 half as often); a grid of about 170
+// large tiles beats one of 340 smaller ones (M = 512 on [11008, 4096]: 60 us
+// against 78), but 128 blocks on 256 CUs do not. For small M the narrow
+// wave tiles (one 32-column MFMA tile each) expand every code once per
+// block where 2 x 2 wavefronts expanded it twice: M = 128 on [4096, 11008]
+// 70.4 -> 50.0 us with 32 x 128 tiles, [4096, 4096] 29.2 -> 21.5 us.
+// Split of K (only with a workspace): a grid of 128 tiles or fewer leaves at
+// least half the CUs idle while each block walks all of K alone, a chain of
+// sub-steps bound by load latency. Then K is cut into S = 2, 4 or 8 shares
+// (the most that keep the grid within two blocks per CU), each at least 16
+// sub-steps and starting on a packed super-tile and a group boundary. The
+// shares' partial tiles meet in the workspace and a second kernel adds them
+// in share order (deterministic; the kernel boundary orders the partials'
+// stores before their loads, where one kernel would need a device-wide cache
+// write-back per block, which measured 4x slower). Measured (graph replays):
+// M = 128 on [4096, 11008] 49.2 -> 31.4 us, on [4096, 4096] 21.0 -> 17.5 us;
+// grids of 256 tiles were slower split (M = 256 on [4096, 4096] 23.0 -> 25.1
+// us, M = 512 29.5 -> 35.0 us) and are not.
+static TiledPlan tiled_plan(int64_t M, int64_t N, int64_t K, int64_t group) {
+  TiledPlan pl{};
+  pl.BK = tiled_bk(group);
   auto grid_of = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   const int64_t Mr = (M + 31) / 32 * 32;
-  int cfg = (Mr >= 128 && grid_of(128, 256) >= 160) ? 0
-          : (Mr >= 128 && grid_of(128, 128) >= 160) ? 1
-          : (Mr >= 64 && grid_of(64, 128) >= 160) ? 2 : 3;
+  pl.cfg = (Mr >= 128 && grid_of(128, 256) >= 160) ? 0
+         : (Mr >= 128 && grid_of(128, 128) >= 160) ? 1
+         : (Mr >= 64 && grid_of(64, 128) >= 160) ? 2 : 3;
   // (a 32-row tile of 32-code sub-steps is 2 KB of x: less than one DMA
   // instruction per wavefront, so group 32 takes 64-row tiles at least)
-  if (BK == 32 && cfg == 3) cfg = 2;
-  const int64_t blocks = cfg == 0 ? grid_of(128, 256) : grid_of(128 >> (cfg - 1), 128);
+  if (pl.BK == 32 && pl.cfg == 3) pl.cfg = 2;
+  pl.tiles = pl.cfg == 0 ? grid_of(128, 256) : grid_of(128 >> (pl.cfg - 1), 128);
+  pl.gs = 0;
+  while ((int64_t(pl.BK) << pl.gs) < group) ++pl.gs;
+  const int64_t T = K / pl.BK;
+  pl.S = 1;
+  pl.steps = (int)T;
+  const int64_t align = std::max<int64_t>(256 / pl.BK, int64_t(1) << pl.gs);
+  for (int S = 8; S >= 2 && pl.tiles <= 128; S /= 2) {
+    if (pl.tiles * S > 512) continue;
+    int64_t steps = (T + S - 1) / S;
+    steps = (steps + align - 1) / align * align;
+    const int64_t shares = (T + steps - 1) / steps;
+    if (steps < 16 || shares < 2) continue;
+    pl.S = (int)shares;
+    pl.steps = (int)steps;
+    break;
+  }
+  if (pl.S > 1) pl.ws_bytes = (int64_t)pl.S * M * N * 4;
+  return pl;
+}
+
+int64_t matmul_tiled_workspace(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (tiled_bk(group) == 0 || M < 1 || M >= (1ll << 31) || N >= (1ll << 31)) return 0;
+  return tiled_plan(M, N, K, group).ws_bytes;
+}
+
+hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
+                               const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                               int64_t group, void* y, Epilogue ep, void* workspace,
+                               int64_t workspace_bytes, hipStream_t stream) {
+  const int G = (int)((K + group - 1) / group);
+  if (M >= (1ll << 31) || N >= (1ll << 31)) return hipErrorInvalidValue;
+  TiledPlan pl = tiled_plan(M, N, K, group);
+  TiledSplit sp{nullptr, 1, pl.steps};
+  if (pl.S > 1 && workspace && workspace_bytes >= pl.ws_bytes) {
+    sp.part = static_cast<float*>(workspace);
+    sp.S = pl.S;
+  } else {
+    sp.steps = (int)(K / pl.BK);
+  }
+  const int64_t blocks = pl.tiles * sp.S;
   if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
-  int gs = 0;                                  // group = BK << gs
-  while ((int64_t(BK) << gs) < group) ++gs;
+  const int BK = pl.BK, gs = pl.gs, cfg = pl.cfg;
 #define INT4DQ_TILED_PICK(TMV, A, TNV)                                                                     \
   (BK == 32 ? matmul_tiled_kernel<32, 1, (TMV > 1 ? TMV : 2), A, 4, TNV>                                 \
    : gs == 0 ? matmul_tiled_kernel<64, 1, TMV, A, 4, TNV> : gs == 1 ? matmul_tiled_kernel<64, 2, TMV, A, 4, TNV> \
@@ -618,7 +727,14 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
 #undef INT4DQ_TILED_PICK
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const _Float16*>(x), (int)M, packed, scales, zeros, (int)N, (int)K, G,
-                     gs, y, ep);
+                     gs, y, ep, sp);
+  if (sp.S > 1) {
+    const int64_t MN = M * N;
+    const int64_t rblocks = (MN + 1023) / 1024;
+    if (rblocks >= (1ll << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, stream, sp.part, sp.S,
+                       MN, (int)N, y, ep);
+  }
   return hipGetLastError();
 }
 

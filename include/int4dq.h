@@ -254,6 +254,37 @@ int int4_linear(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
                 int64_t group, const float *bias, int act, void *y, int y_dtype, void *stream);
 
 /*
+ * int4_linear with a caller-owned device workspace, which lets the kernel for
+ * many rows of x cut K into shares when its grid of output tiles is too small
+ * to fill the GPU (a few hundred rows against a few thousand weight rows):
+ * each share's partial tile goes to the workspace and a second kernel adds
+ * the partials in share order and applies bias, activation and the output
+ * precision, so results do not depend on timing and stay within the
+ * tolerance of int4_matmul. Engine page ("Build a Blockwise INT4 Inference
+ * Engine"), layer forward, as int4_linear.
+ *   workspace       : device memory, 256-byte aligned, any contents, or NULL
+ *                     with workspace_bytes = 0.
+ *   workspace_bytes : its size. A call whose shape wants more than this (see
+ *                     int4_linear_workspace_bytes) runs without the split, as
+ *                     int4_linear does.
+ * Calls that share a workspace must not overlap (same stream, or ordered by
+ * events): they use it as their scratch. Other arguments, results and errors
+ * as int4_linear, plus EINVAL for a negative size, a NULL workspace with a
+ * positive size or a workspace that is not 256-byte aligned.
+ */
+int int4_linear_ws(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                   const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                   int64_t group, const float *bias, int act, void *y, int y_dtype,
+                   void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes int4_linear_ws uses for M rows of x_dtype activations, an
+ * [N, K] weight matrix and this group size, with 16-byte aligned x and packed
+ * codes (0: the call does not split K). -1 on invalid sizes or dtype.
+ */
+int64_t int4_linear_workspace_bytes(int x_dtype, int64_t M, int64_t N, int64_t K, int64_t group);
+
+/*
  * Kernel that int4_matmul would run for these arguments (an INT4DQ_PATH_*
  * other than AUTO), or -1 if the arguments are invalid. Enqueues nothing.
  */

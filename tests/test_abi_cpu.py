@@ -30,7 +30,8 @@ def test_header_declares_the_abi():
     assert _declared() == sorted(["int4_num_groups", "int4_packed_bytes", "int4_quantize", "int4_dequantize",
                                   "int4_unpack", "int4_matmul", "int4_matmul_ex", "int4_matmul_path",
                                   "int4_matmul_select", "int4_last_error", "int4_quantize_affine",
-                                  "int4_dequantize_affine", "int4_matmul_affine", "int4_linear"])
+                                  "int4_dequantize_affine", "int4_matmul_affine", "int4_linear",
+                                  "int4_linear_ws", "int4_linear_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -216,3 +217,58 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         dq.int4_matmul(torch.zeros(2, 8, dtype=torch.float16), torch.zeros(4, 4, dtype=torch.uint8),
                        torch.zeros(4, 1, dtype=torch.float16), 8, 8)
+
+
+def _split_bytes(tiles, S, M, N):
+    """Workspace of a split of K into S shares: S partial [M, N] binary32
+    results (the grid has `tiles` output tiles, S blocks each)."""
+    return S * M * N * 4
+
+
+@pytest.mark.parametrize("M,N,K,g,expect", [
+    # 32 x 128 tiles: 4 x 32 = 128 tiles -> 4 shares of 16 sub-steps (8 would be 1024 blocks)
+    (128, 4096, 4096, 128, _split_bytes(128, 4, 128, 4096)),
+    # K = 11008: 172 sub-steps, shares of 44 (a multiple of the 4-sub-step super-tile)
+    (128, 4096, 11008, 128, _split_bytes(128, 4, 128, 4096)),
+    # grids of more than 128 tiles are not split (64 x 128 tiles, 8 x 32)
+    (512, 4096, 4096, 128, 0), (512, 4096, 11008, 128, 0), (640, 2048, 4096, 128, 0),
+    # group 32: 64 x 128 tiles of 32-code sub-steps, 25 tiles -> 8 shares of 32
+    (300, 640, 8192, 32, _split_bytes(25, 8, 300, 640)),
+    # enough tiles already: 128 x 256 tiles, 16 x 16 and 4 x 43 and 2 x 112
+    (2048, 4096, 4096, 128, 0), (512, 11008, 4096, 128, 0), (256, 28672, 8192, 128, 0),
+    # the kernels for a few rows of x do not split
+    (1, 4096, 4096, 128, 0), (16, 4096, 4096, 128, 0),
+    # too short a K for 16 sub-steps per share
+    (128, 4096, 1024, 128, 0),
+    # 24 tiles of 32 x 128 and K = 8192: 8 shares of 16 sub-steps
+    (96, 1024, 8192, 128, _split_bytes(24, 8, 96, 1024)),
+    # 64 rows against 1024 weight rows: the skinny kernel takes it
+    (64, 1024, 8192, 128, 0),
+    # a group of 1024 codes: shares start on a group boundary (16 sub-steps)
+    (128, 4096, 4096, 1024, _split_bytes(128, 4, 128, 4096)),
+])
+def test_workspace_bytes(M, N, K, g, expect):
+    dq = _lib()
+    assert dq.lib.int4_linear_workspace_bytes(1, M, N, K, g) == expect
+    assert dq.linear_workspace_bytes(M, N, K, g) == expect
+
+
+def test_workspace_bytes_rejects():
+    dq = _lib()
+    L = dq.lib
+    assert L.int4_linear_workspace_bytes(1, -1, 8, 8, 4) == -1
+    assert L.int4_linear_workspace_bytes(1, 4, 0, 8, 4) == -1
+    assert L.int4_linear_workspace_bytes(7, 4, 8, 8, 4) == -1
+    assert L.int4_linear_workspace_bytes(1, 0, 8, 8, 4) == 0
+    assert L.int4_linear_workspace_bytes(0, 512, 4096, 4096, 128) == 0    # fp32 x: generic kernel
+
+
+@pytest.mark.parametrize("ws,nbytes,needle", [
+    (None, 1024, "workspace"), (FAKE, -1, "workspace_bytes"),
+    (ctypes.c_void_p(0x1010), 1024, "256-byte aligned"),
+])
+def test_linear_ws_rejects(ws, nbytes, needle):
+    dq = _lib()
+    rc = dq.lib.int4_linear_ws(FAKE, 1, 4, FAKE, FAKE, None, 8, 64, 32, None, 0, FAKE, 0, ws, nbytes, None)
+    assert rc == dq.EINVAL
+    assert needle in dq.lib.int4_last_error().decode()
