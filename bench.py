@@ -75,9 +75,11 @@ PHASE_KERNELS = {"quantize": "quantize_vec_kernel", "unpack": "unpack_flat_kerne
 
 
 def csrc_digest():
+    """sha256 of the kernel sources (.hip files and their device headers; the
+    host-side C ABI in api.cpp launches them but moves no bytes)."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h"))):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -112,6 +114,56 @@ def summarize_pmc(fetch_csv, write_csv, out_json, command=""):
     with open(out_json, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def summarize_trace(trace_csv, steps, out_txt, command=""):
+    """Per-shape kernel durations of the timed steps from a rocprofv3
+    --kernel-trace CSV of `bench.py --steps STEPS --no-unfused --no-report
+    --no-cpu-baseline`: in each phase's kernel family the last STEPS x
+    (launches per step) dispatches are the timed ones (nothing launches after
+    them in that run), and within a phase the shape of a dispatch is its
+    position mod 3 (every phase launches the shapes in the order of SHAPES)."""
+    import csv
+    import statistics
+
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    per_step = {"quantize": 3, "unpack": 3, "prefill_m2048": 3}
+    out = [f"rocprofv3 kernel trace of the timed steps, per shape (median, mean, min, max of the",
+           f"dispatch durations; timed steps only)", f"command: {command}", ""]
+    work = {}
+    for name, N, K in SHAPES:
+        work[name] = {"quantize": N * K * 4 + packed_weight_bytes(N, K),
+                      "unpack": N * ((K + 1) // 2) + N * K,
+                      "decode_m1": packed_weight_bytes(N, K),
+                      "prefill_m2048": 2 * M_PREFILL * N * K}
+    for phase, frag in PHASE_KERNELS.items():
+        d = [r for r in rows if frag in r["Kernel_Name"]]
+        if not d:
+            continue
+        count = per_step.get(phase)
+        if count is None:                      # decode: 3 shapes x R copies per step
+            R = max(2, -(-POOL_BYTES // sum(packed_weight_bytes(N, K) for _, N, K in SHAPES)))
+            count = 3 * R
+        timed = d[-steps * count:]
+        out.append(f"{phase} ({frag}), {len(timed)} dispatches")
+        unit, peak = ("GB/s", HBM_PEAK_GBS) if phase != "prefill_m2048" else ("TFLOP/s", FP16_MFMA_PEAK_TFLOPS)
+        for i, (name, N, K) in enumerate(SHAPES):
+            us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed[i::3]]
+            med = statistics.median(us)
+            rate = work[name][phase] / med / (1e3 if unit == "GB/s" else 1e6)
+            out.append(f"  {name:10s} [{N},{K}]  median {med:8.3f} us  mean {statistics.mean(us):8.3f}  "
+                       f"min {min(us):8.3f}  max {max(us):8.3f}  -> {rate:8.1f} {unit} "
+                       f"({rate / peak:.4f} of peak)")
+        allus = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        tot = sum(work[n][phase] for n, _, _ in SHAPES)
+        rate = tot * len(allus) / 3 / sum(allus) / (1e3 if unit == "GB/s" else 1e6)
+        out.append(f"  all three: mean {statistics.mean(allus):.3f} us per launch -> {rate:.1f} {unit} "
+                   f"({rate / peak:.4f} of peak)")
+        out.append("")
+    text = "\n".join(out)
+    with open(out_txt, "w") as f:
+        f.write(text + "\n")
+    print(text)
 
 
 def measured_traffic():
@@ -305,23 +357,27 @@ def stream_read_ceiling(copies):
     matmul (graph replays, median of five): a plain read of each copy's packed
     bytes (the probe kernel: 1 KB per wavefront load, four loads in flight per
     lane, 8 blocks of 4 wavefronts per CU), the bytes int4_matmul streams at
-    M = 1 less the 1.5% of scales."""
+    M = 1 less the 1.5% of scales; the faster of 512 and 2048 blocks, the
+    better launch shape for large and for small pools)."""
     import torch
     lib = _probe_lib()
     sink = torch.zeros(1, dtype=torch.int32, device=copies[0][0].device)
-    it = {"k": 0}
+    best = float("inf")
+    for blocks in (512, 2048):                 # the faster of two launch shapes
+        it = {"k": 0}
 
-    def call():
-        p = copies[it["k"] % len(copies)][0]
-        it["k"] += 1
-        assert lib.int4dq_probe_stream_read(p.data_ptr(), p.numel(), sink.data_ptr(), 2048,
-                                            torch.cuda.current_stream().cuda_stream) == 0
-    us = _graph_time_us(call, len(copies))
-    return copies[0][0].numel() / us / 1e3
+        def call():
+            p = copies[it["k"] % len(copies)][0]
+            it["k"] += 1
+            assert lib.int4dq_probe_stream_read(p.data_ptr(), p.numel(), sink.data_ptr(), blocks,
+                                                torch.cuda.current_stream().cuda_stream) == 0
+        best = min(best, _graph_time_us(call, len(copies)))
+    return copies[0][0].numel() / best / 1e3
 
 
 def case_report(dev):
-    """Every case of the report timed on its own: HIP graphs of the call,
+    """Every case of the report timed on its own (int4_linear_ws, binary32 y, with
+    the workspace its shape asks for): HIP graphs of the call,
     median of five replays (min and max beside it); for M <= 16 the weights
     rotate through a >= 1 GiB pool of copies so every launch streams them from
     HBM. Each case gets its roofline min(HBM, MFMA) from its algorithmic bytes
@@ -376,20 +432,22 @@ def case_report(dev):
             x = torch.from_numpy(workloads.activations(M, K)).to(dev)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             pool = copies if M <= 16 else copies[:1]
+            ws = dq.linear_workspace(M, N, K, g, device=dev)      # split of K where it helps
+            wptr = ws.data_ptr() if ws.numel() else None
             it = {"k": 0}
 
             def call():
                 p, s_ = pool[it["k"] % len(pool)]
                 it["k"] += 1
-                assert L.int4_matmul(x.data_ptr(), 1, M, p.data_ptr(), s_.data_ptr(), N, K, g,
-                                     y.data_ptr(), cur()) == 0
+                assert L.int4_linear_ws(x.data_ptr(), 1, M, p.data_ptr(), s_.data_ptr(), None, N, K, g,
+                                        None, 0, y.data_ptr(), 0, wptr, ws.numel(), cur()) == 0
             ts = _graph_times_us(call, len(pool) if M <= 16 else 10)
             us = statistics.median(ts)
             nbytes, flops = algorithmic(N, K, g, M)
             t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e3), flops / (FP16_MFMA_PEAK_TFLOPS * 1e6)
             bound = "hbm" if t_hbm >= t_mfma else "mfma"
             rec = {"case": f"{cfg} {name} [{N},{K}] g={g} M={M}",
-                   "kernel": dq.matmul_select(x, p0, s0, K, g),
+                   "kernel": dq.matmul_select(x, p0, s0, K, g) + (" split of K" if ws.numel() else ""),
                    "time_us": round(us, 3), "min_us": round(min(ts), 3), "max_us": round(max(ts), 3),
                    "bound": bound, "roofline_us": round(max(t_hbm, t_mfma), 3),
                    "frac_of_roofline": round(max(t_hbm, t_mfma) / us, 4),
@@ -406,7 +464,7 @@ def case_report(dev):
                 rec["gate"] = f">= {GATE_MFMA_FRAC} of the fp16 MFMA peak"
                 rec["pass"] = flops / us / 1e6 / FP16_MFMA_PEAK_TFLOPS >= GATE_MFMA_FRAC
             out.append(rec)
-            del x, y
+            del x, y, ws
         del copies, p0, s0
         torch.cuda.empty_cache()
     return out
@@ -461,9 +519,14 @@ def main():
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-report", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STEPS", "OUT_TXT"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, command=os.environ.get("PMC_COMMAND", ""))
+        return
+    if args.summarize_trace:
+        csv_path, steps, out_txt = args.summarize_trace
+        summarize_trace(csv_path, int(steps), out_txt, command=os.environ.get("TRACE_COMMAND", ""))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no "
