@@ -68,6 +68,8 @@ SIGNATURES = {
     "int4_linear_ws": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _int,
                               _vp, _i64, _vp]),
     "int4_linear_workspace_bytes": (_i64, [_int, _i64, _i64, _i64, _i64]),
+    "int4_linear_noalloc": (_int, [_vp, _int, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _int,
+                                   _vp]),
     "int4_last_error": (ctypes.c_char_p, []),
 }
 

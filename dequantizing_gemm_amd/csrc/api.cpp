@@ -8,10 +8,25 @@
 #include <stdio.h>
 #include <stdarg.h>
 
+#include <mutex>
+
 #include "../../include/int4dq.h"
 #include "kernels.h"
 
+// Scratch of int4_linear_noalloc: the workspace of a split of K for callers
+// that cannot allocate. Every GPU the library runs on holds its own copy, from
+// module load to the end of the process. The split plans need at most
+// 16 MiB (four shares of a [512, 2048] binary32 result, or eight of a quarter
+// of that), so the array is that size. In host code its name is only a
+// stand-in: the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[16 << 20];
+
 namespace {
+
+constexpr int64_t kScratchBytes = 16 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};         // device address of scratch, per device
 
 thread_local char g_err[512] = "";
 
@@ -194,6 +209,36 @@ int int4_linear_ws(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
     return fail(INT4DQ_EINVAL, "int4_linear_ws: workspace must be 256-byte aligned");
   return matmul_impl("int4_linear_ws", x, x_dtype, M, packed, scales, zeros, N, K, group, bias, act, y,
                      y_dtype, INT4DQ_PATH_AUTO, stream, workspace, workspace_bytes);
+}
+
+int int4_linear_noalloc(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
+                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                        int64_t group, const float* bias, int act, void* y, int y_dtype, void* stream) {
+  const int rc = check_matmul(x, x_dtype, M, packed, scales, N, K, group, y);
+  if (rc != INT4DQ_OK) return rc;
+  const int64_t need = int4_linear_workspace_bytes(x_dtype, M, N, K, group);
+  if (need > kScratchBytes)
+    return fail(INT4DQ_EINVAL, "int4_linear_noalloc: this shape needs %lld bytes of scratch, more than the "
+                               "%lld the library holds per device", (long long)need, (long long)kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "int4_linear_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+      return fail(INT4DQ_EUNSUPPORTED, "int4_linear_noalloc: device %d is beyond the %d the scratch table holds",
+                  dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {                 // once per device, with that device current
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "int4_linear_noalloc: hipGetSymbolAddress(scratch)");
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return matmul_impl("int4_linear_noalloc", x, x_dtype, M, packed, scales, zeros, N, K, group, bias, act, y,
+                     y_dtype, INT4DQ_PATH_AUTO, stream, ws, ws ? kScratchBytes : 0);
 }
 
 int int4_matmul(const void* x, int x_dtype, int64_t M, const uint8_t* packed,

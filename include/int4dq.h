@@ -278,6 +278,24 @@ int int4_linear_ws(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * int4_linear_ws for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call with the library's own scratch as the workspace. The library
+ * holds one 16 MiB scratch array per GPU from module load to the end of the
+ * process (the split plans need at most that); this call allocates and frees
+ * nothing. The device of the call's stream must be the current device.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (several streams or threads at once) race, so they must be ordered.
+ * Arguments, results and errors as int4_linear, plus EINVAL when a shape would
+ * need more scratch than the library holds, EUNSUPPORTED for a device ordinal
+ * of 64 or more, and EHIP if the scratch's device address cannot be obtained.
+ */
+int int4_linear_noalloc(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
+                        const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                        int64_t group, const float *bias, int act, void *y, int y_dtype,
+                        void *stream);
+
+/*
  * Workspace bytes int4_linear_ws uses for M rows of x_dtype activations, an
  * [N, K] weight matrix and this group size, with 16-byte aligned x and packed
  * codes (0: the call does not split K). -1 on invalid sizes or dtype.

@@ -31,7 +31,7 @@ def test_header_declares_the_abi():
                                   "int4_unpack", "int4_matmul", "int4_matmul_ex", "int4_matmul_path",
                                   "int4_matmul_select", "int4_last_error", "int4_quantize_affine",
                                   "int4_dequantize_affine", "int4_matmul_affine", "int4_linear",
-                                  "int4_linear_ws", "int4_linear_workspace_bytes"])
+                                  "int4_linear_ws", "int4_linear_workspace_bytes", "int4_linear_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -272,3 +272,12 @@ def test_linear_ws_rejects(ws, nbytes, needle):
     rc = dq.lib.int4_linear_ws(FAKE, 1, 4, FAKE, FAKE, None, 8, 64, 32, None, 0, FAKE, 0, ws, nbytes, None)
     assert rc == dq.EINVAL
     assert needle in dq.lib.int4_last_error().decode()
+
+
+def test_linear_noalloc_rejects_before_any_hip_call():
+    dq = _lib()
+    L = dq.lib
+    assert L.int4_linear_noalloc(FAKE, 1, -1, FAKE, FAKE, None, 8, 64, 32, None, 0, FAKE, 0, None) == dq.EINVAL
+    assert L.int4_linear_noalloc(FAKE, 1, 4, None, FAKE, None, 8, 64, 32, None, 0, FAKE, 0, None) == dq.EINVAL
+    assert L.int4_linear_noalloc(FAKE, 9, 4, FAKE, FAKE, None, 8, 64, 32, None, 0, FAKE, 0, None) == dq.EINVAL
+    assert L.int4_linear_noalloc(FAKE, 1, 4, FAKE, FAKE, None, 8, 64, 32, None, 5, FAKE, 0, None) == dq.EINVAL
