@@ -166,6 +166,64 @@ def summarize_trace(trace_csv, steps, out_txt, command=""):
     print(text)
 
 
+def summarize_counters(out_txt, csvs, command=""):
+    """Per-shape medians of the tiled kernel's counters from rocprofv3 --pmc
+    runs of `bench.py --steps 2 --warmup 1 --no-unfused --no-report
+    --no-cpu-baseline` (one CSV per pass): the prefill phase launches the
+    three shapes in the order of SHAPES, so a dispatch's shape is its
+    position mod 3 among the tiled kernel's dispatches. Adds the kernel
+    clock, the matrix-pipe busy share (the profiler's MfmaUtil expression),
+    MFMA flops against 2MNK and each wave-cycle counter as a share of
+    SQ_WAVE_CYCLES."""
+    import csv
+    import statistics
+
+    per = {name: {} for name, _, _ in SHAPES}
+    for path in csvs:
+        rows = [r for r in csv.DictReader(open(path)) if PHASE_KERNELS["prefill_m2048"] in r["Kernel_Name"]]
+        disp = {}
+        for r in rows:
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"dur_us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+        ids = sorted(disp)
+        for i, (name, _, _) in enumerate(SHAPES):
+            for k in ids[i::3]:
+                for c, v in disp[k].items():
+                    per[name].setdefault(c, []).append(v)
+    out = ["Counters of the tiled kernel (matmul_tiled_kernel) in the bench's prefill phase, per shape",
+           "(medians over the dispatches of all passes; M = 2048, group 128, fp16 x, fp32 y)",
+           f"command: {command}", ""]
+    for name, N, K in SHAPES:
+        m = {c: statistics.median(v) for c, v in per[name].items()}
+        out.append(f"{name} [{N},{K}] M={M_PREFILL}: dispatch {m['dur_us']:.1f} us")
+        for c in sorted(k for k in m if k != "dur_us"):
+            out.append(f"  {c:34s} {m[c]:.6g}")
+        if "GRBM_GUI_ACTIVE" in m:
+            gui = m["GRBM_GUI_ACTIVE"] / 8                 # the CSV sums the 8 XCDs
+            out.append(f"  kernel clock {gui / m['dur_us'] / 1e3:.2f} GHz (GRBM_GUI_ACTIVE / 8 / duration)")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                out.append(f"  MfmaUtil {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * 1024):.1f}% "
+                           "(MFMA busy cycles / (GUI-active cycles x 1024 SIMDs))")
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
+            out.append(f"  MFMA flops / 2MNK = {m['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / (2 * M_PREFILL * N * K):.4f}")
+        if "SQ_WAVE_CYCLES" in m:
+            wc = m["SQ_WAVE_CYCLES"]
+            shares = [c for c in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                                  "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_MISC", "SQ_WAIT_INST_ANY",
+                                  "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS") if c in m]
+            out.append("  share of wave cycles: " + ", ".join(f"{c[3:]} {m[c] / wc:.2f}" for c in shares))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            out.append(f"  VALU co-issued in {m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.2f} "
+                       "of the matrix pipe's busy cycles")
+        if "SQ_INSTS_VALU" in m and "SQ_INSTS_MFMA" in m:
+            out.append(f"  VALU instructions per MFMA: {(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / m['SQ_INSTS_MFMA']:.2f}")
+        out.append("")
+    text = "\n".join(out)
+    with open(out_txt, "w") as f:
+        f.write(text + "\n")
+    print(text)
+
+
 def measured_traffic():
     """Per-phase traffic from the committed counter summary, or {} if the
     kernel sources have changed since it was taken."""
@@ -520,9 +578,14 @@ def main():
     ap.add_argument("--no-report", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STEPS", "OUT_TXT"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="OUT_TXT CSV")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, command=os.environ.get("PMC_COMMAND", ""))
+        return
+    if args.summarize_counters:
+        out_txt, *csvs = args.summarize_counters
+        summarize_counters(out_txt, csvs, command=os.environ.get("PMC_COMMAND", ""))
         return
     if args.summarize_trace:
         csv_path, steps, out_txt = args.summarize_trace
