@@ -272,6 +272,234 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   }
 }
 
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left free (gfx9 encoding).
+template <int NW>
+__device__ __forceinline__ void wait_vmcnt_skinny() {
+  static_assert(NW >= 0 && NW < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((NW & 0xF) | ((NW >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane from x (a buffer of nbytes bytes) at byte voff + soff to
+// LDS at lds + 16 * lane, by DMA. (A device function rather than a lambda
+// body: the buffer resource type exists only on the device side.)
+__device__ __forceinline__ void x_to_lds(const _Float16* x, int nbytes, uint8_t* lds, uint32_t voff,
+                                         int soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(x), (short)0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff,
+                                           0, 0);
+}
+
+// v of lane i ^ 8 in each row of 16 lanes (DPP row_ror:8).
+__device__ __forceinline__ uint32_t swap8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+}
+
+// Pipelined form for 5 to 16 rows of x with K a multiple of 256 and group
+// sizes 128 * 2^p. A block of 4 wavefronts owns RG groups of 16 weight rows;
+// the wavefronts split K into pair-blocks of 256 codes (two K-blocks;
+// wavefront w takes pair-blocks w, w + 4, ...), and each walks its share with
+// the loads of the next P pair-blocks in flight.
+//
+//  * Weights: a pair-block is 128 bytes -- one whole cache line -- of each of
+//    16 rows, read by two loads of 8 rows x 128 bytes (load A: rows 0-7,
+//    load B: rows 8-15; lane (n, g) = (lane % 16, lane / 16) reads piece
+//    g + 4 (n / 8) of row n % 8 in A and piece g + 4 (1 - n / 8) of row
+//    8 + n % 8 in B). Loads of 16 rows x 64 bytes touch each line twice and
+//    ran a quarter slower in a read-only test. The MFMA wants row n in lane
+//    (n, g): pieces g and 4 + g of row n are the lane's own half of one load
+//    and the other half of lane (n ^ 8, g)'s, fetched by one DPP row rotate.
+//    Piece g holds codes 32 g .. 32 g + 31 of the first K-block, piece 4 + g
+//    those of the second, so MFMAs 0-3 (first K-block, first group) and 4-7
+//    (second) each stay inside one group.
+//  * x: the pair-block of x (XR rows x 512 bytes, XR = 8 or 16) goes into a
+//    slot of the wavefront's own LDS ring by DMA (2 rows per load); 16-byte
+//    chunk c of row r sits at position c ^ r, so sixteen rows' reads of one
+//    chunk fall in distinct banks.
+//  * Scales (and zero points) of both K-blocks per row group: one 32-bit
+//    (16-bit) load when the group is 128 (GP), else one 16-bit (8-bit) load
+//    that serves both.
+// The MFMA arithmetic is the direct-load form of the kernel above (natural
+// code order, the group's scale on each partial; rows of x >= M repeat a
+// lower row and are discarded). The four wavefronts' partial tiles are added
+// through LDS at the end.
+template <int RG, int P, bool AFF, int XR, bool GP>
+__global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
+    const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
+    int kb_shift, void* __restrict__ y, Epilogue ep) {
+  constexpr int PB = 256, WAVES = 4;           // codes per pair-block
+  static_assert(XR == 8 || XR == 16, "x rows staged");
+  constexpr int XI = XR / 2;                   // x DMA loads per pair-block (2 rows each)
+  constexpr int SLOT = XR * 2 * PB;            // bytes of one pair-block of x
+  constexpr int RING = WAVES * P * SLOT;
+  constexpr int RED = WAVES * RG * 64 * 16;    // the partial tiles at the end
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING > RED ? RING : RED];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const bool lo = col < 8;
+  const int n0 = blockIdx.x * 16 * RG;
+  const int npb = K / PB;
+  const int nj = (npb - wave + WAVES - 1) / WAVES;   // pair-blocks of this wavefront (>= 1: npb >= 4)
+  const uint8_t* wa[RG];
+  const uint8_t* wb[RG];
+  const uint16_t* srow[RG];
+  const uint8_t* zrow[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    // rows past N: read row N - 1, discard
+    const int ra = n0 + 16 * r + (col & 7), rb = ra + 8, rn = n0 + 16 * r + col;
+    wa[r] = packed + (int64_t)(ra < N ? ra : N - 1) * (K >> 1) + 16 * (g + 4 * (col >> 3));
+    wb[r] = packed + (int64_t)(rb < N ? rb : N - 1) * (K >> 1) + 16 * (g + 4 * ((col >> 3) ^ 1));
+    srow[r] = scales + (int64_t)(rn < N ? rn : N - 1) * G;
+    zrow[r] = AFF ? zeros + (int64_t)(rn < N ? rn : N - 1) * G : nullptr;
+  }
+  // DMA source of lane l in x load t: row 2t + l/32 (rows >= M: row M-1),
+  // chunk (l % 32) ^ row, so that position l % 32 of the row holds that chunk
+  // (byte offsets into x; M * K * 2 < 2^31 is checked by the launcher). The
+  // loads are buffer loads: the compiler's wait counting treats a pending
+  // global-to-LDS load of the flat kind as possibly out of order and would
+  // wait for every load at the loop top.
+  const int xbytes = M * K * 2;
+  uint32_t xoff[XI];
+#pragma unroll
+  for (int t = 0; t < XI; ++t) {
+    const int r = 2 * t + (lane >> 5);
+    const int rr = r < M ? r : M - 1;
+    xoff[t] = (uint32_t)(rr * K * 2 + 16 * ((lane & 31) ^ r));
+  }
+  uint8_t* const ring = lds + wave * (P * SLOT);
+  // A operand of lane (col, g) for MFMA i: chunk (i < 4 ? 0 : 16) + 4g +
+  // i % 4 of row col (row col % XR: rows past XR are past M and discarded).
+  const int xr = col & (XR - 1);
+  int aoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) aoff[i] = xr * (2 * PB) + 16 * ((((i >> 2) << 4) + 4 * g + (i & 3)) ^ xr);
+
+  // Ring of P in-flight pair-blocks. Slot q holds the wavefront's pair-block
+  // j with j % P == q; an index past the share is clamped to its last one
+  // (loaded, not used), so every step issues the same loads.
+  u32x4_t wva[P][RG], wvb[P][RG];
+  uint32_t sv[P][RG];
+  uint16_t zv[P][RG];
+  auto issue = [&](int j, int q) __attribute__((always_inline)) {
+    const int jj = j < nj ? j : nj - 1;
+    const int pb = wave + WAVES * jj;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      if constexpr (GP) sv[q][r] = *reinterpret_cast<const uint32_t*>(srow[r] + 2 * pb);
+      else sv[q][r] = srow[r][(2 * pb) >> kb_shift];
+    }
+    if constexpr (AFF) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        if constexpr (GP) zv[q][r] = *reinterpret_cast<const uint16_t*>(zrow[r] + 2 * pb);
+        else zv[q][r] = zrow[r][(2 * pb) >> kb_shift];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < XI; ++t) x_to_lds(x, xbytes, ring + q * SLOT + t * 1024, xoff[t], pb * (2 * PB));
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      wva[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wa[r] + pb * (PB / 2)));
+      wvb[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wb[r] + pb * (PB / 2)));
+    }
+  };
+
+  float4_t acc[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Step j past the share (the last round of the ring) repeats the last
+  // pair-block with a zero scale factor: no branch in the loop, and its
+  // (finite) partial contributes nothing.
+  auto compute = [&](int q, bool live) __attribute__((always_inline)) {
+    half8_t xf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xf[i] = *reinterpret_cast<const half8_t*>(ring + q * SLOT + aoff[i]);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      uint32_t w[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a = wva[q][r][k], b = wvb[q][r][k];
+        w[k] = lo ? a : b;                     // own row, piece g
+        w[4 + k] = swap8(lo ? b : a);          // own row, piece 4 + g (from lane n ^ 8)
+      }
+      const uint32_t s2 = sv[q][r];
+      const float s0 = half_bits_to_float((uint16_t)s2);
+      const float s1 = half_bits_to_float((uint16_t)(GP ? s2 >> 16 : s2));
+      uint32_t zb0 = 0u, zb1 = 0u;
+      if constexpr (AFF) {
+        zb0 = zp_bias_natural((uint32_t)(zv[q][r] & 0xFF));
+        zb1 = zp_bias_natural((uint32_t)(GP ? zv[q][r] >> 8 : zv[q][r] & 0xFF));
+      }
+      float4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        half2_t hw[4];
+        if constexpr (AFF) codes_to_half_natural_zp(w[i], hw, zb0);
+        else codes_to_half_natural(w[i], hw);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[i], as_half8(hw), d0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        half2_t hw[4];
+        if constexpr (AFF) codes_to_half_natural_zp(w[4 + i], hw, zb1);
+        else codes_to_half_natural(w[4 + i], hw);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[4 + i], as_half8(hw), d1, 0, 0, 0);
+      }
+      acc[r] += (live ? s0 : 0.0f) * d0 + (live ? s1 : 0.0f) * d1;
+    }
+  };
+
+  // Loads per step; step j waits only for its own (loads complete in order,
+  // the x DMA included): the P - 1 steps issued after it may still be in
+  // flight. Its slot is then read back and refilled by the step P later.
+  constexpr int L = (AFF ? 2 : 1) * RG + XI + 2 * RG;
+  static_assert((P - 1) * L < 64, "vmcnt range");
+  // The prologue keeps its issue order too, so the first round's waits are
+  // the same as every later round's; the loop runs at least once (nj >= 1),
+  // so no branch separates it from the prologue.
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    issue(q, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int j0 = 0;
+  do {
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      wait_vmcnt_skinny<(P - 1) * L>();
+      __builtin_amdgcn_sched_barrier(0);
+      compute(q, j0 + q < nj);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j0 + q + P, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    j0 += P;
+  } while (j0 < nj);
+  wait_vmcnt_skinny<0>();
+
+  // Sum the four wavefronts' 16x16 partial tiles (the ring's LDS is reused
+  // once every wavefront is done with it). Lane l holds rows 4*(l/16) + i of
+  // column l%16.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG][64][4]
+#pragma unroll
+  for (int r = 0; r < RG; ++r) *reinterpret_cast<float4_t*>(red + ((wave * RG + r) * 64 + lane) * 4) = acc[r];
+  __syncthreads();
+  for (int t = tid; t < 16 * M * RG; t += 256) {
+    const int r = t / (16 * M), rem = t - r * 16 * M;
+    const int m = rem >> 4, nn = rem & 15;
+    const int src = (m >> 2) * 16 + nn, i = m & 3;
+    auto at = [&](int w) { return red[((w * RG + r) * 64 + src) * 4 + i]; };
+    const float v = (at(0) + at(1)) + (at(2) + at(3));
+    const int n = n0 + 16 * r + nn;
+    if (n < N) ep.store(y, (int64_t)m * N + n, v, n);
+  }
+}
+
 // KB for a group size, or 0 if the skinny kernel does not take it
 // (group / KB must be a power of two: the scale index is a shift).
 static int skinny_kb(int64_t group) {
@@ -423,6 +651,40 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
   int kbs = 0;
   while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);
+  if (M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 &&
+      M * K * 2 < ((int64_t)1 << 31)) {
+    // the pipelined form: as many row groups per block (4, 2 or 1) as keep
+    // the grid at 256 blocks or more; the paired scale (zero-point) load of
+    // groups of 128 needs 4-byte (2-byte) aligned scale (zero-point) rows
+    const int64_t rgroups = (N + 15) / 16;
+    const int RG = rgroups >= 4 * 256 ? 4 : rgroups >= 2 * 256 ? 2 : 1;
+    const bool gp = kbs == 0 && ((uintptr_t)scales & 3) == 0 && (!zeros || ((uintptr_t)zeros & 1) == 0);
+    if (kbs != 0 || gp) {
+      const dim3 grid((unsigned)((rgroups + RG - 1) / RG)), block(256);
+#define INT4DQ_PIPE(RGV, A, XRV, GPV)                                                                  \
+  hipLaunchKernelGGL((matmul_skinny_pipe_kernel<RGV, 2, A, XRV, GPV>), grid, block, 0, stream, xh,     \
+                     (int)M, packed, scales, zeros, (int)N, (int)K, G, kbs, y, ep)
+#define INT4DQ_PIPE_RG(A, XRV, GPV)                                                                    \
+  do {                                                                                                 \
+    if (RG == 4) INT4DQ_PIPE(4, A, XRV, GPV);                                                          \
+    else if (RG == 2) INT4DQ_PIPE(2, A, XRV, GPV);                                                     \
+    else INT4DQ_PIPE(1, A, XRV, GPV);                                                                  \
+  } while (0)
+#define INT4DQ_PIPE_X(A, GPV)                                                                          \
+  do {                                                                                                 \
+    if (M <= 8) INT4DQ_PIPE_RG(A, 8, GPV); else INT4DQ_PIPE_RG(A, 16, GPV);                            \
+  } while (0)
+      if (zeros) {
+        if (gp) INT4DQ_PIPE_X(true, true); else INT4DQ_PIPE_X(true, false);
+      } else {
+        if (gp) INT4DQ_PIPE_X(false, true); else INT4DQ_PIPE_X(false, false);
+      }
+#undef INT4DQ_PIPE_X
+#undef INT4DQ_PIPE_RG
+#undef INT4DQ_PIPE
+      return hipGetLastError();
+    }
+  }
   if (zeros)
     launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, stream);
   else
