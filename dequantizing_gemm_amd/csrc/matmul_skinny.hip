@@ -290,6 +290,16 @@ __device__ __forceinline__ void x_to_lds(const _Float16* x, int nbytes, uint8_t*
                                            0, 0);
 }
 
+// 16 bytes per lane from p (a buffer of nbytes bytes) at byte voff + soff to
+// LDS at lds + 16 * lane, by DMA; bytes past nbytes read as zero.
+template <typename T>
+__device__ __forceinline__ void lds_dma_16(const T* p, int nbytes, uint8_t* lds, uint32_t voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), (short)0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff,
+                                           0, 0);
+}
+
 // v of lane i ^ 8 in each row of 16 lanes (DPP row_ror:8).
 __device__ __forceinline__ uint32_t swap8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
@@ -316,9 +326,12 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 //    slot of the wavefront's own LDS ring by DMA (2 rows per load); 16-byte
 //    chunk c of row r sits at position c ^ r, so sixteen rows' reads of one
 //    chunk fall in distinct banks.
-//  * Scales (and zero points) of both K-blocks per row group: one 32-bit
-//    (16-bit) load when the group is 128 (GP), else one 16-bit (8-bit) load
-//    that serves both.
+//  * Scales (and zero points): the block's rows hold them contiguously, so
+//    they are copied to LDS once, at the start, by whole-line DMA (per-step
+//    loads touched one line per row for 4 bytes and cost as much request
+//    traffic as the weights). A step reads both K-blocks' scales of a row
+//    with one 32-bit LDS read when the group is 128 (GP), else one 16-bit
+//    read that serves both.
 // The MFMA arithmetic is the direct-load form of the kernel above (natural
 // code order, the group's scale on each partial; rows of x >= M repeat a
 // lower row and are discarded). The four wavefronts' partial tiles are added
@@ -328,6 +341,9 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
     int kb_shift, void* __restrict__ y, Epilogue ep) {
+  // Dynamic LDS: the block's scales (16 RG G binary16, rounded up to 1 KB),
+  // then its zero points (16 RG G bytes, rounded up to 1 KB).
+  extern __shared__ __attribute__((aligned(16))) uint8_t sz_lds[];
   constexpr int PB = 256, WAVES = 4;           // codes per pair-block
   static_assert(XR == 8 || XR == 16, "x rows staged");
   constexpr int XI = XR / 2;                   // x DMA loads per pair-block (2 rows each)
@@ -342,18 +358,33 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
   const int n0 = blockIdx.x * 16 * RG;
   const int npb = K / PB;
   const int nj = (npb - wave + WAVES - 1) / WAVES;   // pair-blocks of this wavefront (>= 1: npb >= 4)
+  const int nrows = N - n0 < 16 * RG ? N - n0 : 16 * RG;   // rows of the block below N
   const uint8_t* wa[RG];
   const uint8_t* wb[RG];
-  const uint16_t* srow[RG];
-  const uint8_t* zrow[RG];
+  int srow[RG];                                // LDS scale index of the lane's row
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     // rows past N: read row N - 1, discard
-    const int ra = n0 + 16 * r + (col & 7), rb = ra + 8, rn = n0 + 16 * r + col;
+    const int ra = n0 + 16 * r + (col & 7), rb = ra + 8, rl = 16 * r + col;
     wa[r] = packed + (int64_t)(ra < N ? ra : N - 1) * (K >> 1) + 16 * (g + 4 * (col >> 3));
     wb[r] = packed + (int64_t)(rb < N ? rb : N - 1) * (K >> 1) + 16 * (g + 4 * ((col >> 3) ^ 1));
-    srow[r] = scales + (int64_t)(rn < N ? rn : N - 1) * G;
-    zrow[r] = AFF ? zeros + (int64_t)(rn < N ? rn : N - 1) * G : nullptr;
+    srow[r] = (rl < nrows ? rl : nrows - 1) * G;
+  }
+  const int sbytes = (16 * RG * G * 2 + 1023) & ~1023;
+  const uint16_t* const ssh = reinterpret_cast<const uint16_t*>(sz_lds);
+  const uint8_t* const zsh = sz_lds + sbytes;
+  {
+    // 1 KB per DMA load (lane l: bytes 16 l); bytes past the block's rows
+    // (range-checked by the buffer load) read as zero and are not used
+    const int su = sbytes >> 10;
+    for (int u = wave; u < su; u += WAVES)
+      lds_dma_16(scales + (int64_t)n0 * G, nrows * G * 2, sz_lds + u * 1024, (uint32_t)(u * 1024 + 16 * lane), 0);
+    if constexpr (AFF) {
+      const int zu = (16 * RG * G + 1023) >> 10;
+      for (int u = wave; u < zu; u += WAVES)
+        lds_dma_16(zeros + (int64_t)n0 * G, nrows * G, sz_lds + sbytes + u * 1024,
+                   (uint32_t)(u * 1024 + 16 * lane), 0);
+    }
   }
   // DMA source of lane l in x load t: row 2t + l/32 (rows >= M: row M-1),
   // chunk (l % 32) ^ row, so that position l % 32 of the row holds that chunk
@@ -381,23 +412,9 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
   // j with j % P == q; an index past the share is clamped to its last one
   // (loaded, not used), so every step issues the same loads.
   u32x4_t wva[P][RG], wvb[P][RG];
-  uint32_t sv[P][RG];
-  uint16_t zv[P][RG];
   auto issue = [&](int j, int q) __attribute__((always_inline)) {
     const int jj = j < nj ? j : nj - 1;
     const int pb = wave + WAVES * jj;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      if constexpr (GP) sv[q][r] = *reinterpret_cast<const uint32_t*>(srow[r] + 2 * pb);
-      else sv[q][r] = srow[r][(2 * pb) >> kb_shift];
-    }
-    if constexpr (AFF) {
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        if constexpr (GP) zv[q][r] = *reinterpret_cast<const uint16_t*>(zrow[r] + 2 * pb);
-        else zv[q][r] = zrow[r][(2 * pb) >> kb_shift];
-      }
-    }
 #pragma unroll
     for (int t = 0; t < XI; ++t) x_to_lds(x, xbytes, ring + q * SLOT + t * 1024, xoff[t], pb * (2 * PB));
 #pragma unroll
@@ -413,7 +430,10 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
   // Step j past the share (the last round of the ring) repeats the last
   // pair-block with a zero scale factor: no branch in the loop, and its
   // (finite) partial contributes nothing.
-  auto compute = [&](int q, bool live) __attribute__((always_inline)) {
+  auto compute = [&](int q, int j) __attribute__((always_inline)) {
+    const bool live = j < nj;
+    const int pb = wave + WAVES * (live ? j : nj - 1);
+    const int si = GP ? 2 * pb : (2 * pb) >> kb_shift;
     half8_t xf[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) xf[i] = *reinterpret_cast<const half8_t*>(ring + q * SLOT + aoff[i]);
@@ -426,13 +446,13 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
         w[k] = lo ? a : b;                     // own row, piece g
         w[4 + k] = swap8(lo ? b : a);          // own row, piece 4 + g (from lane n ^ 8)
       }
-      const uint32_t s2 = sv[q][r];
+      const uint32_t s2 = GP ? *reinterpret_cast<const uint32_t*>(ssh + srow[r] + si) : ssh[srow[r] + si];
       const float s0 = half_bits_to_float((uint16_t)s2);
       const float s1 = half_bits_to_float((uint16_t)(GP ? s2 >> 16 : s2));
       uint32_t zb0 = 0u, zb1 = 0u;
       if constexpr (AFF) {
-        zb0 = zp_bias_natural((uint32_t)(zv[q][r] & 0xFF));
-        zb1 = zp_bias_natural((uint32_t)(GP ? zv[q][r] >> 8 : zv[q][r] & 0xFF));
+        zb0 = zp_bias_natural(zsh[srow[r] + si]);
+        zb1 = zp_bias_natural(zsh[srow[r] + si + (GP ? 1 : 0)]);
       }
       float4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -456,8 +476,8 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
   // Loads per step; step j waits only for its own (loads complete in order,
   // the x DMA included): the P - 1 steps issued after it may still be in
   // flight. Its slot is then read back and refilled by the step P later.
-  constexpr int L = (AFF ? 2 : 1) * RG + XI + 2 * RG;
-  static_assert((P - 1) * L < 64, "vmcnt range");
+  constexpr int L = XI + 2 * RG;
+  static_assert(P * L < 64, "vmcnt range");
   // The prologue keeps its issue order too, so the first round's waits are
   // the same as every later round's; the loop runs at least once (nj >= 1),
   // so no branch separates it from the prologue.
@@ -466,13 +486,20 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
     issue(q, q);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // every wavefront's scale and zero-point copies (older than the prologue's
+  // loads) have landed. A bare barrier: __syncthreads would also wait for
+  // the prologue's x copies, which only this wavefront reads.
+  wait_vmcnt_skinny<P * L>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   int j0 = 0;
   do {
 #pragma unroll
     for (int q = 0; q < P; ++q) {
       wait_vmcnt_skinny<(P - 1) * L>();
       __builtin_amdgcn_sched_barrier(0);
-      compute(q, j0 + q < nj);
+      compute(q, j0 + q);
       __builtin_amdgcn_sched_barrier(0);
       issue(j0 + q + P, q);
       __builtin_amdgcn_sched_barrier(0);
@@ -654,15 +681,16 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
   if (M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 &&
       M * K * 2 < ((int64_t)1 << 31)) {
     // the pipelined form: as many row groups per block (4, 2 or 1) as keep
-    // the grid at 256 blocks or more; the paired scale (zero-point) load of
-    // groups of 128 needs 4-byte (2-byte) aligned scale (zero-point) rows
+    // the grid at 256 blocks or more; the scale and zero-point copies want
+    // 16-byte aligned arrays and at most 32 KB of LDS
     const int64_t rgroups = (N + 15) / 16;
     const int RG = rgroups >= 4 * 256 ? 4 : rgroups >= 2 * 256 ? 2 : 1;
-    const bool gp = kbs == 0 && ((uintptr_t)scales & 3) == 0 && (!zeros || ((uintptr_t)zeros & 1) == 0);
-    if (kbs != 0 || gp) {
+    const bool gp = kbs == 0;
+    const int lds_sz = ((16 * RG * G * 2 + 1023) & ~1023) + (zeros ? (16 * RG * G + 1023) & ~1023 : 0);
+    if (((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 15) == 0 && lds_sz <= 32 * 1024) {
       const dim3 grid((unsigned)((rgroups + RG - 1) / RG)), block(256);
 #define INT4DQ_PIPE(RGV, A, XRV, GPV)                                                                  \
-  hipLaunchKernelGGL((matmul_skinny_pipe_kernel<RGV, 2, A, XRV, GPV>), grid, block, 0, stream, xh,     \
+  hipLaunchKernelGGL((matmul_skinny_pipe_kernel<RGV, 2, A, XRV, GPV>), grid, block, lds_sz, stream, xh, \
                      (int)M, packed, scales, zeros, (int)N, (int)K, G, kbs, y, ep)
 #define INT4DQ_PIPE_RG(A, XRV, GPV)                                                                    \
   do {                                                                                                 \

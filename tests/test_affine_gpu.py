@@ -151,7 +151,7 @@ MM = [
     (300, 4096, 128, 16, "skinny"),
     (300, 4096, 128, 40, "skinny"),   # four 16-row tiles
     (8200, 1024, 64, 24, "skinny"),   # two tiles, two row groups per block
-    (8300, 1152, 256, 12, "skinny"),  # 5 to 16 rows, K split over wavefronts: 9 K-blocks (3, 2, 2, 2)
+    (8300, 2304, 256, 12, "skinny"),  # 5 to 16 rows, K split over wavefronts: 9 pair-blocks (3, 2, 2, 2)
     # tiled: 32 x 128, 64 x 128, 128 x 128 and 128 x 256 block tiles over every
     # group cadence (BK 32; a group every 1, 2, 4, 8 sub-steps; decided at run time)
     (200, 1024, 32, 40, "tiled"),
