@@ -412,15 +412,22 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
   // j with j % P == q; an index past the share is clamped to its last one
   // (loaded, not used), so every step issues the same loads.
   u32x4_t wva[P][RG], wvb[P][RG];
+  // A step past the wavefront's share (the ring's last round) still issues
+  // its loads, so that the load counts the waits rely on stay fixed, but
+  // every lane of them reads the first 16 bytes of x and of the codes: one
+  // cache line each, not a pair-block's worth of traffic.
   auto issue = [&](int j, int q) __attribute__((always_inline)) {
-    const int jj = j < nj ? j : nj - 1;
-    const int pb = wave + WAVES * jj;
+    const bool live = j < nj;
+    const int pb = wave + WAVES * (live ? j : nj - 1);
 #pragma unroll
-    for (int t = 0; t < XI; ++t) x_to_lds(x, xbytes, ring + q * SLOT + t * 1024, xoff[t], pb * (2 * PB));
+    for (int t = 0; t < XI; ++t)
+      x_to_lds(x, xbytes, ring + q * SLOT + t * 1024, live ? xoff[t] : 0u, live ? pb * (2 * PB) : 0);
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
-      wva[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wa[r] + pb * (PB / 2)));
-      wvb[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wb[r] + pb * (PB / 2)));
+      const uint8_t* pa = live ? wa[r] + pb * (PB / 2) : packed;
+      const uint8_t* pbb = live ? wb[r] + pb * (PB / 2) : packed;
+      wva[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pa));
+      wvb[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pbb));
     }
   };
 
