@@ -42,6 +42,12 @@ copies of 512 MiB: under rocprofv3 --pmc they give the FETCH_SIZE and
 WRITE_SIZE readings of a kernel whose HBM traffic is known, which calibrates
 the same counters on the path's kernels.
 
+--decode-traffic runs, instead of the benchmark, three eager int4_linear_ws
+calls on each matrix of DECODE_TRAFFIC_CASES (the 5-16 row kernel and the
+M = 1 kernels it is compared with) and then the copy probe, for the same two
+counter runs; python bench.py --summarize-decode-pmc FETCH_CSV WRITE_CSV
+OUT_TXT writes their per-call HBM bytes beside the algorithmic bytes.
+
 python bench.py --summarize-pmc FETCH_CSV WRITE_CSV OUT_JSON turns the
 counter_collection.csv files of two such runs (one counter each) into
 per-launch HBM traffic per phase, scaled by the copy calibration, and records
@@ -114,6 +120,94 @@ def summarize_pmc(fetch_csv, write_csv, out_json, command=""):
     with open(out_json, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+# (configuration, matrix, N, K, M) of the decode traffic check, in launch order
+DECODE_TRAFFIC_CASES = [("c4", "q_proj", 4096, 4096, 1), ("c4", "q_proj", 4096, 4096, 16),
+                        ("c4", "up_proj", 11008, 4096, 1), ("c4", "up_proj", 11008, 4096, 16),
+                        ("c4", "down_proj", 4096, 11008, 1), ("c4", "down_proj", 4096, 11008, 16),
+                        ("c5", "ffn", 28672, 8192, 1), ("c5", "ffn", 28672, 8192, 8),
+                        ("c5", "ffn", 28672, 8192, 16)]
+DECODE_TRAFFIC_CALLS = 3
+
+
+def decode_traffic(dev):
+    """Three eager int4_linear_ws calls per case of DECODE_TRAFFIC_CASES (fp16 x,
+    fp32 y, the workspace the shape asks for), then the copy probe."""
+    import torch
+    import dequantizing_gemm_amd as dq
+    import workloads
+    L = dq.lib
+    st = torch.cuda.current_stream().cuda_stream
+    for cfg, name, N, K, M in DECODE_TRAFFIC_CASES:
+        gen = torch.Generator(device=dev).manual_seed(N + K)
+        w = torch.randn((N, K), generator=gen, device=dev) * 0.02
+        p, sc, _ = dq.quantize_int4(w, GROUP)
+        del w
+        x = torch.from_numpy(workloads.activations(M, K)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = dq.linear_workspace(M, N, K, GROUP, device=dev)
+        for _ in range(DECODE_TRAFFIC_CALLS):
+            assert L.int4_linear_ws(x.data_ptr(), 1, M, p.data_ptr(), sc.data_ptr(), None, N, K, GROUP, None,
+                                    0, y.data_ptr(), 0, ws.data_ptr() if ws.numel() else None, ws.numel(),
+                                    st) == 0
+        torch.cuda.synchronize()
+        print(f"bench: decode traffic {cfg} {name} [{N},{K}] M={M} ({dq.matmul_select(x, p, sc, K, GROUP)})",
+              file=sys.stderr, flush=True)
+        del p, sc, x, y, ws
+        torch.cuda.empty_cache()
+    copy_probe(dev)
+
+
+def copy_probe(dev):
+    """Three plain device-to-device copies of COPY_PROBE_BYTES (the counters'
+    calibration)."""
+    import torch
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def summarize_decode_pmc(fetch_csv, write_csv, out_txt, command=""):
+    """Per-call HBM bytes of the int4_linear_ws calls of `bench.py
+    --decode-traffic` from its two counter runs (FETCH_SIZE, WRITE_SIZE),
+    scaled by the copy calibration like summarize_pmc; the matmul dispatches
+    come DECODE_TRAFFIC_CALLS per case in the order of DECODE_TRAFFIC_CASES."""
+    import csv
+    import statistics
+    per = {}
+    factors = {}
+    for label, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        copy_max = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        factors[label] = COPY_PROBE_BYTES / 1024 / copy_max
+        mm = [r for r in rows if "matmul" in r["Kernel_Name"]]
+        if len(mm) != DECODE_TRAFFIC_CALLS * len(DECODE_TRAFFIC_CASES):
+            raise SystemExit(f"{path}: {len(mm)} matmul dispatches, expected "
+                             f"{DECODE_TRAFFIC_CALLS * len(DECODE_TRAFFIC_CASES)}")
+        for i, case in enumerate(DECODE_TRAFFIC_CASES):
+            grp = mm[i * DECODE_TRAFFIC_CALLS:(i + 1) * DECODE_TRAFFIC_CALLS]
+            per.setdefault(case, {})[label] = statistics.median(float(r["Counter_Value"]) for r in grp) \
+                * 1024 * factors[label]
+            per[case]["kernel"] = grp[0]["Kernel_Name"].split("(")[0].replace("void ", "")[:60]
+    lines = ["HBM traffic of int4_linear_ws on the decode shapes (median of "
+             f"{DECODE_TRAFFIC_CALLS} eager calls each; FETCH_SIZE and WRITE_SIZE scaled by",
+             f"the copy calibration: fetch x{factors['fetch']:.4f}, write x{factors['write']:.4f}); "
+             "algorithmic = packed codes + scales + x (fp16) + y (fp32)",
+             f"kernel sources sha256 {csrc_digest()}",
+             f"command: {command}", ""]
+    for case in DECODE_TRAFFIC_CASES:
+        cfg, name, N, K, M = case
+        alg, _ = algorithmic(N, K, GROUP, M)
+        f, w = per[case]["fetch"], per[case]["write"]
+        lines.append(f"{cfg} {name:9s} [{N},{K}] M={M:<2d} {per[case]['kernel']:60s} fetch {f / 1e6:9.3f} MB  "
+                     f"write {w / 1e6:7.3f} MB  algorithmic {alg / 1e6:9.3f} MB  traffic/algorithmic "
+                     f"{(f + w) / alg:.3f}")
+    with open(out_txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_trace(trace_csv, steps, out_txt, command=""):
@@ -440,7 +534,8 @@ def case_report(dev):
     rotate through a >= 1 GiB pool of copies so every launch streams them from
     HBM. Each case gets its roofline min(HBM, MFMA) from its algorithmic bytes
     and flops; M = 1 cases also get the streaming-read ceiling of the same pool
-    and their fraction of it; the gated cases (M = 1 on the 7B-class and FFN
+    and their fraction of it, cases of 2 to 16 rows their time over the same
+    matrix's M = 1 time; the gated cases (M = 1 on the 7B-class and FFN
     matrices, M = 2048 on the 7B-class matrices) report pass or fail."""
     import statistics
     import numpy as np
@@ -486,6 +581,7 @@ def case_report(dev):
         if min(Ms) <= 16:
             copies += [(p0.clone(), s0.clone()) for _ in range(max(1, -(-POOL_BYTES // wb) - 1))]
         ceiling = stream_read_ceiling(copies) if 1 in Ms else None
+        t_m1 = None
         for M in Ms:
             x = torch.from_numpy(workloads.activations(M, K)).to(dev)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -510,6 +606,10 @@ def case_report(dev):
                    "bound": bound, "roofline_us": round(max(t_hbm, t_mfma), 3),
                    "frac_of_roofline": round(max(t_hbm, t_mfma) / us, 4),
                    "gbs": round(nbytes / us / 1e3, 1), "tflops": round(flops / us / 1e6, 2)}
+            if M == 1:
+                t_m1 = us
+            elif M <= 16 and t_m1:
+                rec["time_vs_m1"] = round(us / t_m1, 3)
             if M == 1:
                 rec["weight_gbs"] = round(wb / us / 1e3, 1)
                 rec["weight_frac_of_peak"] = round(wb / us / 1e3 / HBM_PEAK_GBS, 4)
@@ -579,7 +679,12 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STEPS", "OUT_TXT"))
     ap.add_argument("--summarize-counters", nargs="+", metavar="OUT_TXT CSV")
+    ap.add_argument("--decode-traffic", action="store_true")
+    ap.add_argument("--summarize-decode-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"))
     args = ap.parse_args()
+    if args.summarize_decode_pmc:
+        summarize_decode_pmc(*args.summarize_decode_pmc, command=os.environ.get("PMC_COMMAND", ""))
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, command=os.environ.get("PMC_COMMAND", ""))
         return
@@ -603,6 +708,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode_traffic:
+        decode_traffic(dev)
+        return
     print("bench: generating inputs", file=sys.stderr, flush=True)
 
     mats = []
