@@ -306,7 +306,7 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 }
 
 // Pipelined form for 5 to 16 rows of x with K a multiple of 256 and group
-// sizes 128 * 2^p. A block of 4 wavefronts owns RG groups of 16 weight rows;
+// sizes 128 * 2^p. A block of 4 wavefronts owns RG (1 to 4) groups of 16 weight rows;
 // the wavefronts split K into pair-blocks of 256 codes (two K-blocks;
 // wavefront w takes pair-blocks w, w + 4, ...), and each walks its share with
 // the loads of the next P pair-blocks in flight.
@@ -687,11 +687,22 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
   const _Float16* xh = static_cast<const _Float16*>(x);
   if (M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 &&
       M * K * 2 < ((int64_t)1 << 31)) {
-    // the pipelined form: as many row groups per block (4, 2 or 1) as keep
-    // the grid at 256 blocks or more; the scale and zero-point copies want
-    // 16-byte aligned arrays and at most 32 KB of LDS
+    // the pipelined form: 4 row groups per block on wide matrices (x is
+    // re-read once per 64 weight rows); below 1024 row groups, the count of
+    // 1, 2 or 3 that gives the busiest CU the fewest rows (blocks spread
+    // evenly over 256 CUs; ties to more rows per block, which re-read x less):
+    // 688 row groups take 3 (230 blocks, 48 rows per CU, against 64 with 2).
+    // The scale and zero-point copies want 16-byte aligned arrays and at
+    // most 32 KB of LDS.
     const int64_t rgroups = (N + 15) / 16;
-    const int RG = rgroups >= 4 * 256 ? 4 : rgroups >= 2 * 256 ? 2 : 1;
+    int RG = 4;
+    if (rgroups < 4 * 256) {
+      int64_t best = -1;
+      for (int rg = 1; rg <= 3; ++rg) {
+        const int64_t rows = ((rgroups + rg - 1) / rg + 255) / 256 * rg;
+        if (best < 0 || rows <= best) best = rows, RG = rg;
+      }
+    }
     const bool gp = kbs == 0;
     const int lds_sz = ((16 * RG * G * 2 + 1023) & ~1023) + (zeros ? (16 * RG * G + 1023) & ~1023 : 0);
     if (((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 15) == 0 && lds_sz <= 32 * 1024) {
@@ -702,6 +713,7 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
 #define INT4DQ_PIPE_RG(A, XRV, GPV)                                                                    \
   do {                                                                                                 \
     if (RG == 4) INT4DQ_PIPE(4, A, XRV, GPV);                                                          \
+    else if (RG == 3) INT4DQ_PIPE(3, A, XRV, GPV);                                                     \
     else if (RG == 2) INT4DQ_PIPE(2, A, XRV, GPV);                                                     \
     else INT4DQ_PIPE(1, A, XRV, GPV);                                                                  \
   } while (0)

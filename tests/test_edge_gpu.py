@@ -190,6 +190,7 @@ PATH_CASES = [
     (300, 2048, 128, 1, "skinny"), (300, 2048, 64, 2, "skinny"), (300, 2048, 256, 4, "skinny"),
     (300, 2048, 128, 8, "skinny"), (300, 1024, 32, 16, "skinny"), (8200, 1024, 128, 8, "skinny"),
     (16400, 1024, 128, 6, "skinny"), (16400, 2304, 256, 12, "skinny"), (8300, 4096, 128, 16, "skinny"),
+    (8192, 2048, 128, 10, "skinny"),
     (300, 2048, 128, 24, "skinny"), (300, 2048, 128, 40, "skinny"),
     (4100, 1024, 128, 1280, "tiled"), (4100, 1024, 64, 1300, "tiled"), (4100, 2048, 1024, 1280, "tiled"),
     (2050, 1024, 64, 1280, "tiled"), (2048, 2048, 256, 630, "tiled"),
