@@ -28,7 +28,8 @@ Also after the timed steps, "cases" times every (configuration, matrix, M)
 of the workloads on its own (the small-transformer linears at M = 1, 4, 16
 with groups 64 and 32; the 7B-class linears at M = 1, 16, 512, 2048; the
 [28672, 8192] FFN matrix at M = 1, 8, 256, 4096, and its full-W quantize):
-median of five graph replays, each against its roofline min(HBM, MFMA) from
+median of five replays of a HIP graph of at least 100 back-to-back calls,
+each against its roofline min(HBM, MFMA) from
 its algorithmic bytes and flops, M = 1 also against a measured streaming-read
 ceiling of the same weight pool; the gated cases (M = 1 at >= 70% of HBM
 peak on packed weights + scales for the 7B-class and FFN matrices, M = 2048
@@ -452,6 +453,12 @@ def _graph_times_us(fn, reps, trials=5):
     return out
 
 
+def _reps(period, at_least=100):
+    """Calls per timed replay: at least `at_least` back-to-back launches, a
+    whole number of turns of a rotation pool of `period` copies."""
+    return -(-at_least // period) * period
+
+
 def _graph_time_us(fn, reps):
     """Median of five graph replays, microseconds per call."""
     import statistics
@@ -523,13 +530,13 @@ def stream_read_ceiling(copies):
             it["k"] += 1
             assert lib.int4dq_probe_stream_read(p.data_ptr(), p.numel(), sink.data_ptr(), blocks,
                                                 torch.cuda.current_stream().cuda_stream) == 0
-        best = min(best, _graph_time_us(call, len(copies)))
+        best = min(best, _graph_time_us(call, _reps(len(copies))))
     return copies[0][0].numel() / best / 1e3
 
 
 def case_report(dev):
     """Every case of the report timed on its own (int4_linear_ws, binary32 y, with
-    the workspace its shape asks for): HIP graphs of the call,
+    the workspace its shape asks for): HIP graphs of at least 100 calls,
     median of five replays (min and max beside it); for M <= 16 the weights
     rotate through a >= 1 GiB pool of copies so every launch streams them from
     HBM. Each case gets its roofline min(HBM, MFMA) from its algorithmic bytes
@@ -568,7 +575,7 @@ def case_report(dev):
 
             def qcall():
                 assert L.int4_quantize(w.data_ptr(), N, K, g, pq.data_ptr(), sq.data_ptr(), cur()) == 0
-            ts = _graph_times_us(qcall, 5)
+            ts = _graph_times_us(qcall, _reps(1))
             us = statistics.median(ts)
             out.append({"case": f"c5 int4_quantize [{N},{K}] g={g} (full W)", "time_us": round(us, 3),
                         "min_us": round(min(ts), 3), "max_us": round(max(ts), 3),
@@ -595,7 +602,7 @@ def case_report(dev):
                 it["k"] += 1
                 assert L.int4_linear_ws(x.data_ptr(), 1, M, p.data_ptr(), s_.data_ptr(), None, N, K, g,
                                         None, 0, y.data_ptr(), 0, wptr, ws.numel(), cur()) == 0
-            ts = _graph_times_us(call, len(pool) if M <= 16 else 10)
+            ts = _graph_times_us(call, _reps(len(pool)))
             us = statistics.median(ts)
             nbytes, flops = algorithmic(N, K, g, M)
             t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e3), flops / (FP16_MFMA_PEAK_TFLOPS * 1e6)
