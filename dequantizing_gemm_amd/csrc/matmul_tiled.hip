@@ -556,7 +556,10 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   // Store: lane l holds column l%32 and rows 8*(i/4) + 4*(l/32) + (i%4) of each
   // 32x32 tile (register i). A block tile inside y (every block but the last
   // row and column of tiles) stores without per-output bounds checks; the
-  // output precision is one branch for the whole tile.
+  // output precision is one branch for the whole tile. The stores are
+  // nontemporal (streamed past the caches): every block writes its whole
+  // tile at the end, and on the one-round grids all blocks do so at once
+  // (measured 0.8-2.8% faster per launch at M = 2048 on the 7B-class shapes).
   const bool full = m0 + BM <= M && n0 + BN <= N;
   auto store_all = [&](auto* yt) __attribute__((always_inline)) {
     typedef std::remove_pointer_t<decltype(yt)> T;
@@ -570,7 +573,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i], bn);
+            __builtin_nontemporal_store((T)ep.apply(acc[a][b][i], bn), yt + (int64_t)m * N + n);
           }
       } else {
 #pragma unroll
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = m0 + wm * WMT + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (m < M && n < N) yt[(int64_t)m * N + n] = (T)ep.apply(acc[a][b][i], bn);
+            if (m < M && n < N) __builtin_nontemporal_store((T)ep.apply(acc[a][b][i], bn), yt + (int64_t)m * N + n);
           }
       }
     }
