@@ -117,13 +117,16 @@ def test_dequantized_weight(L):
         assert np.array_equal(host(layer.dequantized_weight()).astype(np.float64), wh)
 
 
-def chain_check(layers_cfg, x, L, seed=0):
+def chain_check(layers_cfg, x, L, seed=0, edit=None):
     """Build the stack on the GPU and on the oracle side; check each layer's
-    output with the error carried from the layer before."""
+    output with the error carried from the layer before. edit(w, g), if
+    given, changes each layer's float weights in place before quantization."""
     rng = np.random.default_rng(seed)
     mods, ws = [], []
     for (K, N, g, affine, relu, out16) in layers_cfg:
         w = weights(N, K, int(rng.integers(1 << 30)), scale=1.0 / np.sqrt(K))
+        if edit is not None:
+            edit(w, g)
         b = (rng.normal(size=N) * 0.1).astype(np.float32)
         mods.append(L.Int4Linear.from_float(dev(w), dev(b), group=g, affine=affine, relu=relu,
                                             out_dtype=torch.float16 if out16 else torch.float32))
@@ -175,6 +178,29 @@ def test_c4_mlp_stack(L, M):
     x = np.random.default_rng(100 + M).normal(size=(M, 4096)).astype(np.float16)
     chain_check([(4096, 11008, 128, False, True, True), (11008, 4096, 128, True, False, False)], x, L,
                 seed=M)
+
+
+def edge_rows(w, g):
+    """The method's edge cases in a layer's weights: zero first, middle and
+    last groups, a row of -8 * 2^-24 (binary16 scale 0x0001, every code -8),
+    and a row a thousand times larger than the rest (scales near 4)."""
+    G = w.shape[1] // g
+    w[0, :g] = 0.0
+    w[1, (G // 2) * g:(G // 2 + 1) * g] = 0.0
+    w[2, (G - 1) * g:] = 0.0
+    w[3, :] = -8.0 * 2.0 ** -24
+    w[4, :] *= 1000.0
+
+
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_stack_edge_rows(L, M):
+    """A stack of two layers whose weights hold the edge rows, through the
+    gemv (M = 1), skinny (M = 16) and tiled (M = 300) kernels, symmetric then
+    affine codes, fp16 between the layers."""
+    say(f"case: stack with edge rows M={M}")
+    x = np.random.default_rng(500 + M).normal(size=(M, 512)).astype(np.float16)
+    chain_check([(512, 384, 128, False, True, True), (384, 256, 64, True, False, False)], x, L, seed=M,
+                edit=edge_rows)
 
 
 def test_persistence_round_trip(L, tmp_path):
