@@ -31,7 +31,9 @@ with groups 64 and 32; the 7B-class linears at M = 1, 16, 512, 2048; the
 median of five replays of a HIP graph of at least 100 back-to-back calls,
 each against its roofline min(HBM, MFMA) from
 its algorithmic bytes and flops, M = 1 also against a measured streaming-read
-ceiling of the same weight pool; the gated cases (M = 1 at >= 70% of HBM
+ceiling of the same weight pool, MFMA-bound cases also against a measured
+matrix-core ceiling (an MFMA-only probe kernel; the prefill roofline carries
+the same fraction); the gated cases (M = 1 at >= 70% of HBM
 peak on packed weights + scales for the 7B-class and FFN matrices, M = 2048
 at >= 50% of the fp16 MFMA peak) report pass or fail. --no-report skips it.
 
@@ -498,7 +500,7 @@ _probe = None
 
 
 def _probe_lib():
-    """The streaming-read probe (dequantizing_gemm_amd/probe), loaded by path."""
+    """The measurement probes (dequantizing_gemm_amd/probe), loaded by path."""
     global _probe
     if _probe is None:
         import ctypes
@@ -507,8 +509,40 @@ def _probe_lib():
         lib.int4dq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                                  ctypes.c_int, ctypes.c_void_p]
         lib.int4dq_probe_stream_read.restype = ctypes.c_int
+        lib.int4dq_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.int4dq_probe_mfma.restype = ctypes.c_int
         _probe = lib
     return _probe
+
+
+def mfma_ceiling():
+    """Measured dense binary16 matrix-core rate (TFLOP/s): the probe kernel
+    (eight independent chains of v_mfma_f32_32x32x16_f16 per wavefront, four
+    wavefronts per SIMD, nonzero operands, no memory traffic), median of five
+    launches of about 2 ms after three warm ones (the first launches after an
+    idle spell run at a lower clock). The ceiling MFMA-bound cases are
+    compared with beside the nominal peak."""
+    import statistics
+    import torch
+    lib = _probe_lib()
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    blocks, iters = 1024, 4096
+    flops = blocks * 4 * iters * 8 * 32768
+
+    def launch():
+        assert lib.int4dq_probe_mfma(blocks, iters, sink.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    return flops / statistics.median(ts) / 1e12
 
 
 def stream_read_ceiling(copies):
@@ -534,7 +568,7 @@ def stream_read_ceiling(copies):
     return copies[0][0].numel() / best / 1e3
 
 
-def case_report(dev):
+def case_report(dev, mfma_ceil=None):
     """Every case of the report timed on its own (int4_linear_ws, binary32 y, with
     the workspace its shape asks for): HIP graphs of at least 100 calls,
     median of five replays (min and max beside it); for M <= 16 the weights
@@ -542,8 +576,10 @@ def case_report(dev):
     HBM. Each case gets its roofline min(HBM, MFMA) from its algorithmic bytes
     and flops; M = 1 cases also get the streaming-read ceiling of the same pool
     and their fraction of it, cases of 2 to 16 rows their time over the same
-    matrix's M = 1 time; the gated cases (M = 1 on the 7B-class and FFN
-    matrices, M = 2048 on the 7B-class matrices) report pass or fail."""
+    matrix's M = 1 time; MFMA-bound cases their fraction of the measured
+    matrix-core ceiling `mfma_ceil` (TFLOP/s) when given; the gated cases (M = 1
+    on the 7B-class and FFN matrices, M = 2048 on the 7B-class matrices) report
+    pass or fail."""
     import statistics
     import numpy as np
     import torch
@@ -625,6 +661,9 @@ def case_report(dev):
                 if cfg in ("c4", "c5"):
                     rec["gate"] = f">= {GATE_HBM_FRAC} of HBM peak on packed weights + scales"
                     rec["pass"] = rec["weight_frac_of_peak"] >= GATE_HBM_FRAC
+            if bound == "mfma" and mfma_ceil:
+                rec["mfma_ceiling_tflops"] = round(mfma_ceil, 1)
+                rec["frac_of_measured_ceiling"] = round(flops / us / 1e6 / mfma_ceil, 4)
             if M == 2048 and cfg == "c4":
                 rec["gate"] = f">= {GATE_MFMA_FRAC} of the fp16 MFMA peak"
                 rec["pass"] = flops / us / 1e6 / FP16_MFMA_PEAK_TFLOPS >= GATE_MFMA_FRAC
@@ -867,8 +906,15 @@ def main():
             "fused_frac_of_library": round(roofs[3]["achieved"] / lib_tf, 4),
             "note": "F.linear (hipBLASLt) on the same three shapes, fp16 weights and output"}
     if not args.no_report:
+        print("bench: measured MFMA ceiling", file=sys.stderr, flush=True)
+        ceil_tf = mfma_ceiling()
+        line["mfma_ceiling_tflops"] = round(ceil_tf, 1)
+        for r in roofs:
+            if r["bound"] == "mfma":
+                r["measured_ceiling"] = round(ceil_tf, 1)
+                r["frac_of_measured_ceiling"] = round(r["achieved"] / ceil_tf, 4)
         print("bench: per-case report", file=sys.stderr, flush=True)
-        line["cases"] = case_report(dev)
+        line["cases"] = case_report(dev, ceil_tf)
         gated = [c for c in line["cases"] if "pass" in c]
         line["gates_passed"] = f"{sum(c['pass'] for c in gated)} of {len(gated)}"
     if args.copy_probe:

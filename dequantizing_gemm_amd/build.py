@@ -85,10 +85,11 @@ def _compile(src: str) -> str:
     return obj
 
 
-# The measurement probe (a plain streaming read, the ceiling the benchmark
-# compares bandwidth-bound kernels with) is its own small library: it is not
-# part of the path and the binding never loads it.
-PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+# The measurement probes (a plain streaming read and an MFMA-only loop, the
+# ceilings the benchmark compares bandwidth- and matrix-core-bound kernels
+# with) are their own small library: not part of the path, never loaded by
+# the binding.
+PROBE_SRCS = [os.path.join(PKG, "probe", "stream_read.hip"), os.path.join(PKG, "probe", "mfma_peak.hip")]
 PROBE_LIB = os.path.join(PKG, "probe", "libint4dq_probe.so")
 
 
@@ -107,11 +108,11 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = min(len(SOURCES) + 1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        probe = ex.submit(_compile, PROBE_SRC)
+        probes = [ex.submit(_compile, src) for src in PROBE_SRCS]
         objs = list(ex.map(_compile, SOURCES))
-        probe_obj = probe.result()
+        probe_objs = [f.result() for f in probes]
     _link(objs, LIB)
-    _link([probe_obj], PROBE_LIB)
+    _link(probe_objs, PROBE_LIB)
     if verbose:
         print(f"built {LIB} and {PROBE_LIB}")
     return LIB
