@@ -446,6 +446,31 @@ def test_matmul_epilogue(dq, N, K, g, M, path):
     assert np.array_equal(host(dq.int4_matmul_path(xd, pd, sd, K, g, path, bias=torch.zeros_like(bd))), y0)
 
 
+@pytest.mark.parametrize("g", [128, 64])
+def test_tiled_tile_order_ragged(dq, g):
+    """The tiled kernel's per-XCD tile order (taken when the grid is a
+    multiple of 8 tiles and of 4 tile rows) on a grid whose last row and
+    column of 128 x 256 tiles are partial: M = 1000 (8 tile rows, the last
+    one 104 rows), N = 5000 (20 tile columns, the last one 136 columns);
+    symmetric and affine codes against the oracle (64 sampled rows, every
+    column)."""
+    N, K, M = 5000, 512, 1000
+    say(f"case: tiled tile order, ragged edges N={N} K={K} g={g} M={M}")
+    rng = np.random.default_rng(g)
+    w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
+    x = rng.normal(size=(M, K)).astype(np.float16)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    xd, pd, sd = dev(x), dev(pr), dev(sr)
+    assert dq.matmul_select(xd, pd, sd, K, g) == "tiled"
+    check_matmul(host(dq.int4_matmul(xd, pd, sd, K, g)), x, pr, sr, K, g, what=f"tile order g={g}")
+    pa, sa, za, _ = oracle.quantize_int4_affine(w, g)
+    rows = sample_rows_cols(M, N, K)[0]
+    ya = host(dq.int4_matmul(xd, dev(pa), dev(sa), K, g, zeros=dev(za)))[rows]
+    ref, bound = oracle.int4_matmul_ex(x[rows], pa, sa, K, g, zeros=za, with_bound=True)
+    err = np.abs(ya.astype(np.float64) - ref)
+    assert np.all(err <= TOL * bound), f"affine tile order g={g}: {int((err > TOL * bound).sum())} outputs"
+
+
 def test_matmul_fp32_x(dq):
     say("case: binary32 activations, c1/c2 shapes and a [40,1000] g=7 matrix")
     for (N, K, g, M) in [(64, 256, 128, 4), (48, 301, 128, 3), (40, 1000, 7, 6)]:
