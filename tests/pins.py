@@ -315,7 +315,7 @@ def pin_storage_sizes(lib):
     assert mb(tot["packed"] + tot[32]) == gd["int4_g32_mb"]
     assert round(tot["fp32"] / (tot["packed"] + tot[64]), 2) == gd["ratio_g64"]
     assert round(tot["fp32"] / (tot["packed"] + tot[32]), 2) == gd["ratio_g32"]
-    # this build's own format: binary16 scales; ragged closed forms
+    # the library's own format: binary16 scales; ragged closed forms
     assert lib.int4_oracle_num_groups(301, 128) == 3 and lib.int4_oracle_packed_row_bytes(301) == 151
     assert lib.int4_oracle_num_groups(128, 128) == 1 and lib.int4_oracle_num_groups(129, 128) == 2
 
