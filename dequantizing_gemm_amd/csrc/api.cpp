@@ -87,7 +87,7 @@ int choose_path(const void* x, int x_dtype, int64_t M, const uint8_t* packed, in
   if (!int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group) &&
       int4dq::matmul_skinny_preferred(M, N))
     return INT4DQ_PATH_SKINNY;
-  if (!int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group)) return INT4DQ_PATH_TILED;
+  if (!int4dq::matmul_tiled_unsupported(x_dtype, M, x, packed, N, K, group)) return INT4DQ_PATH_TILED;
   return INT4DQ_PATH_GENERIC;
 }
 
@@ -298,7 +298,7 @@ int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uin
                         "int4_matmul gemv launch");
     }
     case INT4DQ_PATH_TILED: {
-      const char* why = int4dq::matmul_tiled_unsupported(x_dtype, x, packed, K, group);
+      const char* why = int4dq::matmul_tiled_unsupported(x_dtype, M, x, packed, N, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "%s: %s", fn, why);
       return hip_status(int4dq::launch_matmul_tiled(x, M, packed, scales, zeros, N, K, group, y, ep,
                                                     workspace, workspace_bytes, s),

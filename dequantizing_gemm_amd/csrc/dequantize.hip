@@ -18,7 +18,8 @@
 // become exact fp16 with codes_to_half_natural, one packed fp16 multiply per
 // pair (binary16 out) or a widening and one fp32 multiply per code (binary32
 // out), and 64 or 128 bytes of 16-byte stores. HBM-bound: 0.5 B read and 2 or
-// 4 B written per weight. Anything else: one thread per output element.
+// 4 B written per weight. Anything else: one thread per output element, the
+// grid striding over them.
 //
 // Affine codes ("Build a Blockwise INT4 Inference Engine", step 2): the
 // value is (u - zp) * scale with the group's zero point zp; u - zp in
@@ -82,15 +83,16 @@ __global__ __launch_bounds__(256) void dequantize_elem_kernel(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, int64_t N, int64_t K, int64_t G, int64_t group,
     void* __restrict__ out) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N * K) return;
-  const int64_t n = t / K, k = t - n * K;
-  const uint32_t b = packed[n * ((K + 1) >> 1) + (k >> 1)];
-  const uint32_t u = (b >> (4 * (k & 1))) & 0xFu;
-  const int q = AFF ? (int)u - (int)zeros[n * G + k / group] : sx4(u);
-  const float v = (float)q * half_bits_to_float(scales[n * G + k / group]);   // exact
-  if constexpr (HALF) static_cast<_Float16*>(out)[t] = (_Float16)v;           // nearest even
-  else static_cast<float*>(out)[t] = v;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < N * K;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = t / K, k = t - n * K;
+    const uint32_t b = packed[n * ((K + 1) >> 1) + (k >> 1)];
+    const uint32_t u = (b >> (4 * (k & 1))) & 0xFu;
+    const int q = AFF ? (int)u - (int)zeros[n * G + k / group] : sx4(u);
+    const float v = (float)q * half_bits_to_float(scales[n * G + k / group]);   // exact
+    if constexpr (HALF) static_cast<_Float16*>(out)[t] = (_Float16)v;           // nearest even
+    else static_cast<float*>(out)[t] = v;
+  }
 }
 
 template <bool AFF>
@@ -99,6 +101,8 @@ static void launch_dequantize_t(const uint8_t* packed, const uint16_t* scales,
                                 bool half, void* out, hipStream_t stream) {
   const int64_t G = (K + group - 1) / group;
   if (K % 32 == 0 && group % 32 == 0 && (uintptr_t)packed % 16 == 0 && (uintptr_t)out % 16 == 0) {
+    // (one thread per 32 codes: the grid stays below 2^32 threads for any
+    // output that fits a device, 2^37 codes being 256 GiB of binary16)
     const int64_t per_row = K / 32, chunks = N * per_row;
     const dim3 grid((unsigned)((chunks + 255) / 256)), block(256);
     if (half)
@@ -106,8 +110,7 @@ static void launch_dequantize_t(const uint8_t* packed, const uint16_t* scales,
     else
       hipLaunchKernelGGL((dequantize_flat_kernel<false, AFF>), grid, block, 0, stream, packed, scales, zeros, chunks, per_row, G, group, out);
   } else {
-    const int64_t total = N * K;
-    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    const dim3 grid(stride_grid((N * K + 255) / 256)), block(256);
     if (half)
       hipLaunchKernelGGL((dequantize_elem_kernel<true, AFF>), grid, block, 0, stream, packed, scales, zeros, N, K, G, group, out);
     else

@@ -153,4 +153,16 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// A dispatch holds fewer than 2^32 work items along each grid dimension, so a
+// grid of one thread (or one wavefront) per element stops launching at a few
+// billion elements, which one 288 GB device can hold. The element-wise kernels
+// therefore walk their elements with the grid's stride over at most this many
+// blocks of 256 threads (16.8 M threads, many times what the CUs hold at once).
+constexpr int64_t kStrideBlocks = int64_t(1) << 16;
+
+// Grid size for a kernel that would want `blocks` blocks, capped as above.
+inline unsigned stride_grid(int64_t blocks) {
+  return (unsigned)(blocks < kStrideBlocks ? (blocks > 0 ? blocks : 1) : kStrideBlocks);
+}
+
 }  // namespace int4dq

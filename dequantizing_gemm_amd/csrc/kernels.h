@@ -79,8 +79,8 @@ hipError_t launch_matmul_gemv(const void* x, int64_t M, const uint8_t* packed, c
                               const uint8_t* zeros, int64_t N, int64_t K, int64_t group, void* y, Epilogue ep,
                               hipStream_t stream);
 
-const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
-                                     int64_t K, int64_t group);
+const char* matmul_tiled_unsupported(int x_dtype, int64_t M, const void* x, const uint8_t* packed,
+                                     int64_t N, int64_t K, int64_t group);
 // workspace: nullptr, or workspace_bytes of device memory for a split of K
 // (any contents). The split is taken only when the workspace holds
 // matmul_tiled_workspace(M, N, K, group) bytes; that is 0 when the shape is

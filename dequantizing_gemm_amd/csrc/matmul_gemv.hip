@@ -536,7 +536,9 @@ const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
   if (group % 32 != 0) return "gemv kernel needs group to be a multiple of 32";
   if (K % 32 != 0) return "gemv kernel needs K to be a multiple of 32";
   if (K / 2 > 1024 * kGemvMaxChunks) return "gemv kernel takes K <= 32768";
-  if (N >= (1ll << 31)) return "gemv kernel needs N below 2^31";
+  // (its widest grids launch up to 128 threads per weight row, and a
+  // dispatch holds fewer than 2^32)
+  if (N >= (1ll << 25)) return "gemv kernel needs N below 2^25";
   if ((uintptr_t)x % 16 || (uintptr_t)packed % 16) return "gemv kernel needs 16-byte aligned x and packed";
   return nullptr;
 }

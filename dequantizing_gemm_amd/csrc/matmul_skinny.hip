@@ -556,7 +556,8 @@ const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
   if (K / KB > kSkinnyMaxKB) return "skinny kernel takes K <= 128 * min(group, 128)";
   // (four row tiles and eight K-blocks per wave do not fit 16 wavefronts' registers)
   if (M > 32 && K / KB > 16 * 6) return "skinny kernel takes M <= 32 when K > 96 * min(group, 128)";
-  if (N >= (1ll << 30)) return "skinny kernel needs N below 2^30";
+  // (up to 64 threads per weight row; a dispatch holds fewer than 2^32)
+  if (N >= (1ll << 25)) return "skinny kernel needs N below 2^25";
   if ((uintptr_t)x % 16 || (uintptr_t)packed % 16) return "skinny kernel needs 16-byte aligned x and packed";
   return nullptr;
 }

@@ -610,17 +610,6 @@ static int tiled_bk(int64_t group) {
   return 0;
 }
 
-const char* matmul_tiled_unsupported(int x_dtype, const void* x, const uint8_t* packed,
-                                     int64_t K, int64_t group) {
-  if (x_dtype != 1) return "tiled kernel takes binary16 activations only";
-  const int BK = tiled_bk(group);
-  if (BK == 0) return "tiled kernel takes group 32 or 64 times a power of two";
-  if (K % BK != 0) return "tiled kernel needs K to be a multiple of min(group, 64)";
-  if (K >= (1ll << 23)) return "tiled kernel needs K below 2^23";
-  if ((uintptr_t)x % 16 || (uintptr_t)packed % 16) return "tiled kernel needs 16-byte aligned x and packed";
-  return nullptr;
-}
-
 // Second step of a split of K: y[m, n] = act(sum over shares q = 0 .. S-1,
 // in that order, of part[q, m, n] + bias[n]) in y's precision. Four outputs
 // per thread (N a multiple of 4), one per thread otherwise.
@@ -712,6 +701,22 @@ int64_t matmul_tiled_workspace(int64_t M, int64_t N, int64_t K, int64_t group) {
   return tiled_plan(M, N, K, group).ws_bytes;
 }
 
+const char* matmul_tiled_unsupported(int x_dtype, int64_t M, const void* x, const uint8_t* packed,
+                                     int64_t N, int64_t K, int64_t group) {
+  if (x_dtype != 1) return "tiled kernel takes binary16 activations only";
+  const int BK = tiled_bk(group);
+  if (BK == 0) return "tiled kernel takes group 32 or 64 times a power of two";
+  if (K % BK != 0) return "tiled kernel needs K to be a multiple of min(group, 64)";
+  if (K >= (1ll << 23)) return "tiled kernel needs K below 2^23";
+  if (M >= (1ll << 31) || N >= (1ll << 31)) return "tiled kernel needs M and N below 2^31";
+  // one block of 256 threads per tile and share of K; a dispatch holds fewer
+  // than 2^32 threads
+  const TiledPlan pl = tiled_plan(M < 1 ? 1 : M, N, K, group);
+  if (pl.tiles * pl.S >= (1ll << 24)) return "tiled kernel takes at most 2^24 blocks (M x N too large)";
+  if ((uintptr_t)x % 16 || (uintptr_t)packed % 16) return "tiled kernel needs 16-byte aligned x and packed";
+  return nullptr;
+}
+
 hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
                                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                                int64_t group, void* y, Epilogue ep, void* workspace,
@@ -727,7 +732,7 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
     sp.steps = (int)(K / pl.BK);
   }
   const int64_t blocks = pl.tiles * sp.S;
-  if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
+  if (blocks >= (1ll << 24)) return hipErrorInvalidValue;   // refused by matmul_tiled_unsupported
   const int BK = pl.BK, gs = pl.gs, cfg = pl.cfg;
 #define INT4DQ_TILED_PICK(TMV, A, TNV)                                                                     \
   (BK == 32 ? matmul_tiled_kernel<32, 1, (TMV > 1 ? TMV : 2), A, 4, TNV>                                 \

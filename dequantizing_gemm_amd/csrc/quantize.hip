@@ -158,32 +158,34 @@ __global__ __launch_bounds__(256) void quantize_vec_kernel(
 __global__ __launch_bounds__(256) void quantize_scales_kernel(
     const float* __restrict__ w, int64_t N, int64_t K, int64_t group, int64_t G,
     uint16_t* __restrict__ scales) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N * G) return;
-  const int64_t n = t / G, gi = t - n * G;
-  const int64_t k0 = gi * group;
-  const int64_t k1 = k0 + group < K ? k0 + group : K;
-  float amax = 0.0f;
-  for (int64_t k = k0; k < k1; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(w[n * K + k]));
-  const _Float16 s16 = (_Float16)(amax / 7.0f);
-  scales[t] = __builtin_bit_cast(uint16_t, s16);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < N * G;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = t / G, gi = t - n * G;
+    const int64_t k0 = gi * group;
+    const int64_t k1 = k0 + group < K ? k0 + group : K;
+    float amax = 0.0f;
+    for (int64_t k = k0; k < k1; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(w[n * K + k]));
+    const _Float16 s16 = (_Float16)(amax / 7.0f);
+    scales[t] = __builtin_bit_cast(uint16_t, s16);
+  }
 }
 
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const float* __restrict__ w, int64_t N, int64_t K, int64_t group, int64_t G,
     const uint16_t* __restrict__ scales, uint8_t* __restrict__ packed) {
   const int64_t B = (K + 1) >> 1;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N * B) return;
-  const int64_t n = t / B, j = t - n * B;
-  const int64_t k = 2 * j;
-  const float sf0 = half_bits_to_float(scales[n * G + k / group]);
-  uint32_t byte = code_of(w[n * K + k], sf0, scale_rcp(sf0));
-  if (k + 1 < K) {
-    const float sf1 = half_bits_to_float(scales[n * G + (k + 1) / group]);
-    byte |= code_of(w[n * K + k + 1], sf1, scale_rcp(sf1)) << 4;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < N * B;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = t / B, j = t - n * B;
+    const int64_t k = 2 * j;
+    const float sf0 = half_bits_to_float(scales[n * G + k / group]);
+    uint32_t byte = code_of(w[n * K + k], sf0, scale_rcp(sf0));
+    if (k + 1 < K) {
+      const float sf1 = half_bits_to_float(scales[n * G + (k + 1) / group]);
+      byte |= code_of(w[n * K + k + 1], sf1, scale_rcp(sf1)) << 4;
+    }
+    packed[t] = (uint8_t)byte;
   }
-  packed[t] = (uint8_t)byte;
 }
 
 // ---------------------------------------------------------------------------
@@ -288,19 +290,20 @@ __global__ __launch_bounds__(256) void quantize_affine_vec_kernel(
 __global__ __launch_bounds__(256) void quantize_affine_params_kernel(
     const float* __restrict__ w, int64_t N, int64_t K, int64_t group, int64_t G,
     uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N * G) return;
-  const int64_t n = t / G, gi = t - n * G;
-  const int64_t k0 = gi * group;
-  const int64_t k1 = k0 + group < K ? k0 + group : K;
-  float lo = 0.0f, hi = 0.0f;
-  for (int64_t k = k0; k < k1; ++k) {
-    lo = __builtin_fminf(lo, w[n * K + k]);
-    hi = __builtin_fmaxf(hi, w[n * K + k]);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < N * G;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = t / G, gi = t - n * G;
+    const int64_t k0 = gi * group;
+    const int64_t k1 = k0 + group < K ? k0 + group : K;
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t k = k0; k < k1; ++k) {
+      lo = __builtin_fminf(lo, w[n * K + k]);
+      hi = __builtin_fmaxf(hi, w[n * K + k]);
+    }
+    const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
+    scales[t] = __builtin_bit_cast(uint16_t, s16);
+    zeros[t] = (uint8_t)affine_zp(lo, (float)s16);
   }
-  const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
-  scales[t] = __builtin_bit_cast(uint16_t, s16);
-  zeros[t] = (uint8_t)affine_zp(lo, (float)s16);
 }
 
 __global__ __launch_bounds__(256) void quantize_affine_pack_kernel(
@@ -308,19 +311,20 @@ __global__ __launch_bounds__(256) void quantize_affine_pack_kernel(
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
     uint8_t* __restrict__ packed) {
   const int64_t B = (K + 1) >> 1;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N * B) return;
-  const int64_t n = t / B, j = t - n * B;
-  const int64_t k = 2 * j;
-  const int64_t g0 = n * G + k / group;
-  const float sf0 = half_bits_to_float(scales[g0]);
-  uint32_t byte = affine_code(w[n * K + k], sf0, scale_rcp(sf0), zeros[g0]);
-  if (k + 1 < K) {
-    const int64_t g1 = n * G + (k + 1) / group;
-    const float sf1 = half_bits_to_float(scales[g1]);
-    byte |= affine_code(w[n * K + k + 1], sf1, scale_rcp(sf1), zeros[g1]) << 4;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < N * B;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = t / B, j = t - n * B;
+    const int64_t k = 2 * j;
+    const int64_t g0 = n * G + k / group;
+    const float sf0 = half_bits_to_float(scales[g0]);
+    uint32_t byte = affine_code(w[n * K + k], sf0, scale_rcp(sf0), zeros[g0]);
+    if (k + 1 < K) {
+      const int64_t g1 = n * G + (k + 1) / group;
+      const float sf1 = half_bits_to_float(scales[g1]);
+      byte |= affine_code(w[n * K + k + 1], sf1, scale_rcp(sf1), zeros[g1]) << 4;
+    }
+    packed[t] = (uint8_t)byte;
   }
-  packed[t] = (uint8_t)byte;
 }
 
 bool quantize_vec_supported(const float* w, int64_t K, int64_t group, const uint8_t* packed,
@@ -350,11 +354,11 @@ hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, 
     return hipGetLastError();
   }
   const int64_t B = (K + 1) / 2;
-  hipLaunchKernelGGL(quantize_scales_kernel, dim3((unsigned)((N * G + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(quantize_scales_kernel, dim3(stride_grid((N * G + 255) / 256)), dim3(256), 0,
                      stream, w, N, K, group, G, scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quantize_pack_kernel, dim3((unsigned)((N * B + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(quantize_pack_kernel, dim3(stride_grid((N * B + 255) / 256)), dim3(256), 0,
                      stream, w, N, K, group, G, scales, packed);
   return hipGetLastError();
 }
@@ -380,11 +384,11 @@ hipError_t launch_quantize_affine(const float* w, int64_t N, int64_t K, int64_t 
     return hipGetLastError();
   }
   const int64_t B = (K + 1) / 2;
-  hipLaunchKernelGGL(quantize_affine_params_kernel, dim3((unsigned)((N * G + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL(quantize_affine_params_kernel, dim3(stride_grid((N * G + 255) / 256)), dim3(256),
                      0, stream, w, N, K, group, G, scales, zeros);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quantize_affine_pack_kernel, dim3((unsigned)((N * B + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL(quantize_affine_pack_kernel, dim3(stride_grid((N * B + 255) / 256)), dim3(256),
                      0, stream, w, N, K, group, G, scales, zeros, packed);
   return hipGetLastError();
 }

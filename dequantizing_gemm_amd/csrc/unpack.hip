@@ -37,25 +37,26 @@ __device__ __forceinline__ u32x2_t unpack_word(uint32_t w) {
 __global__ __launch_bounds__(256) void unpack_flat_kernel(const uint8_t* __restrict__ packed,
                                                           int64_t nbytes, int8_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 1024;
-  if (base >= nbytes) return;
-  if (base + 1024 <= nbytes) {
+  for (int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 1024; base < nbytes;
+       base += (int64_t)gridDim.x * 4 * 1024) {
+    if (base + 1024 <= nbytes) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t b0 = base + 512 * h + 8 * lane;
-      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(packed + b0));
-      const u32x2_t a = unpack_word(v.x), b = unpack_word(v.y);
-      u32x4_t o;
-      o.x = a.x; o.y = a.y; o.z = b.x; o.w = b.y;
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + 2 * b0));
-    }
-  } else {
-    for (int h = 0; h < 2; ++h)
-      for (int64_t b = base + 512 * h + 8 * lane; b < base + 512 * h + 8 * lane + 8 && b < nbytes; ++b) {
-        const uint32_t v = packed[b];
-        out[2 * b] = (int8_t)sx4(v & 0xFu);
-        out[2 * b + 1] = (int8_t)sx4(v >> 4);
+      for (int h = 0; h < 2; ++h) {
+        const int64_t b0 = base + 512 * h + 8 * lane;
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(packed + b0));
+        const u32x2_t a = unpack_word(v.x), b = unpack_word(v.y);
+        u32x4_t o;
+        o.x = a.x; o.y = a.y; o.z = b.x; o.w = b.y;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + 2 * b0));
       }
+    } else {
+      for (int h = 0; h < 2; ++h)
+        for (int64_t b = base + 512 * h + 8 * lane; b < base + 512 * h + 8 * lane + 8 && b < nbytes; ++b) {
+          const uint32_t v = packed[b];
+          out[2 * b] = (int8_t)sx4(v & 0xFu);
+          out[2 * b + 1] = (int8_t)sx4(v >> 4);
+        }
+    }
   }
 }
 
@@ -63,12 +64,13 @@ __global__ __launch_bounds__(256) void unpack_rows_kernel(const uint8_t* __restr
                                                           int64_t N, int64_t K,
                                                           int8_t* __restrict__ out) {
   const int64_t B = (K + 1) >> 1;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N * B) return;
-  const int64_t n = t / B, j = t - n * B;
-  const uint32_t v = packed[t];
-  out[n * K + 2 * j] = (int8_t)sx4(v & 0xFu);
-  if (2 * j + 1 < K) out[n * K + 2 * j + 1] = (int8_t)sx4(v >> 4);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < N * B;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = t / B, j = t - n * B;
+    const uint32_t v = packed[t];
+    out[n * K + 2 * j] = (int8_t)sx4(v & 0xFu);
+    if (2 * j + 1 < K) out[n * K + 2 * j + 1] = (int8_t)sx4(v >> 4);
+  }
 }
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* out,
@@ -76,11 +78,11 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* ou
   if (K % 2 == 0 && ((uintptr_t)packed % 16) == 0 && ((uintptr_t)out % 16) == 0) {
     const int64_t nbytes = N * (K / 2);
     const int64_t kb = (nbytes + 1023) / 1024;                 // one wavefront per KB
-    hipLaunchKernelGGL(unpack_flat_kernel, dim3((unsigned)((kb + 3) / 4)), dim3(256), 0,
+    hipLaunchKernelGGL(unpack_flat_kernel, dim3(stride_grid((kb + 3) / 4)), dim3(256), 0,
                        stream, packed, nbytes, out);
   } else {
     const int64_t total = N * ((K + 1) / 2);
-    hipLaunchKernelGGL(unpack_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(unpack_rows_kernel, dim3(stride_grid((total + 255) / 256)), dim3(256), 0,
                        stream, packed, N, K, out);
   }
   return hipGetLastError();

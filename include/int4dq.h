@@ -67,10 +67,11 @@ extern "C" {
 /* Kernel selection for int4_matmul_path (int4_matmul always uses AUTO). */
 #define INT4DQ_PATH_AUTO    0  /* choose by M, dtype and alignment */
 #define INT4DQ_PATH_GENERIC 1  /* VALU kernel, any shape, any group, fp32 or fp16 x */
-#define INT4DQ_PATH_SKINNY  2  /* M <= 64, fp16 x: weight-streaming MFMA kernel */
-#define INT4DQ_PATH_TILED   3  /* any M, fp16 x: LDS-tiled MFMA kernel */
-#define INT4DQ_PATH_GEMV    4  /* fp16 x, group and K multiples of 32, M = 1; or M <= 4 with K <= 12288
-                                   and group = 32 * 2^p: weight-streaming kernels */
+#define INT4DQ_PATH_SKINNY  2  /* M <= 64, fp16 x, N < 2^25: weight-streaming MFMA kernel */
+#define INT4DQ_PATH_TILED   3  /* any M, fp16 x, M and N < 2^31 and fewer than 2^24 output
+                                   tiles (128 x 256 for large M): LDS-tiled MFMA kernel */
+#define INT4DQ_PATH_GEMV    4  /* fp16 x, N < 2^25, group and K multiples of 32, M = 1; or M <= 4
+                                   with K <= 12288 and group = 32 * 2^p: weight-streaming kernels */
 
 /*
  * Number of scale groups per row, G = ceil(K / group) (drill page,
@@ -147,7 +148,9 @@ int int4_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, in
  *   2e-3 * sum_k |x[m,k] * q[n,k] * scale| of the exactly rounded result.
  *   A group whose scale is zero (+0 or -0) contributes nothing, whatever its
  *   codes. M = 0 is a valid no-op. The pad nibble of an odd K is never used
- *   and x[:, K] is never read.
+ *   and x[:, K] is never read. Every shape that passes the checks below is
+ *   computed: where the fast kernels' limits (INT4DQ_PATH_*) exclude it, the
+ *   generic kernel takes it.
  *   Errors: EINVAL if M < 0, N, K or group < 1, a pointer is NULL (when M > 0),
  *   x_dtype is unknown, or sizes overflow.
  */

@@ -59,7 +59,7 @@ hipError_t launch_matmul_gemv(const void*, int64_t M, const uint8_t*, const uint
   stub_last_M = M;
   return hipSuccess;
 }
-const char* matmul_tiled_unsupported(int, const void*, const uint8_t*, int64_t, int64_t) {
+const char* matmul_tiled_unsupported(int, int64_t, const void*, const uint8_t*, int64_t, int64_t, int64_t) {
   return stub_tiled_ok ? nullptr : "tiled stub refuses";
 }
 hipError_t launch_matmul_tiled(const void*, int64_t M, const uint8_t*, const uint16_t*, const uint8_t*, int64_t,

@@ -210,6 +210,30 @@ def test_kernel_selection_rules():
     assert sel(1, 512, 4096, 256) == P["tiled"]
 
 
+def test_kernel_selection_keeps_grids_launchable():
+    """A dispatch holds fewer than 2^32 work items per grid dimension. The
+    weight-streaming kernels launch up to 128 threads per weight row and the
+    tiled kernel 256 per output tile, so the automatic choice passes shapes
+    beyond their limits on to a kernel whose grid fits (the generic kernel
+    strides over any number of outputs); a forced kernel refuses them."""
+    dq = _lib()
+    sel = lambda M, N, K=64, g=32: dq.lib.int4_matmul_select(
+        ctypes.c_void_p(0x1000), 1, M, ctypes.c_void_p(0x2000), FAKE, N, K, g, FAKE)
+    P = dq.PATHS
+    assert sel(1, (1 << 25) - 1) == P["gemv"] and sel(4, (1 << 25) - 1) == P["gemv"]
+    assert sel(8, (1 << 25) - 1) == P["skinny"]
+    # 2^25 weight rows: one 32 x 128 tile per 128 rows, 2^18 tiles
+    assert sel(1, 1 << 25) == P["tiled"] and sel(8, 1 << 25) == P["tiled"]
+    # 2048 x 2^28 outputs are 2^24 tiles of 128 x 256: one block too many for the tiled grid
+    assert sel(2048, (1 << 28) - 256) == P["tiled"] and sel(2048, 1 << 28) == P["generic"]
+    assert sel(1, 1 << 31) == P["generic"] and sel(1 << 31, 1) == P["generic"]
+    y = ctypes.c_void_p(0x3000)
+    for path, M, N in (("gemv", 1, 1 << 25), ("skinny", 8, 1 << 25), ("tiled", 2048, 1 << 28)):
+        rc = dq.lib.int4_matmul_path(ctypes.c_void_p(0x1000), 1, M, ctypes.c_void_p(0x2000), FAKE, N, 64, 32,
+                                     None, 0, y, P[path], None)
+        assert rc == dq.EUNSUPPORTED and b"2^" in dq.lib.int4_last_error(), path
+
+
 def test_binding_rejects_host_tensors():
     dq = _lib()
     with pytest.raises(ValueError, match="GPU"):
