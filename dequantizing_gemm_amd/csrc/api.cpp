@@ -16,8 +16,9 @@
 // Scratch of int4_linear_noalloc: the workspace of a split of K for callers
 // that cannot allocate. Every GPU the library runs on holds its own copy, from
 // module load to the end of the process. The split plans need at most
-// 16 MiB (four shares of a [512, 2048] binary32 result, or eight of a quarter
-// of that), so the array is that size. In host code its name is only a
+// 16 MiB (the tiled kernel's: four shares of a [512, 2048] binary32 result,
+// or eight of a quarter of that; the skinny kernel's: at most eight shares of
+// a [64, 2032] result, 4 MiB), so the array is that size. In host code its name is only a
 // stand-in: the device address comes from hipGetSymbolAddress.
 static __device__ __align__(256) uint8_t scratch[16 << 20];
 
@@ -193,10 +194,12 @@ int int4_linear(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
 int64_t int4_linear_workspace_bytes(int x_dtype, int64_t M, int64_t N, int64_t K, int64_t group) {
   if (M < 0 || N < 1 || K < 1 || group < 1 || (x_dtype != INT4DQ_X_F32 && x_dtype != INT4DQ_X_F16)) return -1;
   if (M == 0) return 0;
-  // The kernel choice of an aligned call (the split applies to the tiled kernel only).
+  // The kernel choice of an aligned call (the skinny and tiled kernels split K).
   static const uint8_t aligned_probe[16] __attribute__((aligned(16))) = {0};
-  if (choose_path(aligned_probe, x_dtype, M, aligned_probe, N, K, group) != INT4DQ_PATH_TILED) return 0;
-  return int4dq::matmul_tiled_workspace(M, N, K, group);
+  const int path = choose_path(aligned_probe, x_dtype, M, aligned_probe, N, K, group);
+  if (path == INT4DQ_PATH_SKINNY) return int4dq::matmul_skinny_workspace(M, N, K, group);
+  if (path == INT4DQ_PATH_TILED) return int4dq::matmul_tiled_workspace(M, N, K, group);
+  return 0;
 }
 
 int int4_linear_ws(const void* x, int x_dtype, int64_t M, const uint8_t* packed,
@@ -288,7 +291,8 @@ int matmul_impl(const char* fn, const void* x, int x_dtype, int64_t M, const uin
     case INT4DQ_PATH_SKINNY: {
       const char* why = int4dq::matmul_skinny_unsupported(x_dtype, M, x, packed, N, K, group);
       if (why) return fail(INT4DQ_EUNSUPPORTED, "%s: %s", fn, why);
-      return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, zeros, N, K, group, y, ep, s),
+      return hip_status(int4dq::launch_matmul_skinny(x, M, packed, scales, zeros, N, K, group, y, ep,
+                                                     workspace, workspace_bytes, s),
                         "int4_matmul skinny launch");
     }
     case INT4DQ_PATH_GEMV: {

@@ -43,6 +43,21 @@ struct TiledSplit {
   int steps;
 };
 
+// Split of K for the skinny kernel: S shares of kb_per_share K-blocks each
+// (blockIdx.y is the share), whose partial tiles go to part ([S, M, N]
+// binary32). S = 1: no split, part unused.
+struct SkinnySplit {
+  float* part;
+  int S;
+  int kb_per_share;
+};
+
+// y[m, n] = act(sum over shares q = 0 .. S-1, in that order, of
+// part[q, m, n] + bias[n]) in y's precision: the second step of every split
+// of K.
+hipError_t launch_split_reduce(const float* part, int S, int64_t M, int64_t N, void* y, Epilogue ep,
+                               hipStream_t stream);
+
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, int64_t group, uint8_t* packed,
                            uint16_t* scales, hipStream_t stream);
 
@@ -69,9 +84,14 @@ const char* matmul_skinny_unsupported(int x_dtype, int64_t M, const void* x,
                                       const uint8_t* packed, int64_t N, int64_t K, int64_t group);
 // Whether the automatic choice takes the skinny kernel for a supported shape.
 bool matmul_skinny_preferred(int64_t M, int64_t N);
+// workspace: nullptr, or workspace_bytes of device memory for a split of K
+// (any contents), taken only when it holds matmul_skinny_workspace(M, N, K,
+// group) bytes; that is 0 when the shape is not split.
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int64_t group,
-                                void* y, Epilogue ep, hipStream_t stream);
+                                void* y, Epilogue ep, void* workspace, int64_t workspace_bytes,
+                                hipStream_t stream);
+int64_t matmul_skinny_workspace(int64_t M, int64_t N, int64_t K, int64_t group);
 
 const char* matmul_gemv_unsupported(int x_dtype, int64_t M, const void* x,
                                     const uint8_t* packed, int64_t N, int64_t K, int64_t group);

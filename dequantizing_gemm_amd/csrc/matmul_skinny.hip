@@ -78,11 +78,14 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 // activation traffic per weight byte by RG (x is re-read by every block).
 // MT > 1 (MR == 0 only): M up to 16 MT rows of x as MT tiles of 16; each
 // expanded code word feeds MT MFMAs, one per tile.
+// sp.S > 1: the block takes share blockIdx.y of K (K-blocks kb0 .. kb0 +
+// sp.kb_per_share - 1, kb0 = blockIdx.y * sp.kb_per_share, a multiple of group / KB) and writes
+// its partial [M, 16 RG] tile to sp.part instead of y.
 template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
-    int kb_shift, void* __restrict__ y, Epilogue ep) {
+    int kb_shift, void* __restrict__ y, Epilogue ep, SkinnySplit sp) {
   typedef typename WLoad<KB>::T wvec_t;
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
   constexpr int XB = (RG > 1 || MT > 1) ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
@@ -94,17 +97,20 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * 16 * RG;
+  const int q = blockIdx.y;                    // share of K (0 without a split)
+  const int kb0 = q * sp.kb_per_share;                  // its first K-block
+  const int nkb = sp.S > 1 ? min(sp.kb_per_share, K / KB - kb0) : K / KB;   // K-blocks of the share
+  x += (int64_t)kb0 * KB;                      // every x address below is x + m K + j KB + ...
   const uint8_t* prow[RG];
   const uint16_t* srow[RG];
   const uint8_t* zrow[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     const int nrow = (n0 + 16 * r + col < N) ? n0 + 16 * r + col : N - 1;   // tail rows: read, discard
-    prow[r] = packed + (int64_t)nrow * (K >> 1) + h * (KB / 8);
-    srow[r] = scales + (int64_t)nrow * G;
-    zrow[r] = AFF ? zeros + (int64_t)nrow * G : nullptr;
+    prow[r] = packed + (int64_t)nrow * (K >> 1) + (int64_t)kb0 * (KB / 2) + h * (KB / 8);
+    srow[r] = scales + (int64_t)nrow * G + (kb0 >> kb_shift);
+    zrow[r] = AFF ? zeros + (int64_t)nrow * G + (kb0 >> kb_shift) : nullptr;
   }
-  const int nkb = K / KB;
 
   // Weight and scale loads of the wave's share, K-block by K-block. They are
   // issued after the (smaller) x staging loads, so that each K-block's
@@ -268,7 +274,10 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) s += red[((w * RG + r) * MT + tm) * 256 + src];
     const int n = n0 + 16 * r + nn;
-    if (n < N) ep.store(y, (int64_t)m * N + n, s, n);
+    if (n < N) {
+      if (sp.S > 1) sp.part[((int64_t)q * M + m) * N + n] = s;
+      else ep.store(y, (int64_t)m * N + n, s, n);
+    }
   }
 }
 
@@ -582,12 +591,12 @@ constexpr size_t kSkinnyLdsMax = 64 * 1024;
 
 template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1>
 static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
+                      const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                       hipStream_t stream) {
   hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG, AFF, MT>),
-                     dim3((unsigned)((N + 16 * RG - 1) / (16 * RG))), dim3(WAVES * 64),
+                     dim3((unsigned)((N + 16 * RG - 1) / (16 * RG)), (unsigned)sp.S), dim3(WAVES * 64),
                      skinny_lds(WAVES, U, KB, MR, RG, MT), stream, x, M, packed, scales, zeros, N, K, G,
-                     kbs, y, ep);
+                     kbs, y, ep, sp);
 }
 
 // 17 <= M <= 64: MT = 2 or 4 row tiles, direct x loads. Every block re-reads
@@ -596,30 +605,30 @@ static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uin
 // about one block per CU.
 template <int KB, int WAVES, int U, bool AFF, int MT>
 static void launch_tiles(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                         const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
+                         const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                          hipStream_t stream) {
   constexpr bool rg2 = WAVES <= 8;
   if constexpr (rg2) {
     if (N >= 256 * 16 * 2) {
-      launch_mr<KB, WAVES, U, 0, 2, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+      launch_mr<KB, WAVES, U, 0, 2, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
-  launch_mr<KB, WAVES, U, 0, 1, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+  launch_mr<KB, WAVES, U, 0, 1, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
 }
 
 template <int KB, int WAVES, int U, bool AFF>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                       const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
+                       const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                        hipStream_t stream) {
   if constexpr (WAVES < 16 || U <= 6) {           // refused by matmul_skinny_unsupported otherwise
     if (M > 32) {
-      launch_tiles<KB, WAVES, U, AFF, 4>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+      launch_tiles<KB, WAVES, U, AFF, 4>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
   if (M > 16) {
-    launch_tiles<KB, WAVES, U, AFF, 2>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+    launch_tiles<KB, WAVES, U, AFF, 2>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
     return;
   }
   const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
@@ -630,64 +639,124 @@ static void launch_one(const _Float16* x, int M, const uint8_t* packed, const ui
   constexpr bool rg4 = WAVES <= 8, rg2 = WAVES <= 8 || U <= 6;
   if constexpr (rg4) {
     if (M > 4 && N >= 256 * 16 * 4) {
-      launch_mr<KB, WAVES, U, 0, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+      launch_mr<KB, WAVES, U, 0, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
   if constexpr (rg2) {
     if (M > 4 && N >= 256 * 16 * 2) {
-      launch_mr<KB, WAVES, U, 0, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+      launch_mr<KB, WAVES, U, 0, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
   if (M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax)
-    launch_mr<KB, WAVES, U, 0, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 0, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (MR == 1)
-    launch_mr<KB, WAVES, U, 1, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 1, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (MR == 2)
-    launch_mr<KB, WAVES, U, 2, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 2, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else
-    launch_mr<KB, WAVES, U, 4, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+    launch_mr<KB, WAVES, U, 4, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
 }
 
 // Waves per block and K-blocks per wave for nkb K-blocks: the fewest waves
 // (<= 16) that cover K with at most 4 K-blocks each, else 16 waves with up to 8.
 template <int KB, bool AFF>
 static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
-                      const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep,
+                      const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                       hipStream_t stream) {
-  const int nkb = K / KB;
-  if (nkb <= 4 * 2) launch_one<KB, 4, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 4 * 4) launch_one<KB, 4, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 8 * 4) launch_one<KB, 8, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
-  else if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
-  else launch_one<KB, 16, 8, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream);
+  const int nkb = sp.S > 1 ? sp.kb_per_share : K / KB;   // K-blocks of one block (of its share)
+  if (nkb <= 4 * 2) launch_one<KB, 4, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 4 * 4) launch_one<KB, 4, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 8 * 4) launch_one<KB, 8, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else launch_one<KB, 16, 8, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
 }
 
 template <bool AFF>
 static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
                             const uint16_t* scales, const uint8_t* zeros, int N, int K, int G,
-                            int KB, int kbs, void* y, Epilogue ep, hipStream_t stream) {
+                            int KB, int kbs, void* y, Epilogue ep, const SkinnySplit& sp, hipStream_t stream) {
   switch (KB) {
-    case 128: launch_kb<128, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
-    case 64: launch_kb<64, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
-    default: launch_kb<32, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, stream); break;
+    case 128: launch_kb<128, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
+    case 64: launch_kb<64, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
+    default: launch_kb<32, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
   }
+}
+
+// Split of K (only with a workspace), for 17 to 64 rows of x and for long
+// rows: with fewer than 128 groups of 16 weight rows the grid leaves at least
+// half the CUs idle, and each block walks all of K for its rows alone. K is
+// then cut into S = 2, 4 or 8 shares (the most that keep the grid within two
+// blocks per CU), each at least 6 K-blocks and a whole number of groups; the
+// shares' partial tiles meet in the workspace and a second kernel adds them
+// in share order, as for the tiled kernel. That second kernel and the
+// boundary between the two cost about 4 us, so the split is taken only where
+// a block's work is long enough to lose more than that: at least 96 K-blocks
+// times 16-row tiles of x per row group, and not where the pipelined form
+// runs (5 to 16 rows, groups of 128 2^p). Measured (graph replays over a
+// >= 1 GiB pool, unsplit against split): [1024, 8192] M = 64 36.4 -> 17.1 us,
+// [768, 3072] group 64 M = 32 11.6 -> 9.6 us, group 32 M = 16 10.6 -> 9.6 us;
+// shorter work lost: group 64 M = 16 8.7 -> 8.8 us, M = 8 7.7 -> 8.4 us,
+// [768, 768] M = 16 3.9 -> 6.1 us, the pipelined form's [768, 3072] M = 16
+// 5.4 -> 7.1 us and [1024, 8192] M = 8 6.8 -> 9.4 us.
+struct SkinnyPlan {
+  int S, kb_per_share;
+  int64_t ws_bytes;
+};
+static bool skinny_pipe_takes(int64_t M, int KB, int64_t K) {
+  return M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 && M * K * 2 < ((int64_t)1 << 31);
+}
+static SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group) {
+  SkinnyPlan pl{1, 0, 0};
+  const int KB = skinny_kb(group);
+  if (KB == 0 || M <= 4 || K % KB != 0 || skinny_pipe_takes(M, KB, K)) return pl;
+  const int64_t per_group = group / KB;        // K-blocks per group (a power of two)
+  const int64_t nkb = K / KB, rgroups = (N + 15) / 16, tiles = (M + 15) / 16;
+  if (rgroups >= 128 || nkb * tiles < 96) return pl;
+  for (int S = 8; S >= 2; S /= 2) {
+    if (rgroups * S > 512) continue;
+    int64_t kbps = (nkb + S - 1) / S;
+    kbps = (kbps + per_group - 1) / per_group * per_group;
+    const int64_t shares = (nkb + kbps - 1) / kbps;
+    if (kbps < 6 || shares < 2) continue;
+    pl.S = (int)shares;
+    pl.kb_per_share = (int)kbps;
+    break;
+  }
+  if (pl.S > 1) pl.ws_bytes = (int64_t)pl.S * M * N * 4;
+  return pl;
+}
+
+int64_t matmul_skinny_workspace(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (M < 1 || M > 64 || N >= (1ll << 25)) return 0;
+  return skinny_plan(M, N, K, group).ws_bytes;
 }
 
 hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
                                 const uint16_t* scales, const uint8_t* zeros, int64_t N,
-                                int64_t K, int64_t group, void* y, Epilogue ep,
-                                hipStream_t stream) {
+                                int64_t K, int64_t group, void* y, Epilogue ep, void* workspace,
+                                int64_t workspace_bytes, hipStream_t stream) {
   const int KB = skinny_kb(group);
   const int G = (int)((K + group - 1) / group);
   if (M > 32 && K / KB > 16 * 6) return hipErrorInvalidValue;   // refused by matmul_skinny_unsupported
   int kbs = 0;
   while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);
-  if (M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 &&
-      M * K * 2 < ((int64_t)1 << 31)) {
+  const SkinnyPlan pl = skinny_plan(M, N, K, group);
+  SkinnySplit sp{nullptr, 1, 0};
+  if (pl.S > 1 && workspace && workspace_bytes >= pl.ws_bytes) {
+    sp = SkinnySplit{static_cast<float*>(workspace), pl.S, pl.kb_per_share};
+    if (zeros)
+      launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
+    else
+      launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_split_reduce(sp.part, sp.S, M, N, y, ep, stream);
+  }
+  if (skinny_pipe_takes(M, KB, K)) {
     // the pipelined form: 4 row groups per block on wide matrices (x is
     // re-read once per 64 weight rows); below 1024 row groups, the count of
     // 1, 2 or 3 that gives the busiest CU the fewest rows (blocks spread
@@ -734,9 +803,9 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
     }
   }
   if (zeros)
-    launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, stream);
+    launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
   else
-    launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, stream);
+    launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
   return hipGetLastError();
 }
 

@@ -748,13 +748,17 @@ hipError_t launch_matmul_tiled(const void* x, int64_t M, const uint8_t* packed,
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const _Float16*>(x), (int)M, packed, scales, zeros, (int)N, (int)K, G,
                      gs, y, ep, sp);
-  if (sp.S > 1) {
-    const int64_t MN = M * N;
-    const int64_t rblocks = (MN + 1023) / 1024;
-    if (rblocks >= (1ll << 31)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, stream, sp.part, sp.S,
-                       MN, (int)N, y, ep);
-  }
+  if (sp.S > 1) return launch_split_reduce(sp.part, sp.S, M, N, y, ep, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const float* part, int S, int64_t M, int64_t N, void* y, Epilogue ep,
+                               hipStream_t stream) {
+  const int64_t MN = M * N;
+  const int64_t rblocks = (MN + 1023) / 1024;
+  if (rblocks >= (1ll << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, stream, part, S, MN,
+                     (int)N, y, ep);
   return hipGetLastError();
 }
 

@@ -257,13 +257,16 @@ int int4_linear(const void *x, int x_dtype, int64_t M, const uint8_t *packed,
                 int64_t group, const float *bias, int act, void *y, int y_dtype, void *stream);
 
 /*
- * int4_linear with a caller-owned device workspace, which lets the kernel for
- * many rows of x cut K into shares when its grid of output tiles is too small
- * to fill the GPU (a few hundred rows against a few thousand weight rows):
- * each share's partial tile goes to the workspace and a second kernel adds
- * the partials in share order and applies bias, activation and the output
- * precision, so results do not depend on timing and stay within the
- * tolerance of int4_matmul. Engine page ("Build a Blockwise INT4 Inference
+ * int4_linear with a caller-owned device workspace, which lets a kernel cut K
+ * into shares when its grid is too small to fill the GPU: the kernel for many
+ * rows of x when its output tiles are few (a few hundred rows against a few
+ * thousand weight rows), and the kernel for 5 to 64 rows when the weight
+ * matrix has fewer than 2048 rows and long rows (a small transformer's MLP
+ * down projection at 16 or more rows, 64 rows against 1024 weight rows of
+ * 8192 codes). Each share's partial tile goes to the workspace and a second
+ * kernel adds the partials in share order and applies bias, activation and
+ * the output precision, so results do not depend on timing and stay within
+ * the tolerance of int4_matmul. Engine page ("Build a Blockwise INT4 Inference
  * Engine"), layer forward, as int4_linear.
  *   workspace       : device memory, 256-byte aligned, any contents, or NULL
  *                     with workspace_bytes = 0.

@@ -21,7 +21,7 @@ extern int stub_calls[8];
 extern int64_t stub_last_M, stub_last_ws_bytes;
 extern void* stub_last_ws;
 extern bool stub_gemv_ok, stub_skinny_ok, stub_skinny_pref, stub_tiled_ok;
-extern int64_t stub_tiled_ws;
+extern int64_t stub_tiled_ws, stub_skinny_ws;
 
 static int failures = 0;
 #define CHECK(cond, what)                                                          \
@@ -169,6 +169,16 @@ int main() {
             stub_last_ws == nullptr && stub_last_ws_bytes == 0,
         "noalloc without a split");
   stub_gemv_ok = stub_skinny_ok = true;
+  // the skinny kernel's split takes the workspace the same way
+  stub_gemv_ok = false;
+  stub_skinny_ws = 777;
+  CHECK(int4_linear_workspace_bytes(INT4DQ_X_F16, 16, 768, 3072, 32) == 777, "workspace_bytes skinny");
+  CHECK(int4_linear_ws(P, INT4DQ_X_F16, 16, packed, scales, nullptr, 768, 3072, 32, nullptr, 0, y, 0, arena,
+                       1024, nullptr) == INT4DQ_OK &&
+            stub_last_ws == arena && stub_last_ws_bytes == 1024,
+        "workspace passed to the skinny launcher");
+  stub_skinny_ws = 0;
+  stub_gemv_ok = true;
 
   // the error text belongs to the thread that made the call
   std::string t1, t2;

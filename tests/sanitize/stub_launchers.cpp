@@ -13,6 +13,7 @@ int64_t stub_last_M = -1, stub_last_ws_bytes = -1;
 void* stub_last_ws = nullptr;
 bool stub_gemv_ok = true, stub_skinny_ok = true, stub_skinny_pref = true, stub_tiled_ok = true;
 int64_t stub_tiled_ws = 0;         // what matmul_tiled_workspace answers
+int64_t stub_skinny_ws = 0;        // what matmul_skinny_workspace answers
 
 namespace int4dq {
 
@@ -45,11 +46,15 @@ const char* matmul_skinny_unsupported(int, int64_t, const void*, const uint8_t*,
 }
 bool matmul_skinny_preferred(int64_t, int64_t) { return stub_skinny_pref; }
 hipError_t launch_matmul_skinny(const void*, int64_t M, const uint8_t*, const uint16_t*, const uint8_t*, int64_t,
-                                int64_t, int64_t, void*, Epilogue, hipStream_t) {
+                                int64_t, int64_t, void*, Epilogue, void* workspace, int64_t workspace_bytes,
+                                hipStream_t) {
   ++stub_calls[5];
   stub_last_M = M;
+  stub_last_ws = workspace;
+  stub_last_ws_bytes = workspace_bytes;
   return hipSuccess;
 }
+int64_t matmul_skinny_workspace(int64_t, int64_t, int64_t, int64_t) { return stub_skinny_ws; }
 const char* matmul_gemv_unsupported(int, int64_t, const void*, const uint8_t*, int64_t, int64_t, int64_t) {
   return stub_gemv_ok ? nullptr : "gemv stub refuses";
 }

@@ -142,3 +142,64 @@ def test_small_workspace_runs_unsplit(dq):
     b = host(dq.int4_linear(x, pd, sd, K, g))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert not host(small).any()
+
+
+# The skinny kernel's split of K (fewer than 128 groups of 16 weight rows, at
+# least 96 K-blocks times 16-row tiles of x per row group): (M, N, K, group).
+# Group 32 at M = 16 (8 shares), 32 and 40 rows (two and four row tiles),
+# [1024, 8192] at M = 64, five rows against 100 weight rows, ragged M and N
+# with a last share shorter than the others (K = 4224: 66 K-blocks in shares
+# of 17), group 256 (two K-blocks per group), 33 rows of group 128.
+SKINNY_SPLIT_CASES = [(16, 768, 3072, 32), (32, 768, 3072, 64), (40, 768, 3072, 64), (64, 1024, 8192, 128),
+                      (5, 100, 4096, 32), (20, 1030, 4224, 64), (24, 2000, 8192, 256), (33, 1000, 4096, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", SKINNY_SPLIT_CASES,
+                         ids=[f"M{m}-N{n}-K{k}-g{g}" for m, n, k, g in SKINNY_SPLIT_CASES])
+def test_skinny_split_matches_oracle(dq, M, N, K, g):
+    nbytes = dq.linear_workspace_bytes(M, N, K, g)
+    assert nbytes > 0, "this shape is meant to split K"
+    w = np.random.default_rng(N + K + g).normal(0, 0.02, size=(N, K)).astype(np.float32)
+    x = np.random.default_rng(M + 1).normal(size=(M, K)).astype(np.float16)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    pd, sd, xd = dev(pr), dev(sr), dev(x)
+    assert dq.matmul_select(xd, pd, sd, K, g) == "skinny"
+    ws = dq.linear_workspace(M, N, K, g, device=DEV)
+    say(f"case: skinny split M={M} N={N} K={K} g={g} workspace={nbytes} B")
+    y1 = host(dq.int4_linear(xd, pd, sd, K, g, workspace=ws))
+    ws.fill_(0xA5)
+    y2 = host(dq.int4_linear(xd, pd, sd, K, g, workspace=ws))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "two calls differ"
+    check(y1, x, pr, sr, K, g, what=f"skinny split M={M} N={N} K={K} g={g}")
+    y0 = host(dq.int4_linear(xd, pd, sd, K, g))
+    check(y0, x, pr, sr, K, g, what="no split")
+
+
+def test_skinny_split_epilogue_affine_edge(dq):
+    """Bias, ReLU and fp16 output after the share-order reduction; affine
+    codes; the edge rows (zero groups, -8 codes, subnormal and 65504 scales)."""
+    M, N, K, g = 32, 768, 3072, 64
+    w = np.random.default_rng(21).normal(0, 0.02, size=(N, K)).astype(np.float32)
+    x = np.random.default_rng(22).normal(size=(M, K)).astype(np.float16)
+    b = np.random.default_rng(23).normal(0, 0.5, N).astype(np.float32)
+    pr, sr, _ = oracle.quantize_int4(w, g)
+    pd, sd, xd, bd = dev(pr), dev(sr), dev(x), dev(b)
+    ws = dq.linear_workspace(M, N, K, g, device=DEV)
+    assert ws.numel() > 0
+    for relu in (False, True):
+        for half in (False, True):
+            say(f"case: skinny split epilogue relu={relu} fp16 output={half}")
+            y = host(dq.int4_linear(xd, pd, sd, K, g, bias=bd, relu=relu,
+                                    out_dtype=torch.float16 if half else torch.float32, workspace=ws))
+            check(y, x, pr, sr, K, g, bias=b, relu=relu, half_out=half, what=f"relu={relu} half={half}")
+            if relu:
+                assert np.all(y >= 0)
+    say("case: skinny split affine codes")
+    wa = (np.random.default_rng(24).normal(0, 0.02, size=(N, K)) + 0.01).astype(np.float32)
+    pa, sa, za, _ = oracle.quantize_int4_affine(wa, g)
+    y = host(dq.int4_linear(xd, dev(pa), dev(sa), K, g, zeros=dev(za), workspace=ws))
+    check(y, x, pa, sa, K, g, zeros=za, what="skinny split affine")
+    say("case: skinny split edge rows")
+    pe, se = edge_matrix(N, K, g, seed=5)
+    y = host(dq.int4_linear(xd, dev(pe), dev(se), K, g, workspace=ws))
+    check(y, x, pe, se, K, g, what="skinny split edge rows")
