@@ -79,9 +79,14 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 // MT > 1 (MR == 0 only): M up to 16 MT rows of x as MT tiles of 16; each
 // expanded code word feeds MT MFMAs, one per tile.
 // sp.S > 1: the block takes share blockIdx.y of K (K-blocks kb0 .. kb0 +
-// sp.kb_per_share - 1, kb0 = blockIdx.y * sp.kb_per_share, a multiple of group / KB) and writes
-// its partial [M, 16 RG] tile to sp.part instead of y.
-template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1>
+// sp.kb_per_share - 1, kb0 = blockIdx.y * sp.kb_per_share, a whole number of
+// groups) and writes its partial [M, 16 RG] tile to sp.part instead of y.
+// GPK = 2 (KB = 64, group 32, MR = 0 only): each K-block holds two groups,
+// whose integer sums are kept apart (an MFMA per group, the other group's
+// codes zeroed) and multiplied by their own scales; the two scales (zero
+// points) are one 32-bit (16-bit) load. 64-code K-blocks halve the loads and
+// K-block steps of group 32 at 5 or more rows of x.
+template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1, int GPK = 1>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
@@ -90,12 +95,17 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
   constexpr int XB = (RG > 1 || MT > 1) ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
   static_assert(MR == 0 || (RG == 1 && MT == 1), "row groups and row tiles with direct x loads only");
+  static_assert(GPK == 1 || (GPK == 2 && KB == 64 && MR == 0), "two groups per K-block: KB = 64, direct x loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds);                  // [WAVES][RG][MT][64][4]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 15, h = lane >> 4;
+  // GPK = 2: the group (of the K-block's two) whose codes the lane holds, and
+  // a mask that keeps them where that is the first one
+  const int lgrp = h >> 1;
+  const uint32_t own0 = lgrp == 0 ? 0xFFFFFFFFu : 0u;
   const int n0 = blockIdx.x * 16 * RG;
   const int q = blockIdx.y;                    // share of K (0 without a split)
   const int kb0 = q * sp.kb_per_share;                  // its first K-block
@@ -108,8 +118,9 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   for (int r = 0; r < RG; ++r) {
     const int nrow = (n0 + 16 * r + col < N) ? n0 + 16 * r + col : N - 1;   // tail rows: read, discard
     prow[r] = packed + (int64_t)nrow * (K >> 1) + (int64_t)kb0 * (KB / 2) + h * (KB / 8);
-    srow[r] = scales + (int64_t)nrow * G + (kb0 >> kb_shift);
-    zrow[r] = AFF ? zeros + (int64_t)nrow * G + (kb0 >> kb_shift) : nullptr;
+    const int g0 = GPK == 2 ? 2 * kb0 : kb0 >> kb_shift;   // first group of the share
+    srow[r] = scales + (int64_t)nrow * G + g0;
+    zrow[r] = AFF ? zeros + (int64_t)nrow * G + g0 : nullptr;
   }
 
   // Weight and scale loads of the wave's share, K-block by K-block. They are
@@ -128,7 +139,8 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
-        sraw[r][u] = srow[r][j >> kb_shift];
+        if constexpr (GPK == 2) sraw[r][u] = *reinterpret_cast<const uint32_t*>(srow[r] + 2 * j);
+        else sraw[r][u] = srow[r][j >> kb_shift];
       }
     if constexpr (AFF) {
 #pragma unroll
@@ -136,7 +148,8 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
-          zraw[r][u] = zrow[r][j >> kb_shift];
+          if constexpr (GPK == 2) zraw[r][u] = *reinterpret_cast<const uint16_t*>(zrow[r] + 2 * j);
+          else zraw[r][u] = zrow[r][j >> kb_shift];
         }
     }
 #pragma unroll
@@ -235,23 +248,55 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
         if (u < U && wave + u * WAVES < nkb) {
 #pragma unroll
           for (int r = 0; r < RG; ++r) {
-            float4_t d[MT];
+            float4_t d[GPK][MT];               // integer sums, one per group of the K-block
 #pragma unroll
-            for (int t = 0; t < MT; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint32_t zb = AFF ? zp_bias_natural(zraw[r][u]) : 0u;
+            for (int q = 0; q < GPK; ++q)
+#pragma unroll
+              for (int t = 0; t < MT; ++t) d[q][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < DW; ++i) {
               half2_t hw[4];
-              if constexpr (AFF) codes_to_half_natural_zp(word_at<KB>(wv[r][u], i), hw, zb);
-              else codes_to_half_natural(word_at<KB>(wv[r][u], i), hw);
-              const half8_t bw = as_half8(hw);
+              if constexpr (AFF) {
+                // (GPK = 2: the zero point of the lane's own group)
+                const uint32_t zb = zp_bias_natural(GPK == 2 ? (zraw[r][u] >> (8 * lgrp)) & 0xFFu : zraw[r][u]);
+                codes_to_half_natural_zp(word_at<KB>(wv[r][u], i), hw, zb);
+              } else {
+                codes_to_half_natural(word_at<KB>(wv[r][u], i), hw);
+              }
+              if constexpr (GPK == 2) {
+                // An MFMA adds the products of all four lane groups, and the
+                // lanes of groups h = 0, 1 hold codes of the K-block's first
+                // group (codes 0-31), h = 2, 3 of its second: each group's sum
+                // is an MFMA in which the other group's lanes give zeros.
+                half2_t h0[4], h1[4];
 #pragma unroll
-              for (int t = 0; t < MT; ++t)
-                d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], bw, d[t], 0, 0, 0);
+                for (int k = 0; k < 4; ++k) {
+                  const uint32_t c = __builtin_bit_cast(uint32_t, hw[k]);
+                  h0[k] = __builtin_bit_cast(half2_t, c & own0);
+                  h1[k] = __builtin_bit_cast(half2_t, c & ~own0);
+                }
+                const half8_t b0 = as_half8(h0), b1 = as_half8(h1);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                  d[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], b0, d[0][t], 0, 0, 0);
+                  d[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], b1, d[1][t], 0, 0, 0);
+                }
+              } else {
+                const half8_t bw = as_half8(hw);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                  d[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], bw, d[0][t], 0, 0, 0);
+              }
             }
             const float sc = half_bits_to_float((uint16_t)sraw[r][u]);
+            if constexpr (GPK == 2) {
+              const float sc1 = half_bits_to_float((uint16_t)(sraw[r][u] >> 16));
 #pragma unroll
-            for (int t = 0; t < MT; ++t) acc[r][t] += sc * d[t];
+              for (int t = 0; t < MT; ++t) acc[r][t] += sc * d[0][t] + sc1 * d[1][t];
+            } else {
+#pragma unroll
+              for (int t = 0; t < MT; ++t) acc[r][t] += sc * d[0][t];
+            }
           }
         }
       }
@@ -589,11 +634,11 @@ static size_t skinny_lds(int waves, int U, int KB, int MR, int RG = 1, int MT = 
 }
 constexpr size_t kSkinnyLdsMax = 64 * 1024;
 
-template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1>
+template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1, int GPK = 1>
 static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                       const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                       hipStream_t stream) {
-  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG, AFF, MT>),
+  hipLaunchKernelGGL((matmul_skinny_kernel<KB, WAVES, U, MR, RG, AFF, MT, GPK>),
                      dim3((unsigned)((N + 16 * RG - 1) / (16 * RG)), (unsigned)sp.S), dim3(WAVES * 64),
                      skinny_lds(WAVES, U, KB, MR, RG, MT), stream, x, M, packed, scales, zeros, N, K, G,
                      kbs, y, ep, sp);
@@ -603,32 +648,32 @@ static void launch_mr(const _Float16* x, int M, const uint8_t* packed, const uin
 // its rows' share of x (M/(4 RG) bytes of x per byte of weights), so the
 // block takes as many row groups as its registers allow while the grid keeps
 // about one block per CU.
-template <int KB, int WAVES, int U, bool AFF, int MT>
+template <int KB, int WAVES, int U, bool AFF, int MT, int GPK>
 static void launch_tiles(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                          const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                          hipStream_t stream) {
   constexpr bool rg2 = WAVES <= 8;
   if constexpr (rg2) {
     if (N >= 256 * 16 * 2) {
-      launch_mr<KB, WAVES, U, 0, 2, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+      launch_mr<KB, WAVES, U, 0, 2, AFF, MT, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
-  launch_mr<KB, WAVES, U, 0, 1, AFF, MT>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  launch_mr<KB, WAVES, U, 0, 1, AFF, MT, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
 }
 
-template <int KB, int WAVES, int U, bool AFF>
+template <int KB, int WAVES, int U, bool AFF, int GPK>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                        const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                        hipStream_t stream) {
   if constexpr (WAVES < 16 || U <= 6) {           // refused by matmul_skinny_unsupported otherwise
     if (M > 32) {
-      launch_tiles<KB, WAVES, U, AFF, 4>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+      launch_tiles<KB, WAVES, U, AFF, 4, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
   if (M > 16) {
-    launch_tiles<KB, WAVES, U, AFF, 2>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+    launch_tiles<KB, WAVES, U, AFF, 2, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
     return;
   }
   const int MR = M == 1 ? 1 : (M == 2 ? 2 : 4);
@@ -639,18 +684,21 @@ static void launch_one(const _Float16* x, int M, const uint8_t* packed, const ui
   constexpr bool rg4 = WAVES <= 8, rg2 = WAVES <= 8 || U <= 6;
   if constexpr (rg4) {
     if (M > 4 && N >= 256 * 16 * 4) {
-      launch_mr<KB, WAVES, U, 0, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+      launch_mr<KB, WAVES, U, 0, 4, AFF, 1, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
   if constexpr (rg2) {
     if (M > 4 && N >= 256 * 16 * 2) {
-      launch_mr<KB, WAVES, U, 0, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+      launch_mr<KB, WAVES, U, 0, 2, AFF, 1, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
     }
   }
-  if (M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax)
-    launch_mr<KB, WAVES, U, 0, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  if (GPK == 2 || M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax) {
+    launch_mr<KB, WAVES, U, 0, 1, AFF, 1, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+    return;
+  }
+  if constexpr (GPK != 1) return;              // (two groups per K-block only with M > 4)
   else if (MR == 1)
     launch_mr<KB, WAVES, U, 1, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (MR == 2)
@@ -661,27 +709,33 @@ static void launch_one(const _Float16* x, int M, const uint8_t* packed, const ui
 
 // Waves per block and K-blocks per wave for nkb K-blocks: the fewest waves
 // (<= 16) that cover K with at most 4 K-blocks each, else 16 waves with up to 8.
-template <int KB, bool AFF>
+template <int KB, bool AFF, int GPK>
 static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                       const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                       hipStream_t stream) {
   const int nkb = sp.S > 1 ? sp.kb_per_share : K / KB;   // K-blocks of one block (of its share)
-  if (nkb <= 4 * 2) launch_one<KB, 4, 2, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else if (nkb <= 4 * 4) launch_one<KB, 4, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else if (nkb <= 8 * 4) launch_one<KB, 8, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else launch_one<KB, 16, 8, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  if (nkb <= 4 * 2) launch_one<KB, 4, 2, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 4 * 4) launch_one<KB, 4, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 8 * 4) launch_one<KB, 8, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  else launch_one<KB, 16, 8, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
 }
 
+// KB: codes per K-block. gpk = 2: K-blocks of 64 codes over groups of 32.
 template <bool AFF>
 static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
                             const uint16_t* scales, const uint8_t* zeros, int N, int K, int G,
-                            int KB, int kbs, void* y, Epilogue ep, const SkinnySplit& sp, hipStream_t stream) {
+                            int KB, int kbs, int gpk, void* y, Epilogue ep, const SkinnySplit& sp,
+                            hipStream_t stream) {
+  if (gpk == 2) {
+    launch_kb<64, AFF, 2>(xh, M, packed, scales, zeros, N, K, G, 0, y, ep, sp, stream);
+    return;
+  }
   switch (KB) {
-    case 128: launch_kb<128, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
-    case 64: launch_kb<64, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
-    default: launch_kb<32, AFF>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
+    case 128: launch_kb<128, AFF, 1>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
+    case 64: launch_kb<64, AFF, 1>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
+    default: launch_kb<32, AFF, 1>(xh, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream); break;
   }
 }
 
@@ -708,11 +762,17 @@ struct SkinnyPlan {
 static bool skinny_pipe_takes(int64_t M, int KB, int64_t K) {
   return M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 && M * K * 2 < ((int64_t)1 << 31);
 }
+// Codes per K-block of the older form for 5 or more rows of x: group 32 runs
+// as 64-code K-blocks of two groups each where K allows (see the kernel).
+static int skinny_rows_kb(int64_t M, int64_t K, int64_t group) {
+  return group == 32 && M > 4 && K % 64 == 0 ? 64 : skinny_kb(group);
+}
+// (kb_per_share counts K-blocks of skinny_rows_kb(M, K, group) codes)
 static SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group) {
   SkinnyPlan pl{1, 0, 0};
-  const int KB = skinny_kb(group);
+  const int KB = skinny_rows_kb(M, K, group);
   if (KB == 0 || M <= 4 || K % KB != 0 || skinny_pipe_takes(M, KB, K)) return pl;
-  const int64_t per_group = group / KB;        // K-blocks per group (a power of two)
+  const int64_t per_group = group > KB ? group / KB : 1;   // K-blocks per group (a power of two)
   const int64_t nkb = K / KB, rgroups = (N + 15) / 16, tiles = (M + 15) / 16;
   if (rgroups >= 128 || nkb * tiles < 96) return pl;
   for (int S = 8; S >= 2; S /= 2) {
@@ -744,14 +804,21 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
   int kbs = 0;
   while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);
+  // Two groups of 32 per 64-code K-block: their scales (zero points) are read
+  // as one 4-byte (2-byte) word, so the arrays must be aligned to that.
+  const int gpk = skinny_rows_kb(M, K, group) == 64 && group == 32 && ((uintptr_t)scales & 3) == 0 &&
+                  ((uintptr_t)zeros & 1) == 0 ? 2 : 1;
   const SkinnyPlan pl = skinny_plan(M, N, K, group);
   SkinnySplit sp{nullptr, 1, 0};
   if (pl.S > 1 && workspace && workspace_bytes >= pl.ws_bytes) {
-    sp = SkinnySplit{static_cast<float*>(workspace), pl.S, pl.kb_per_share};
+    // the plan counts K-blocks of skinny_rows_kb codes; without the 64-code
+    // form (unaligned scales) a share is twice as many 32-code K-blocks
+    const int kbps = gpk == 1 && skinny_rows_kb(M, K, group) != KB ? pl.kb_per_share * 2 : pl.kb_per_share;
+    sp = SkinnySplit{static_cast<float*>(workspace), pl.S, kbps};
     if (zeros)
-      launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
+      launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, gpk, y, ep, sp, stream);
     else
-      launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
+      launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, gpk, y, ep, sp, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_reduce(sp.part, sp.S, M, N, y, ep, stream);
@@ -803,9 +870,9 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
     }
   }
   if (zeros)
-    launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
+    launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, gpk, y, ep, sp, stream);
   else
-    launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, y, ep, sp, stream);
+    launch_skinny_t<false>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, gpk, y, ep, sp, stream);
   return hipGetLastError();
 }
 
