@@ -81,11 +81,12 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 // sp.S > 1: the block takes share blockIdx.y of K (K-blocks kb0 .. kb0 +
 // sp.kb_per_share - 1, kb0 = blockIdx.y * sp.kb_per_share, a whole number of
 // groups) and writes its partial [M, 16 RG] tile to sp.part instead of y.
-// GPK = 2 (KB = 64, group 32, MR = 0 only): each K-block holds two groups,
-// whose integer sums are kept apart (an MFMA per group, the other group's
-// codes zeroed) and multiplied by their own scales; the two scales (zero
-// points) are one 32-bit (16-bit) load. 64-code K-blocks halve the loads and
-// K-block steps of group 32 at 5 or more rows of x.
+// GPK = 2 (group KB / 2: KB = 64 for group 32, 128 for group 64; MR = 0
+// only): each K-block holds two groups, whose integer sums are kept apart
+// (an MFMA per group, the other group's codes zeroed) and multiplied by their
+// own scales; the two scales (zero points) are one 32-bit (16-bit) load.
+// K-blocks of two groups halve the loads and K-block steps at 5 or more rows
+// of x.
 template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1, int GPK = 1>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
   constexpr int XB = (RG > 1 || MT > 1) ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
   static_assert(MR == 0 || (RG == 1 && MT == 1), "row groups and row tiles with direct x loads only");
-  static_assert(GPK == 1 || (GPK == 2 && KB == 64 && MR == 0), "two groups per K-block: KB = 64, direct x loads");
+  static_assert(GPK == 1 || (GPK == 2 && KB >= 64 && MR == 0), "two groups per K-block: KB = 64 or 128, direct x loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds);                  // [WAVES][RG][MT][64][4]
 
@@ -718,18 +719,24 @@ static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uin
   else if (nkb <= 4 * 4) launch_one<KB, 4, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (nkb <= 8 * 4) launch_one<KB, 8, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else launch_one<KB, 16, 8, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  // (K-blocks of two groups number at most 64: K <= 128 groups; the longer
+  // forms are not built for them)
+  else if constexpr (GPK == 1) {
+    if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+    else launch_one<KB, 16, 8, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  }
 }
 
-// KB: codes per K-block. gpk = 2: K-blocks of 64 codes over groups of 32.
+// KB: codes per group-sized K-block (skinny_kb). gpk = 2: K-blocks of two
+// groups (2 KB codes) instead.
 template <bool AFF>
 static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
                             const uint16_t* scales, const uint8_t* zeros, int N, int K, int G,
                             int KB, int kbs, int gpk, void* y, Epilogue ep, const SkinnySplit& sp,
                             hipStream_t stream) {
-  if (gpk == 2) {
-    launch_kb<64, AFF, 2>(xh, M, packed, scales, zeros, N, K, G, 0, y, ep, sp, stream);
+  if (gpk == 2) {                              // K-blocks of two groups (32 or 64 codes)
+    if (KB == 32) launch_kb<64, AFF, 2>(xh, M, packed, scales, zeros, N, K, G, 0, y, ep, sp, stream);
+    else launch_kb<128, AFF, 2>(xh, M, packed, scales, zeros, N, K, G, 0, y, ep, sp, stream);
     return;
   }
   switch (KB) {
@@ -739,22 +746,24 @@ static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
   }
 }
 
-// Split of K (only with a workspace), for 17 to 64 rows of x and for long
-// rows: with fewer than 128 groups of 16 weight rows the grid leaves at least
-// half the CUs idle, and each block walks all of K for its rows alone. K is
-// then cut into S = 2, 4 or 8 shares (the most that keep the grid within two
-// blocks per CU), each at least 6 K-blocks and a whole number of groups; the
-// shares' partial tiles meet in the workspace and a second kernel adds them
-// in share order, as for the tiled kernel. That second kernel and the
-// boundary between the two cost about 4 us, so the split is taken only where
-// a block's work is long enough to lose more than that: at least 96 K-blocks
-// times 16-row tiles of x per row group, and not where the pipelined form
-// runs (5 to 16 rows, groups of 128 2^p). Measured (graph replays over a
-// >= 1 GiB pool, unsplit against split): [1024, 8192] M = 64 36.4 -> 17.1 us,
-// [768, 3072] group 64 M = 32 11.6 -> 9.6 us, group 32 M = 16 10.6 -> 9.6 us;
-// shorter work lost: group 64 M = 16 8.7 -> 8.8 us, M = 8 7.7 -> 8.4 us,
-// [768, 768] M = 16 3.9 -> 6.1 us, the pipelined form's [768, 3072] M = 16
-// 5.4 -> 7.1 us and [1024, 8192] M = 8 6.8 -> 9.4 us.
+// Split of K (only with a workspace), for 5 to 64 rows of x against small
+// matrices with long rows: with fewer than 128 groups of 16 weight rows the
+// grid leaves at least half the CUs idle, and each block walks all of K for
+// its rows alone. K is then cut into S = 2, 4 or 8 shares (the most that keep
+// the grid within two blocks per CU), each at least 6 K-blocks and a whole
+// number of groups; the shares' partial tiles meet in the workspace and a
+// second kernel adds them in share order, as for the tiled kernel. That
+// second kernel and the boundary between the two cost about 4 us, so the
+// split is taken only where a block's work is long enough to lose more than
+// that: at least 48 K-blocks (of skinny_rows_kb codes) times 16-row tiles of
+// x per row group, and not where the pipelined form runs (5 to 16 rows,
+// groups of 128 2^p). Measured (graph replays over a >= 1 GiB pool, split
+// against unsplit): [1024, 8192] M = 64 17.1 / 36.4 us, [1000, 4096] M = 33
+// 9.3 / 13.4, [768, 3072] group 128 M = 32 7.7 / 9.5, group 64 M = 32 8.2 /
+// 9.8 and M = 40 9.0 / 12.5, group 32 M = 32 9.7 / 11.7, [100, 4096] group 32
+// M = 17 7.8 / 10.2 and M = 5 6.8 / 7.7; at the threshold group 32 M = 16
+// 8.84 / 8.86; below it the split lost: [768, 3072] group 64 M = 16 7.5 /
+// 7.4 and M = 8 7.0 / 6.5, [300, 2048] group 64 M = 24 7.4 / 6.7.
 struct SkinnyPlan {
   int S, kb_per_share;
   int64_t ws_bytes;
@@ -762,19 +771,19 @@ struct SkinnyPlan {
 static bool skinny_pipe_takes(int64_t M, int KB, int64_t K) {
   return M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 && M * K * 2 < ((int64_t)1 << 31);
 }
-// Codes per K-block of the older form for 5 or more rows of x: group 32 runs
-// as 64-code K-blocks of two groups each where K allows (see the kernel).
+// Codes per K-block of the older form for 5 or more rows of x: groups 32 and
+// 64 run as K-blocks of two groups each where K allows (see the kernel).
 static int skinny_rows_kb(int64_t M, int64_t K, int64_t group) {
-  return group == 32 && M > 4 && K % 64 == 0 ? 64 : skinny_kb(group);
+  return (group == 32 || group == 64) && M > 4 && K % (2 * group) == 0 ? (int)(2 * group) : skinny_kb(group);
 }
 // (kb_per_share counts K-blocks of skinny_rows_kb(M, K, group) codes)
 static SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group) {
   SkinnyPlan pl{1, 0, 0};
   const int KB = skinny_rows_kb(M, K, group);
-  if (KB == 0 || M <= 4 || K % KB != 0 || skinny_pipe_takes(M, KB, K)) return pl;
+  if (KB == 0 || M <= 4 || K % KB != 0 || skinny_pipe_takes(M, skinny_kb(group), K)) return pl;
   const int64_t per_group = group > KB ? group / KB : 1;   // K-blocks per group (a power of two)
   const int64_t nkb = K / KB, rgroups = (N + 15) / 16, tiles = (M + 15) / 16;
-  if (rgroups >= 128 || nkb * tiles < 96) return pl;
+  if (rgroups >= 128 || nkb * tiles < 48) return pl;
   for (int S = 8; S >= 2; S /= 2) {
     if (rgroups * S > 512) continue;
     int64_t kbps = (nkb + S - 1) / S;
@@ -806,7 +815,7 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
   const _Float16* xh = static_cast<const _Float16*>(x);
   // Two groups of 32 per 64-code K-block: their scales (zero points) are read
   // as one 4-byte (2-byte) word, so the arrays must be aligned to that.
-  const int gpk = skinny_rows_kb(M, K, group) == 64 && group == 32 && ((uintptr_t)scales & 3) == 0 &&
+  const int gpk = skinny_rows_kb(M, K, group) == 2 * group && K <= 128 * group && ((uintptr_t)scales & 3) == 0 &&
                   ((uintptr_t)zeros & 1) == 0 ? 2 : 1;
   const SkinnyPlan pl = skinny_plan(M, N, K, group);
   SkinnySplit sp{nullptr, 1, 0};

@@ -179,7 +179,7 @@ def check(y, x, p, s, K, g, zeros=None, bias=None, relu=False, half_out=False, w
 # group 32, the VALU variant (group 96), the whole-row variant (50 MB);
 # M = 2 .. 4 with four x rows. skinny: staged x slices (M <= 4), direct loads
 # (M = 8, 16), two or four row groups per block (N >= 8192 / 16384), two and
-# four 16-row tiles (M = 24, 40), group 32 as 64-code K-blocks of two groups
+# four 16-row tiles (M = 24, 40), groups 32 and 64 as K-blocks of two groups
 # (M = 5 .. 40, one, two and four row groups). tiled: the 128 x 256, 128 x 128, 64 x 128
 # and 32 x 128 block tiles with 1, 2, 4 and 8 sub-steps per group, a group
 # size decided at run time (1024), 32-code sub-steps (group 32), ragged N and
@@ -195,6 +195,8 @@ PATH_CASES = [
     (300, 2048, 128, 24, "skinny"), (300, 2048, 128, 40, "skinny"),
     (300, 1024, 32, 5, "skinny"), (300, 2048, 32, 24, "skinny"), (300, 1024, 32, 40, "skinny"),
     (8200, 1024, 32, 8, "skinny"), (16400, 1024, 32, 6, "skinny"),
+    (300, 2048, 64, 8, "skinny"), (300, 1024, 64, 24, "skinny"), (300, 2048, 64, 40, "skinny"),
+    (8200, 1024, 64, 16, "skinny"), (16400, 2048, 64, 5, "skinny"),
     (4100, 1024, 128, 1280, "tiled"), (4100, 1024, 64, 1300, "tiled"), (4100, 2048, 1024, 1280, "tiled"),
     (2050, 1024, 64, 1280, "tiled"), (2048, 2048, 256, 630, "tiled"),
     (1030, 2048, 512, 100, "tiled"), (640, 4096, 1024, 300, "tiled"), (520, 1024, 32, 200, "tiled"),
@@ -216,7 +218,7 @@ def test_edge_rows_every_kernel(dq, N, K, g, M, path):
 
 AFFINE_CASES = [(300, 1024, 128, 1, "gemv"), (12300, 8192, 128, 1, "gemv"), (300, 1536, 96, 1, "gemv"),
                 (300, 4096, 128, 4, "gemv"), (300, 2048, 128, 8, "skinny"), (300, 2048, 64, 2, "skinny"),
-                (300, 1024, 32, 8, "skinny"), (300, 2048, 32, 24, "skinny"),
+                (300, 1024, 32, 8, "skinny"), (300, 2048, 32, 24, "skinny"), (300, 2048, 64, 16, "skinny"),
                 (4100, 1024, 128, 1280, "tiled"), (640, 4096, 1024, 300, "tiled"),
                 (520, 1024, 32, 200, "tiled"), (300, 1024, 128, 3, "generic")]
 
@@ -254,13 +256,12 @@ def test_edge_rows_epilogue(dq, N, K, g, M, path):
     check(yh, x, packed, scales, K, g, bias=b, relu=True, half_out=True, what=f"fp16 output M={M}")
 
 
-def test_group32_unaligned_scales(dq):
-    """Group 32 at 5 or more rows reads each 64-code K-block's two scales as one
-    4-byte word; scales at an address that is 2 mod 4 take the 32-code form,
-    with and without the split of K (whose shares are then counted in 32-code
-    K-blocks). Both against the oracle."""
-    for (N, K, M) in [(300, 1024, 16), (768, 3072, 32)]:
-        g = 32
+def test_two_group_kblocks_unaligned_scales(dq):
+    """Groups 32 and 64 at 5 or more rows read each K-block's two scales as one
+    4-byte word; scales at an address that is 2 mod 4 take the one-group
+    K-blocks, with and without the split of K (whose shares are then counted
+    in those K-blocks). Both against the oracle."""
+    for (N, K, M, g) in [(300, 1024, 16, 32), (768, 3072, 32, 32), (300, 1024, 8, 64), (768, 3072, 32, 64)]:
         packed, scales = edge_matrix(N, K, g, seed=N + M)
         G = scales.shape[1]
         buf = torch.zeros(N * G + 1, dtype=torch.float16, device=DEV)
@@ -269,7 +270,7 @@ def test_group32_unaligned_scales(dq):
         assert s_odd.data_ptr() % 4 == 2
         x = activations(M, K, seed=M + 3, extreme=False)
         xd, pd = dev(x), dev(packed)
-        say(f"case: group 32 unaligned scales N={N} K={K} M={M}")
+        say(f"case: unaligned scales N={N} K={K} M={M} g={g}")
         y = host(dq.int4_matmul_path(xd, pd, s_odd, K, g, "skinny"))
         check(y, x, packed, scales, K, g, what=f"unaligned scales N={N} M={M}")
         ws = dq.linear_workspace(M, N, K, g, device=DEV)

@@ -41,7 +41,7 @@ def test_noalloc_matches_workspace_entry_point():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream().cuda_stream
     # (M, N, K, group): four shares (8 MiB of scratch), then a smaller call with
-    # eight shares (3 MiB), the skinny kernel's split (eight shares, 768 KiB),
+    # eight shares (3 MiB), the skinny kernel's split (four shares, 384 KiB),
     # then one row (no scratch)
     for M, N, K, g in [(128, 4096, 4096, 128), (96, 1024, 8192, 128), (32, 768, 3072, 64), (1, 2048, 4096, 128)]:
         need = dq.linear_workspace_bytes(M, N, K, g)
