@@ -233,7 +233,8 @@ def test_edge_rows_affine(dq, N, K, g, M, path):
 
 
 EPI_CASES = [(300, 1024, 128, 1, "gemv"), (12300, 8192, 128, 1, "gemv"), (300, 4096, 128, 3, "gemv"),
-             (300, 2048, 128, 16, "skinny"), (4100, 1024, 128, 1280, "tiled"), (520, 1024, 32, 200, "tiled"),
+             (300, 2048, 128, 16, "skinny"), (300, 2048, 64, 16, "skinny"), (300, 1024, 32, 24, "skinny"),
+             (4100, 1024, 128, 1280, "tiled"), (520, 1024, 32, 200, "tiled"),
              (300, 1024, 128, 3, "generic")]
 
 
