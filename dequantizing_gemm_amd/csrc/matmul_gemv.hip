@@ -569,6 +569,22 @@ static void launch_gemv_t(const _Float16* xh0, int64_t M, const uint8_t* packed,
     hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, (int)M, packed, scales, zeros, (int)N, \
                        (int)K, G, (int)group, gsh, y, ep);                                      \
   } while (0)
+    if (N <= 1024 && cols > 4 && cols <= 6) {
+      // Small matrices (64 blocks of 16 rows or fewer) with rows of 5 or 6
+      // column blocks: 4 rows per block, their columns split over 3
+      // wavefronts, so that four times as many CUs stream the weights.
+      // Measured (graph replays over a >= 1 GiB pool): [768, 3072] M = 4
+      // 4.04 -> 3.62 us, M = 2 3.72 -> 3.29; [2048, 3072] M = 4 4.02 -> 4.43
+      // (not taken there).
+      const dim3 grid((unsigned)((N + 3) / 4)), block(64 * 3);
+      const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<6, 0, 1, AFF, 3, 4>
+                      : gsh == 1 ? matmul_gemv_mfma_kernel<6, 1, 1, AFF, 3, 4>
+                      : gsh == 2 ? matmul_gemv_mfma_kernel<6, 2, 1, AFF, 3, 4>
+                                 : matmul_gemv_mfma_kernel<6, 3, 1, AFF, 3, 4>;
+      hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, (int)M, packed, scales, zeros, (int)N,
+                         (int)K, G, (int)group, gsh, y, ep);
+      return;
+    }
     if (cols <= 2) INT4DQ_GEMV_MFMA4(2);
     else if (cols <= 4) INT4DQ_GEMV_MFMA4(4);
     else if (cols <= 6) INT4DQ_GEMV_MFMA4(6);
@@ -604,6 +620,31 @@ static void launch_gemv_t(const _Float16* xh0, int64_t M, const uint8_t* packed,
         break;
     }
 #undef INT4DQ_GEMV_ROWS
+    return;
+  }
+  if (gsh >= 0 && g_gemv_mfma && cols > 4 && cols <= 12 && (N <= 1024 || (N <= 2048 && cols > 8))) {
+    // Small matrices (64 blocks of 16 rows or fewer; 128 for rows of 9-12
+    // column blocks) with rows of 5 to 12 column blocks: 4 rows per block,
+    // their columns split over 3 (rows of 6) or 4 wavefronts, so that four
+    // times as many CUs stream the weights. Measured (graph replays over a
+    // >= 1 GiB pool), against 4 wavefronts of whole rows: [768, 3072] 3.26 ->
+    // 2.79 us, [512, 3072] 3.15 -> 2.76, [768, 4096] 3.37 -> 2.86, [1024, 6144]
+    // 4.37 -> 3.22, [2048, 6144] 4.59 -> 4.00; [4096, 3072] 3.60 -> 4.05 (not
+    // taken there); rows of 2 column blocks gained nothing.
+#define INT4DQ_GEMV_SPLITCOL(CMV, KSV)                                                            \
+  do {                                                                                          \
+    const dim3 grid((unsigned)((N + 3) / 4)), block(64 * KSV);                                  \
+    const auto kern = gsh == 0 ? matmul_gemv_mfma_kernel<CMV, 0, 1, AFF, KSV>                   \
+                    : gsh == 1 ? matmul_gemv_mfma_kernel<CMV, 1, 1, AFF, KSV>                   \
+                    : gsh == 2 ? matmul_gemv_mfma_kernel<CMV, 2, 1, AFF, KSV>                   \
+                               : matmul_gemv_mfma_kernel<CMV, 3, 1, AFF, KSV>;                  \
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, xh0, 1, packed, scales, zeros, (int)N,     \
+                       (int)K, G, (int)group, gsh, y, ep);                                      \
+  } while (0)
+    if (cols <= 6) INT4DQ_GEMV_SPLITCOL(6, 3);
+    else if (cols <= 8) INT4DQ_GEMV_SPLITCOL(8, 4);
+    else INT4DQ_GEMV_SPLITCOL(12, 4);
+#undef INT4DQ_GEMV_SPLITCOL
     return;
   }
   if (cols <= 24 && gsh >= 0 && g_gemv_mfma) {

@@ -176,18 +176,23 @@ def check(y, x, p, s, K, g, zeros=None, bias=None, relu=False, half_out=False, w
 
 # (N, K, group, M, path): each forced kernel, with the block layouts and group
 # cadences it has. gemv M = 1: matrix-core variant unsplit / column-split /
-# group 32, the VALU variant (group 96), the whole-row variant (50 MB);
-# M = 2 .. 4 with four x rows. skinny: staged x slices (M <= 4), direct loads
-# (M = 8, 16), two or four row groups per block (N >= 8192 / 16384), two and
-# four 16-row tiles (M = 24, 40), groups 32 and 64 as K-blocks of two groups
-# (M = 5 .. 40, one, two and four row groups). tiled: the 128 x 256, 128 x 128, 64 x 128
-# and 32 x 128 block tiles with 1, 2, 4 and 8 sub-steps per group, a group
-# size decided at run time (1024), 32-code sub-steps (group 32), ragged N and
-# M tails. generic: binary16 x.
+# group 32, the VALU variant (group 96), the whole-row variant (50 MB), the
+# 4-row blocks of small matrices with columns split over 3 and 4 wavefronts
+# (rows of 6, 11 and 12 column blocks); M = 2 .. 4 with four x rows, also in
+# 4-row blocks over 3 wavefronts (rows of 5 and 6 column blocks). skinny:
+# staged x slices (M <= 4), direct loads (M = 8, 16), two or four row groups
+# per block (N >= 8192 / 16384), two and four 16-row tiles (M = 24, 40),
+# groups 32 and 64 as K-blocks of two groups (M = 5 .. 40, one, two and four
+# row groups). tiled: the 128 x 256, 128 x 128, 64 x 128 and 32 x 128 block
+# tiles with 1, 2, 4 and 8 sub-steps per group, a group size decided at run
+# time (1024), 32-code sub-steps (group 32), ragged N and M tails. generic:
+# binary16 x.
 PATH_CASES = [
     (300, 1024, 128, 1, "gemv"), (300, 8192, 128, 1, "gemv"), (300, 1024, 32, 1, "gemv"),
     (300, 1536, 96, 1, "gemv"), (12300, 8192, 128, 1, "gemv"), (300, 4096, 512, 1, "gemv"),
     (300, 4096, 256, 2, "gemv"), (300, 8192, 128, 3, "gemv"), (77, 2048, 64, 4, "gemv"),
+    (300, 3072, 64, 1, "gemv"), (700, 5632, 128, 1, "gemv"), (2000, 6144, 32, 1, "gemv"),
+    (300, 2560, 32, 3, "gemv"), (1000, 3072, 128, 4, "gemv"),
     (300, 2048, 128, 1, "skinny"), (300, 2048, 64, 2, "skinny"), (300, 2048, 256, 4, "skinny"),
     (300, 2048, 128, 8, "skinny"), (300, 1024, 32, 16, "skinny"), (8200, 1024, 128, 8, "skinny"),
     (16400, 1024, 128, 6, "skinny"), (16400, 2304, 256, 12, "skinny"), (8300, 4096, 128, 16, "skinny"),
@@ -217,7 +222,8 @@ def test_edge_rows_every_kernel(dq, N, K, g, M, path):
 
 
 AFFINE_CASES = [(300, 1024, 128, 1, "gemv"), (12300, 8192, 128, 1, "gemv"), (300, 1536, 96, 1, "gemv"),
-                (300, 4096, 128, 4, "gemv"), (300, 2048, 128, 8, "skinny"), (300, 2048, 64, 2, "skinny"),
+                (300, 4096, 128, 4, "gemv"), (300, 3072, 64, 4, "gemv"), (700, 6144, 128, 1, "gemv"),
+                (300, 2048, 128, 8, "skinny"), (300, 2048, 64, 2, "skinny"),
                 (300, 1024, 32, 8, "skinny"), (300, 2048, 32, 24, "skinny"), (300, 2048, 64, 16, "skinny"),
                 (4100, 1024, 128, 1280, "tiled"), (640, 4096, 1024, 300, "tiled"),
                 (520, 1024, 32, 200, "tiled"), (300, 1024, 128, 3, "generic")]
