@@ -361,7 +361,8 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 }
 
 // Pipelined form for 5 to 16 rows of x with K a multiple of 256 and group
-// sizes 128 * 2^p. A block of 4 wavefronts owns RG (1 to 4) groups of 16 weight rows;
+// sizes 128 * 2^p. A block of 4 wavefronts (8, with one pair-block in flight
+// each, for one row group and long rows) owns RG (1 to 4) groups of 16 weight rows;
 // the wavefronts split K into pair-blocks of 256 codes (two K-blocks;
 // wavefront w takes pair-blocks w, w + 4, ...), and each walks its share with
 // the loads of the next P pair-blocks in flight.
@@ -391,15 +392,16 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 // code order, the group's scale on each partial; rows of x >= M repeat a
 // lower row and are discarded). The four wavefronts' partial tiles are added
 // through LDS at the end.
-template <int RG, int P, bool AFF, int XR, bool GP>
-__global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
+template <int RG, int P, bool AFF, int XR, bool GP, int WAVES_ = 4>
+__global__ __launch_bounds__(64 * WAVES_) void matmul_skinny_pipe_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N, int K, int G,
     int kb_shift, void* __restrict__ y, Epilogue ep) {
   // Dynamic LDS: the block's scales (16 RG G binary16, rounded up to 1 KB),
   // then its zero points (16 RG G bytes, rounded up to 1 KB).
   extern __shared__ __attribute__((aligned(16))) uint8_t sz_lds[];
-  constexpr int PB = 256, WAVES = 4;           // codes per pair-block
+  constexpr int PB = 256, WAVES = WAVES_;      // codes per pair-block; wavefronts (4 or 8)
+  static_assert(WAVES == 4 || WAVES == 8, "wavefronts per block");
   static_assert(XR == 8 || XR == 16, "x rows staged");
   constexpr int XI = XR / 2;                   // x DMA loads per pair-block (2 rows each)
   constexpr int SLOT = XR * 2 * PB;            // bytes of one pair-block of x
@@ -578,12 +580,13 @@ __global__ __launch_bounds__(256) void matmul_skinny_pipe_kernel(
 #pragma unroll
   for (int r = 0; r < RG; ++r) *reinterpret_cast<float4_t*>(red + ((wave * RG + r) * 64 + lane) * 4) = acc[r];
   __syncthreads();
-  for (int t = tid; t < 16 * M * RG; t += 256) {
+  for (int t = tid; t < 16 * M * RG; t += 64 * WAVES) {
     const int r = t / (16 * M), rem = t - r * 16 * M;
     const int m = rem >> 4, nn = rem & 15;
     const int src = (m >> 2) * 16 + nn, i = m & 3;
     auto at = [&](int w) { return red[((w * RG + r) * 64 + src) * 4 + i]; };
-    const float v = (at(0) + at(1)) + (at(2) + at(3));
+    float v = (at(0) + at(1)) + (at(2) + at(3));
+    if constexpr (WAVES == 8) v += (at(4) + at(5)) + (at(6) + at(7));
     const int n = n0 + 16 * r + nn;
     if (n < N) ep.store(y, (int64_t)m * N + n, v, n);
   }
@@ -852,10 +855,23 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
     const bool gp = kbs == 0;
     const int lds_sz = ((16 * RG * G * 2 + 1023) & ~1023) + (zeros ? (16 * RG * G + 1023) & ~1023 : 0);
     if (((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 15) == 0 && lds_sz <= 32 * 1024) {
-      const dim3 grid((unsigned)((rgroups + RG - 1) / RG)), block(256);
+      // One row group per block and rows of 32 pair-blocks or more: eight
+      // wavefronts with one pair-block in flight each (the same loads in
+      // flight per CU, half as many steps per wavefront). Measured on
+      // [4096, 11008] (graph replays over a >= 1 GiB pool): M = 16 11.66 ->
+      // 11.25 us, M = 8 10.04 -> 9.64; on [4096, 4096] (16 pair-blocks) and
+      // with several row groups per block it was slower.
+      const bool eight = RG == 1 && K / 256 >= 32;
+      const dim3 grid((unsigned)((rgroups + RG - 1) / RG)), block(eight ? 512 : 256);
 #define INT4DQ_PIPE(RGV, A, XRV, GPV)                                                                  \
-  hipLaunchKernelGGL((matmul_skinny_pipe_kernel<RGV, 2, A, XRV, GPV>), grid, block, lds_sz, stream, xh, \
-                     (int)M, packed, scales, zeros, (int)N, (int)K, G, kbs, y, ep)
+  do {                                                                                                 \
+    if (RGV == 1 && eight)                                                                             \
+      hipLaunchKernelGGL((matmul_skinny_pipe_kernel<1, 1, A, XRV, GPV, 8>), grid, block, lds_sz, stream, \
+                         xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, kbs, y, ep);              \
+    else                                                                                               \
+      hipLaunchKernelGGL((matmul_skinny_pipe_kernel<RGV, 2, A, XRV, GPV>), grid, block, lds_sz, stream,  \
+                         xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, kbs, y, ep);              \
+  } while (0)
 #define INT4DQ_PIPE_RG(A, XRV, GPV)                                                                    \
   do {                                                                                                 \
     if (RG == 4) INT4DQ_PIPE(4, A, XRV, GPV);                                                          \

@@ -181,7 +181,9 @@ def check(y, x, p, s, K, g, zeros=None, bias=None, relu=False, half_out=False, w
 # (rows of 6, 11 and 12 column blocks); M = 2 .. 4 with four x rows, also in
 # 4-row blocks over 3 wavefronts (rows of 5 and 6 column blocks). skinny:
 # staged x slices (M <= 4), direct loads (M = 8, 16), two or four row groups
-# per block (N >= 8192 / 16384), two and four 16-row tiles (M = 24, 40),
+# per block (N >= 8192 / 16384), eight wavefronts for one row group and rows
+# of 32 or more pair-blocks (K = 8192, 11008), two and four 16-row tiles
+# (M = 24, 40),
 # groups 32 and 64 as K-blocks of two groups (M = 5 .. 40, one, two and four
 # row groups). tiled: the 128 x 256, 128 x 128, 64 x 128 and 32 x 128 block
 # tiles with 1, 2, 4 and 8 sub-steps per group, a group size decided at run
@@ -196,7 +198,7 @@ PATH_CASES = [
     (300, 2048, 128, 1, "skinny"), (300, 2048, 64, 2, "skinny"), (300, 2048, 256, 4, "skinny"),
     (300, 2048, 128, 8, "skinny"), (300, 1024, 32, 16, "skinny"), (8200, 1024, 128, 8, "skinny"),
     (16400, 1024, 128, 6, "skinny"), (16400, 2304, 256, 12, "skinny"), (8300, 4096, 128, 16, "skinny"),
-    (8192, 2048, 128, 10, "skinny"),
+    (8192, 2048, 128, 10, "skinny"), (300, 8192, 128, 16, "skinny"), (1000, 11008, 128, 5, "skinny"),
     (300, 2048, 128, 24, "skinny"), (300, 2048, 128, 40, "skinny"),
     (300, 1024, 32, 5, "skinny"), (300, 2048, 32, 24, "skinny"), (300, 1024, 32, 40, "skinny"),
     (8200, 1024, 32, 8, "skinny"), (16400, 1024, 32, 6, "skinny"),
@@ -223,7 +225,7 @@ def test_edge_rows_every_kernel(dq, N, K, g, M, path):
 
 AFFINE_CASES = [(300, 1024, 128, 1, "gemv"), (12300, 8192, 128, 1, "gemv"), (300, 1536, 96, 1, "gemv"),
                 (300, 4096, 128, 4, "gemv"), (300, 3072, 64, 4, "gemv"), (700, 6144, 128, 1, "gemv"),
-                (300, 2048, 128, 8, "skinny"), (300, 2048, 64, 2, "skinny"),
+                (300, 2048, 128, 8, "skinny"), (300, 8192, 128, 12, "skinny"), (300, 2048, 64, 2, "skinny"),
                 (300, 1024, 32, 8, "skinny"), (300, 2048, 32, 24, "skinny"), (300, 2048, 64, 16, "skinny"),
                 (4100, 1024, 128, 1280, "tiled"), (640, 4096, 1024, 300, "tiled"),
                 (520, 1024, 32, 200, "tiled"), (300, 1024, 128, 3, "generic")]
