@@ -185,7 +185,8 @@ def check(y, x, p, s, K, g, zeros=None, bias=None, relu=False, half_out=False, w
 # of 32 or more pair-blocks (K = 8192, 11008), two and four 16-row tiles
 # (M = 24, 40),
 # groups 32 and 64 as K-blocks of two groups (M = 5 .. 40, one, two and four
-# row groups). tiled: the 128 x 256, 128 x 128, 64 x 128 and 32 x 128 block
+# row groups, rows of a single K-block; K = 192 with group 64 keeps one-group
+# K-blocks). tiled: the 128 x 256, 128 x 128, 64 x 128 and 32 x 128 block
 # tiles with 1, 2, 4 and 8 sub-steps per group, a group size decided at run
 # time (1024), 32-code sub-steps (group 32), ragged N and M tails. generic:
 # binary16 x.
@@ -201,6 +202,7 @@ PATH_CASES = [
     (8192, 2048, 128, 10, "skinny"), (300, 8192, 128, 16, "skinny"), (1000, 11008, 128, 5, "skinny"),
     (300, 2048, 128, 24, "skinny"), (300, 2048, 128, 40, "skinny"),
     (300, 1024, 32, 5, "skinny"), (300, 2048, 32, 24, "skinny"), (300, 1024, 32, 40, "skinny"),
+    (40, 64, 32, 8, "skinny"), (33, 128, 64, 6, "skinny"), (50, 192, 64, 20, "skinny"),
     (8200, 1024, 32, 8, "skinny"), (16400, 1024, 32, 6, "skinny"),
     (300, 2048, 64, 8, "skinny"), (300, 1024, 64, 24, "skinny"), (300, 2048, 64, 40, "skinny"),
     (8200, 1024, 64, 16, "skinny"), (16400, 2048, 64, 5, "skinny"),
