@@ -81,12 +81,12 @@ __device__ __forceinline__ uint32_t word_at(const typename WLoad<KB>::T& v, int 
 // sp.S > 1: the block takes share blockIdx.y of K (K-blocks kb0 .. kb0 +
 // sp.kb_per_share - 1, kb0 = blockIdx.y * sp.kb_per_share, a whole number of
 // groups) and writes its partial [M, 16 RG] tile to sp.part instead of y.
-// GPK = 2 (group KB / 2: KB = 64 for group 32, 128 for group 64; MR = 0
-// only): each K-block holds two groups, whose integer sums are kept apart
-// (an MFMA per group, the other group's codes zeroed) and multiplied by their
-// own scales; the two scales (zero points) are one 32-bit (16-bit) load.
-// K-blocks of two groups halve the loads and K-block steps at 5 or more rows
-// of x.
+// GPK = 2 or 4 (MR = 0 only): each K-block holds GPK groups of KB / GPK
+// codes (two of 32 or 64, four of 32), whose integer sums are kept apart (an
+// MFMA per group, the other groups' codes zeroed) and multiplied by their own
+// scales; the scales (zero points) of a K-block are one 4- or 8-byte (2- or
+// 4-byte) load. K-blocks of several groups cut the loads and K-block steps
+// at 5 or more rows of x.
 template <int KB, int WAVES, int U, int MR, int RG, bool AFF, int MT = 1, int GPK = 1>
 __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
     const _Float16* __restrict__ x, int M, const uint8_t* __restrict__ packed,
@@ -96,17 +96,17 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   constexpr int DW = KB / 32;                 // code words per lane per K-block = MFMAs
   constexpr int XB = (RG > 1 || MT > 1) ? 1 : (U < 4 ? U : 4);   // K-blocks per batch of direct x loads
   static_assert(MR == 0 || (RG == 1 && MT == 1), "row groups and row tiles with direct x loads only");
-  static_assert(GPK == 1 || (GPK == 2 && KB >= 64 && MR == 0), "two groups per K-block: KB = 64 or 128, direct x loads");
+  static_assert(GPK == 1 || ((GPK == 2 || GPK == 4) && KB / GPK >= 32 && MR == 0),
+                "several groups per K-block: groups of 32 codes or more, direct x loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds);                  // [WAVES][RG][MT][64][4]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 15, h = lane >> 4;
-  // GPK = 2: the group (of the K-block's two) whose codes the lane holds, and
-  // a mask that keeps them where that is the first one
-  const int lgrp = h >> 1;
-  const uint32_t own0 = lgrp == 0 ? 0xFFFFFFFFu : 0u;
+  // GPK > 1: lane group h holds codes h KB/4 .. (h+1) KB/4 - 1 of a K-block,
+  // all in the K-block's group (h GPK) / 4
+  const int lgrp = (h * GPK) >> 2;
   const int n0 = blockIdx.x * 16 * RG;
   const int q = blockIdx.y;                    // share of K (0 without a split)
   const int kb0 = q * sp.kb_per_share;                  // its first K-block
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   for (int r = 0; r < RG; ++r) {
     const int nrow = (n0 + 16 * r + col < N) ? n0 + 16 * r + col : N - 1;   // tail rows: read, discard
     prow[r] = packed + (int64_t)nrow * (K >> 1) + (int64_t)kb0 * (KB / 2) + h * (KB / 8);
-    const int g0 = GPK == 2 ? 2 * kb0 : kb0 >> kb_shift;   // first group of the share
+    const int g0 = GPK > 1 ? GPK * kb0 : kb0 >> kb_shift;   // first group of the share
     srow[r] = scales + (int64_t)nrow * G + g0;
     zrow[r] = AFF ? zeros + (int64_t)nrow * G + g0 : nullptr;
   }
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
   // issued after the (smaller) x staging loads, so that each K-block's
   // compute waits only for its own weights (loads return in order).
   wvec_t wv[RG][U];
-  uint32_t sraw[RG][U], zraw[RG][U];
+  uint32_t sraw[RG][U][GPK == 4 ? 2 : 1], zraw[RG][U];   // scale bits (two per word), zero points
   // Straight-line, unconditional loads: a K-block index past the end is
   // clamped to the wave's last valid one (the value is loaded and ignored), so
   // no branch splits the sequence and no use is scheduled between the loads.
@@ -140,8 +140,15 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
-        if constexpr (GPK == 2) sraw[r][u] = *reinterpret_cast<const uint32_t*>(srow[r] + 2 * j);
-        else sraw[r][u] = srow[r][j >> kb_shift];
+        if constexpr (GPK == 4) {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(srow[r] + 4 * j);
+          sraw[r][u][0] = v.x;
+          sraw[r][u][GPK == 4 ? 1 : 0] = v.y;
+        } else if constexpr (GPK == 2) {
+          sraw[r][u][0] = *reinterpret_cast<const uint32_t*>(srow[r] + 2 * j);
+        } else {
+          sraw[r][u][0] = srow[r][j >> kb_shift];
+        }
       }
     if constexpr (AFF) {
 #pragma unroll
@@ -149,7 +156,8 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int j = wave + u * WAVES < nkb ? wave + u * WAVES : nkb - 1;
-          if constexpr (GPK == 2) zraw[r][u] = *reinterpret_cast<const uint16_t*>(zrow[r] + 2 * j);
+          if constexpr (GPK == 4) zraw[r][u] = *reinterpret_cast<const uint32_t*>(zrow[r] + 4 * j);
+          else if constexpr (GPK == 2) zraw[r][u] = *reinterpret_cast<const uint16_t*>(zrow[r] + 2 * j);
           else zraw[r][u] = zrow[r][j >> kb_shift];
         }
     }
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
           else codes_to_half_spread(word_at<KB>(wv[0][u], i), hw);
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], as_half8(hw), d, 0, 0, 0);
         }
-        acc[0][0] += half_bits_to_float((uint16_t)sraw[0][u]) * d;
+        acc[0][0] += half_bits_to_float((uint16_t)sraw[0][u][0]) * d;
       }
     }
   } else {
@@ -258,29 +266,28 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
             for (int i = 0; i < DW; ++i) {
               half2_t hw[4];
               if constexpr (AFF) {
-                // (GPK = 2: the zero point of the lane's own group)
-                const uint32_t zb = zp_bias_natural(GPK == 2 ? (zraw[r][u] >> (8 * lgrp)) & 0xFFu : zraw[r][u]);
+                // (GPK > 1: the zero point of the lane's own group)
+                const uint32_t zb = zp_bias_natural(GPK > 1 ? (zraw[r][u] >> (8 * lgrp)) & 0xFFu : zraw[r][u]);
                 codes_to_half_natural_zp(word_at<KB>(wv[r][u], i), hw, zb);
               } else {
                 codes_to_half_natural(word_at<KB>(wv[r][u], i), hw);
               }
-              if constexpr (GPK == 2) {
-                // An MFMA adds the products of all four lane groups, and the
-                // lanes of groups h = 0, 1 hold codes of the K-block's first
-                // group (codes 0-31), h = 2, 3 of its second: each group's sum
-                // is an MFMA in which the other group's lanes give zeros.
-                half2_t h0[4], h1[4];
+              if constexpr (GPK > 1) {
+                // An MFMA adds the products of all four lane groups, and lane
+                // group h holds codes of the K-block's group (h GPK) / 4 only:
+                // each group's sum is an MFMA in which the other groups'
+                // lanes give zeros.
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                  const uint32_t c = __builtin_bit_cast(uint32_t, hw[k]);
-                  h0[k] = __builtin_bit_cast(half2_t, c & own0);
-                  h1[k] = __builtin_bit_cast(half2_t, c & ~own0);
-                }
-                const half8_t b0 = as_half8(h0), b1 = as_half8(h1);
+                for (int g = 0; g < GPK; ++g) {
+                  const uint32_t keep = lgrp == g ? 0xFFFFFFFFu : 0u;
+                  half2_t hg[4];
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                  d[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], b0, d[0][t], 0, 0, 0);
-                  d[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], b1, d[1][t], 0, 0, 0);
+                  for (int k = 0; k < 4; ++k)
+                    hg[k] = __builtin_bit_cast(half2_t, __builtin_bit_cast(uint32_t, hw[k]) & keep);
+                  const half8_t bg = as_half8(hg);
+#pragma unroll
+                  for (int t = 0; t < MT; ++t)
+                    d[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], bg, d[g][t], 0, 0, 0);
                 }
               } else {
                 const half8_t bw = as_half8(hw);
@@ -289,14 +296,14 @@ __global__ __launch_bounds__(WAVES * 64) void matmul_skinny_kernel(
                   d[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][v][i], bw, d[0][t], 0, 0, 0);
               }
             }
-            const float sc = half_bits_to_float((uint16_t)sraw[r][u]);
-            if constexpr (GPK == 2) {
-              const float sc1 = half_bits_to_float((uint16_t)(sraw[r][u] >> 16));
+            // each group's integer sum times its scale, groups in order
 #pragma unroll
-              for (int t = 0; t < MT; ++t) acc[r][t] += sc * d[0][t] + sc1 * d[1][t];
-            } else {
+            for (int t = 0; t < MT; ++t) {
+              float4_t part = half_bits_to_float((uint16_t)sraw[r][u][0]) * d[0][t];
 #pragma unroll
-              for (int t = 0; t < MT; ++t) acc[r][t] += sc * d[0][t];
+              for (int g = 1; g < GPK; ++g)
+                part += half_bits_to_float((uint16_t)(sraw[r][u][g >> 1] >> (16 * (g & 1)))) * d[g][t];
+              acc[r][t] += part;
             }
           }
         }
@@ -670,7 +677,9 @@ template <int KB, int WAVES, int U, bool AFF, int GPK>
 static void launch_one(const _Float16* x, int M, const uint8_t* packed, const uint16_t* scales,
                        const uint8_t* zeros, int N, int K, int G, int kbs, void* y, Epilogue ep, const SkinnySplit& sp,
                        hipStream_t stream) {
-  if constexpr (WAVES < 16 || U <= 6) {           // refused by matmul_skinny_unsupported otherwise
+  if constexpr ((WAVES < 16 || U <= 6) && GPK < 4) {   // refused by matmul_skinny_unsupported otherwise
+    // (four groups per K-block are not taken for more than 32 rows of x: four
+    // sums of four row tiles would spill)
     if (M > 32) {
       launch_tiles<KB, WAVES, U, AFF, 4, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
       return;
@@ -698,11 +707,11 @@ static void launch_one(const _Float16* x, int M, const uint8_t* packed, const ui
       return;
     }
   }
-  if (GPK == 2 || M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax) {
+  if (GPK > 1 || M > 4 || skinny_lds(WAVES, U, KB, MR) > kSkinnyLdsMax) {
     launch_mr<KB, WAVES, U, 0, 1, AFF, 1, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
     return;
   }
-  if constexpr (GPK != 1) return;              // (two groups per K-block only with M > 4)
+  if constexpr (GPK != 1) return;              // (several groups per K-block only with M > 4)
   else if (MR == 1)
     launch_mr<KB, WAVES, U, 1, 1, AFF>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (MR == 2)
@@ -721,22 +730,28 @@ static void launch_kb(const _Float16* x, int M, const uint8_t* packed, const uin
   if (nkb <= 4 * 2) launch_one<KB, 4, 2, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (nkb <= 4 * 4) launch_one<KB, 4, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
   else if (nkb <= 8 * 4) launch_one<KB, 8, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  else if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-  // (K-blocks of two groups number at most 64: K <= 128 groups; the longer
-  // forms are not built for them)
-  else if constexpr (GPK == 1) {
-    if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
-    else launch_one<KB, 16, 8, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+  // (K-blocks of two groups number at most 64, of four at most 32: K <= 128
+  // groups; the longer forms are not built for them)
+  else if constexpr (GPK <= 2) {
+    if (nkb <= 16 * 4) launch_one<KB, 16, 4, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+    else if constexpr (GPK == 1) {
+      if (nkb <= 16 * 6) launch_one<KB, 16, 6, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+      else launch_one<KB, 16, 8, AFF, GPK>(x, M, packed, scales, zeros, N, K, G, kbs, y, ep, sp, stream);
+    }
   }
 }
 
-// KB: codes per group-sized K-block (skinny_kb). gpk = 2: K-blocks of two
-// groups (2 KB codes) instead.
+// KB: codes per group-sized K-block (skinny_kb). gpk = 2 or 4: K-blocks of
+// gpk groups (gpk KB codes) instead.
 template <bool AFF>
 static void launch_skinny_t(const _Float16* xh, int M, const uint8_t* packed,
                             const uint16_t* scales, const uint8_t* zeros, int N, int K, int G,
                             int KB, int kbs, int gpk, void* y, Epilogue ep, const SkinnySplit& sp,
                             hipStream_t stream) {
+  if (gpk == 4) {                              // K-blocks of four groups of 32
+    launch_kb<128, AFF, 4>(xh, M, packed, scales, zeros, N, K, G, 0, y, ep, sp, stream);
+    return;
+  }
   if (gpk == 2) {                              // K-blocks of two groups (32 or 64 codes)
     if (KB == 32) launch_kb<64, AFF, 2>(xh, M, packed, scales, zeros, N, K, G, 0, y, ep, sp, stream);
     else launch_kb<128, AFF, 2>(xh, M, packed, scales, zeros, N, K, G, 0, y, ep, sp, stream);
@@ -775,9 +790,12 @@ static bool skinny_pipe_takes(int64_t M, int KB, int64_t K) {
   return M > 4 && M <= 16 && KB == 128 && K % 256 == 0 && K >= 4 * 256 && M * K * 2 < ((int64_t)1 << 31);
 }
 // Codes per K-block of the older form for 5 or more rows of x: groups 32 and
-// 64 run as K-blocks of two groups each where K allows (see the kernel).
+// 64 run as K-blocks of 128 codes (four or two groups) where K allows, group
+// 32 else as 64-code K-blocks of two groups (see the kernel).
 static int skinny_rows_kb(int64_t M, int64_t K, int64_t group) {
-  return (group == 32 || group == 64) && M > 4 && K % (2 * group) == 0 ? (int)(2 * group) : skinny_kb(group);
+  if ((group == 32 || group == 64) && M > 4 && K % 128 == 0) return 128;
+  if (group == 32 && M > 4 && K % 64 == 0) return 64;
+  return skinny_kb(group);
 }
 // (kb_per_share counts K-blocks of skinny_rows_kb(M, K, group) codes)
 static SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int64_t group) {
@@ -816,16 +834,21 @@ hipError_t launch_matmul_skinny(const void* x, int64_t M, const uint8_t* packed,
   int kbs = 0;
   while ((KB << kbs) < group) ++kbs;                  // group = KB << kbs
   const _Float16* xh = static_cast<const _Float16*>(x);
-  // Two groups of 32 per 64-code K-block: their scales (zero points) are read
-  // as one 4-byte (2-byte) word, so the arrays must be aligned to that.
-  const int gpk = skinny_rows_kb(M, K, group) == 2 * group && K <= 128 * group && ((uintptr_t)scales & 3) == 0 &&
-                  ((uintptr_t)zeros & 1) == 0 ? 2 : 1;
+  // Groups per K-block (1, 2 or 4): a K-block's scales (zero points) are read
+  // as one 2 gpk-byte (gpk-byte) word, so the arrays must be aligned to that;
+  // else fewer groups per K-block.
+  int gpk = skinny_rows_kb(M, K, group) / KB;
+  if (gpk == 4 && M > 32) gpk = 2;             // (four sums of four row tiles would spill)
+  while (gpk > 1 && (((uintptr_t)scales & (2 * gpk - 1)) != 0 || ((uintptr_t)zeros & (gpk - 1)) != 0 ||
+                     K % (gpk * group) != 0))
+    gpk >>= 1;
+  if (K > 128 * group) gpk = 1;                // (refused by matmul_skinny_unsupported)
   const SkinnyPlan pl = skinny_plan(M, N, K, group);
   SkinnySplit sp{nullptr, 1, 0};
   if (pl.S > 1 && workspace && workspace_bytes >= pl.ws_bytes) {
-    // the plan counts K-blocks of skinny_rows_kb codes; without the 64-code
-    // form (unaligned scales) a share is twice as many 32-code K-blocks
-    const int kbps = gpk == 1 && skinny_rows_kb(M, K, group) != KB ? pl.kb_per_share * 2 : pl.kb_per_share;
+    // the plan counts K-blocks of skinny_rows_kb codes; with fewer groups per
+    // K-block (unaligned scales) a share is proportionally more K-blocks
+    const int kbps = pl.kb_per_share * (skinny_rows_kb(M, K, group) / (gpk * KB));
     sp = SkinnySplit{static_cast<float*>(workspace), pl.S, kbps};
     if (zeros)
       launch_skinny_t<true>(xh, (int)M, packed, scales, zeros, (int)N, (int)K, G, KB, kbs, gpk, y, ep, sp, stream);

@@ -269,13 +269,12 @@ def _split_bytes(tiles, S, M, N):
     # 64 rows against 1024 weight rows: the skinny kernel, K in 8 shares of 8
     # K-blocks (64 row groups)
     (64, 1024, 8192, 128, 8 * 64 * 1024 * 4),
-    # the skinny kernel's split: group 32 at M = 32 and 16 (48 K-blocks of
-    # 64 codes times two and one row tiles, 8 shares), group 64 at M = 32
-    # (24 K-blocks of 128 codes times two row tiles, 4 shares of 6); not
-    # taken for less work per row group (group 64 at M = 16: 24 K-blocks),
-    # where the pipelined form runs (group 128, 5-16 rows) or with 128 row
-    # groups or more
-    (32, 768, 3072, 32, 8 * 32 * 768 * 4), (16, 768, 3072, 32, 8 * 16 * 768 * 4),
+    # the skinny kernel's split: groups 32 and 64 at M = 32 (24 K-blocks of
+    # 128 codes times two row tiles, 4 shares of 6); not taken for less work
+    # per row group (groups 32 and 64 at M = 16: 24 K-blocks), where the
+    # pipelined form runs (group 128, 5-16 rows) or with 128 row groups or
+    # more
+    (32, 768, 3072, 32, 4 * 32 * 768 * 4), (16, 768, 3072, 32, 0),
     (32, 768, 3072, 64, 4 * 32 * 768 * 4), (16, 768, 3072, 64, 0),
     (8, 1024, 8192, 128, 0), (32, 2048, 3072, 64, 0),
     # ragged: 65 row groups, 33 K-blocks of 128 codes in 4 shares of 9

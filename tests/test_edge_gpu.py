@@ -184,9 +184,9 @@ def check(y, x, p, s, K, g, zeros=None, bias=None, relu=False, half_out=False, w
 # per block (N >= 8192 / 16384), eight wavefronts for one row group and rows
 # of 32 or more pair-blocks (K = 8192, 11008), two and four 16-row tiles
 # (M = 24, 40),
-# groups 32 and 64 as K-blocks of two groups (M = 5 .. 40, one, two and four
-# row groups, rows of a single K-block; K = 192 with group 64 keeps one-group
-# K-blocks). tiled: the 128 x 256, 128 x 128, 64 x 128 and 32 x 128 block
+# groups 32 and 64 as K-blocks of four and two groups (M = 5 .. 40, one, two
+# and four row groups, rows of a single K-block; K = 64 with group 32 takes
+# two-group K-blocks, K = 192 with group 64 one-group K-blocks). tiled: the 128 x 256, 128 x 128, 64 x 128 and 32 x 128 block
 # tiles with 1, 2, 4 and 8 sub-steps per group, a group size decided at run
 # time (1024), 32-code sub-steps (group 32), ragged N and M tails. generic:
 # binary16 x.
@@ -267,21 +267,23 @@ def test_edge_rows_epilogue(dq, N, K, g, M, path):
     check(yh, x, packed, scales, K, g, bias=b, relu=True, half_out=True, what=f"fp16 output M={M}")
 
 
-def test_two_group_kblocks_unaligned_scales(dq):
-    """Groups 32 and 64 at 5 or more rows read each K-block's two scales as one
-    4-byte word; scales at an address that is 2 mod 4 take the one-group
-    K-blocks, with and without the split of K (whose shares are then counted
-    in those K-blocks). Both against the oracle."""
+@pytest.mark.parametrize("offset", [1, 2], ids=["scales-2-mod-4", "scales-4-mod-8"])
+def test_multi_group_kblocks_unaligned_scales(dq, offset):
+    """Groups 32 and 64 at 5 or more rows read each K-block's scales as one
+    word (8 bytes for four groups of 32, 4 for two groups); scales at an
+    address of 2 mod 4 take one-group K-blocks, at 4 mod 8 two-group ones,
+    with and without the split of K (whose shares are then counted in those
+    K-blocks). Both against the oracle."""
     for (N, K, M, g) in [(300, 1024, 16, 32), (768, 3072, 32, 32), (300, 1024, 8, 64), (768, 3072, 32, 64)]:
         packed, scales = edge_matrix(N, K, g, seed=N + M)
         G = scales.shape[1]
-        buf = torch.zeros(N * G + 1, dtype=torch.float16, device=DEV)
-        buf[1:] = dev(scales).reshape(-1)
-        s_odd = buf[1:].view(N, G)
-        assert s_odd.data_ptr() % 4 == 2
+        buf = torch.zeros(N * G + offset, dtype=torch.float16, device=DEV)
+        buf[offset:] = dev(scales).reshape(-1)
+        s_odd = buf[offset:].view(N, G)
+        assert s_odd.data_ptr() % 8 == 2 * offset
         x = activations(M, K, seed=M + 3, extreme=False)
         xd, pd = dev(x), dev(packed)
-        say(f"case: unaligned scales N={N} K={K} M={M} g={g}")
+        say(f"case: unaligned scales (+{2 * offset} B) N={N} K={K} M={M} g={g}")
         y = host(dq.int4_matmul_path(xd, pd, s_odd, K, g, "skinny"))
         check(y, x, packed, scales, K, g, what=f"unaligned scales N={N} M={M}")
         ws = dq.linear_workspace(M, N, K, g, device=DEV)

@@ -146,8 +146,8 @@ def test_small_workspace_runs_unsplit(dq):
 
 # The skinny kernel's split of K (fewer than 128 groups of 16 weight rows, at
 # least 96 K-blocks times 16-row tiles of x per row group): (M, N, K, group).
-# Group 32 (64-code K-blocks of two groups) at M = 32 (8 shares) and 17 rows
-# against 100 weight rows, group 64 (128-code K-blocks of two groups) at 32
+# Group 32 (128-code K-blocks of four groups) at M = 32 and 17 rows against
+# 100 weight rows (4 shares), group 64 (128-code K-blocks of two groups) at 32
 # and 40 rows (two and three row tiles), [1024, 8192] at M = 64, ragged M and
 # N with a last share shorter than the others (K = 4224: 33 K-blocks in
 # shares of 9), group 256 (two K-blocks per group), 33 rows of group 128.
